@@ -1,0 +1,199 @@
+"""Pins of the oracle's residual-window bookkeeping and decode attention.
+
+Closed form of the quantized count, ring contents, block bytes equal to the
+stateless quantizer, the workloads' stated (quantized, residual) splits,
+capacity overflow; attention against torch's scaled_dot_product_attention in
+fp64 (a library routine), identical keys, GQA mapping, rotation invariance.
+"""
+import numpy as np
+import pytest
+import torch
+
+from int2_kv_cache_amd import synth
+
+
+def q_closed_form(n):
+    return 32 * ((max(0, n - 128) + 31) // 32)
+
+
+def _cache(orc, wl, max_blocks=None, **kw):
+    cfg = wl.cfg
+    mb = max_blocks if max_blocks is not None else (max(wl.ctx_lens) + 31) // 32 + 1
+    return orc.OracleCache(cfg.batch, cfg.hq, cfg.hkv, mb, **kw)
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 31, 32, 33, 127, 128, 129, 160, 161, 300])
+def test_quantized_count_closed_form(orc, n):
+    wl = synth.workload(0, ctx=max(n, 1) + 1)
+    c = _cache(orc, wl)
+    if n:
+        k, v = wl.prefill(0, n)
+        c.prefill(0, k, v, wl.cfg.dtype)
+    assert c.n(0) == n and c.q(0) == q_closed_form(n)
+    assert 0 <= n - c.q(0) <= 128
+
+
+def test_workload_splits(orc):
+    """Context 1024 after the first decode step: 896 INT2 (28 blocks) + 128."""
+    for ctx, q in [(1024, 896), (32768, 32640), (131072, 130944), (65536, 65408)]:
+        assert q_closed_form(ctx) == q and ctx - q == 128
+    wl = synth.workload(0)
+    c = _cache(orc, wl)
+    k, v = wl.prefill(0)
+    c.prefill(0, k, v, wl.cfg.dtype)
+    kn, vn, _ = next(wl.steps(1))
+    c.append(kn, vn, wl.cfg.dtype)
+    assert (c.n(0), c.q(0)) == (1024, 896)
+
+
+def test_ring_and_blocks_match_stateless_steps(orc):
+    """After n appends: ring slot t%128 holds token t's k_hat, norm and fp16 v
+    for every t in [Q, n); pool block j holds the stateless quantizer's record
+    of tokens 32j..32j+31."""
+    wl = synth.workload(2, ctx=400, batch=2)
+    c = _cache(orc, wl)
+    dt = wl.cfg.dtype
+    ks, vs = [], []
+    for b in range(2):
+        k, v = wl.prefill(b, 333 + 17 * b)
+        c.prefill(b, k, v, dt)
+        ks.append(k)
+        vs.append(v)
+    for b in range(2):
+        n, Q = c.n(b), c.q(b)
+        khat, norm = orc.rotate_scale_key(ks[b], dt)
+        v16 = orc.in_to_f16(vs[b], dt)
+        for t in range(Q, n):
+            s = t % 128
+            assert np.array_equal(c.res_k[b, :, s, :], khat[t])
+            assert np.array_equal(c.res_v[b, :, :, s], v16[t])
+            assert c.res_norm[b, s] == norm[t]
+        rec, bn = orc.quant_pack(khat[:Q], norm[:Q], v16[:Q])
+        for j in range(Q // 32):
+            p = c.block_table[b, j]
+            assert np.array_equal(c.pool[p], rec[j])
+            assert np.array_equal(c.pool_norm[p], bn[j])
+
+
+def test_capacity_overflow_sets_flag_and_drops(orc):
+    wl = synth.workload(0, ctx=300)
+    c = _cache(orc, wl, max_blocks=2)
+    k, v = wl.prefill(0, 260)
+    c.prefill(0, k, v, wl.cfg.dtype)
+    # 2 blocks fit (Q=64 at n=192); the append that needs block 2 is dropped
+    assert c.error_flag[0] == 1
+    assert c.q(0) == 64 and c.n(0) == 192
+
+
+def test_prefill_rejects_nonempty(orc):
+    wl = synth.workload(0, ctx=50)
+    c = _cache(orc, wl)
+    k, v = wl.prefill(0, 10)
+    c.prefill(0, k, v, wl.cfg.dtype)
+    with pytest.raises(ValueError):
+        c.prefill(0, k, v, wl.cfg.dtype)
+
+
+def test_dequantized_keys_within_half_step(orc):
+    """|k_row - n * k_hat| <= n * delta16/2 (+ fp16 parameter rounding)."""
+    wl = synth.workload(2, ctx=300)
+    c = _cache(orc, wl)
+    k, v = wl.prefill(0, 290)
+    dt = wl.cfg.dtype
+    c.prefill(0, k, v, dt)
+    khat, norm = orc.rotate_scale_key(k, dt)
+    for t in list(range(0, c.q(0), 13)) + list(range(c.q(0), c.n(0), 9)):
+        for h in range(wl.cfg.hkv):
+            row = c.key_row(0, h, t)
+            nn = float(norm[t:t + 1].view(np.float16)[0])
+            kh = khat[t, h].view(np.float16).astype(np.float64)
+            if t >= c.q(0):
+                assert np.array_equal(row, nn * kh)
+                continue
+            p = c.block_table[0, t // 32]
+            d16 = c.pool[p, h, 2048:2304].view(np.float16).astype(np.float64)
+            assert np.all(np.abs(row - nn * kh) <= nn * (0.5 * d16 * (1 + 2e-3)) + 1e-12)
+
+
+def _sdpa64(q, K, V):
+    """torch SDPA in fp64: q [Hq, 128], K/V [Hq, n, 128] -> out [Hq, 128]."""
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None, None, :].double(),
+        torch.from_numpy(K)[:, None].double(), torch.from_numpy(V)[:, None].double())
+    return out[:, 0, 0].numpy()
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 127, 128, 129, 160, 161, 1024])
+def test_attention_equals_library_sdpa_on_dequantized_cache(orc, n):
+    wl = synth.workload(0, ctx=n)
+    c = _cache(orc, wl)
+    dt = wl.cfg.dtype
+    k, v = wl.prefill(0)
+    if n > 1:
+        c.prefill(0, k, v, dt)
+    kn, vn, q = next(wl.steps(1))
+    c.append(kn, vn, dt)
+    assert c.n(0) == n
+    qr = orc.rotate_query(q, dt)
+    out, lse = c.decode_attn(qr)
+    hq, hkv = wl.cfg.hq, wl.cfg.hkv
+    K = np.stack([np.stack([c.key_row(0, i // (hq // hkv), t) for t in range(n)]) for i in range(hq)])
+    V = np.stack([np.stack([c.value_row(0, i // (hq // hkv), t) for t in range(n)]) for i in range(hq)])
+    ref = _sdpa64(qr[0].astype(np.float64), K, V)
+    assert np.abs(out[0] - ref).max() < 1e-6
+    s = np.einsum("hc,htc->ht", qr[0].astype(np.float64), K) / np.sqrt(128.0)
+    m = s.max(axis=1)
+    assert np.allclose(lse[0], m + np.log(np.exp(s - m[:, None]).sum(1)), rtol=1e-6)
+
+
+def test_identical_keys_give_mean_of_values(orc):
+    wl = synth.workload(0, ctx=300)
+    c = _cache(orc, wl)
+    rng = np.random.default_rng(5)
+    kone = synth.to_fp16_bits(rng.standard_normal((1, 1, 128)))
+    K = np.repeat(kone, 299, axis=0)
+    V = synth.to_fp16_bits(rng.standard_normal((299, 1, 128)))
+    c.prefill(0, K, V, synth.FP16)
+    qr = orc.rotate_query(synth.to_fp16_bits(rng.standard_normal((1, 4, 128))), synth.FP16)
+    out, _ = c.decode_attn(qr)
+    Vd = np.stack([c.value_row(0, 0, t) for t in range(299)])
+    assert np.abs(out[0] - Vd.mean(0)[None, :]).max() < 1e-6
+
+
+def test_gqa_mapping_contiguous(orc):
+    """Hq=4, Hkv=2: query heads 0,1 read KV head 0, heads 2,3 read KV head 1."""
+    c = orc.OracleCache(1, 4, 2, 8)
+    rng = np.random.default_rng(6)
+    K = synth.to_fp16_bits(rng.standard_normal((150, 2, 128)))
+    V = np.zeros((150, 2, 128), np.float32)
+    V[:, 0, :] = -3.0
+    V[:, 1, :] = 7.0
+    c.prefill(0, K, synth.to_fp16_bits(V), synth.FP16)
+    qr = orc.rotate_query(synth.to_fp16_bits(rng.standard_normal((1, 4, 128))), synth.FP16)
+    out, _ = c.decode_attn(qr)
+    assert np.all(out[0, :2] == -3.0) and np.all(out[0, 2:] == 7.0)
+
+
+def test_rotated_pipeline_matches_plain_attention_without_quantization(orc):
+    """n <= 128: everything sits in the fp16 window, so the oracle's attention
+    over rotated q, k must equal plain attention over the raw q, k (rotation
+    invariance) up to fp16 rounding of k_hat and the norm."""
+    wl = synth.workload(0, ctx=100)
+    c = _cache(orc, wl)
+    k, v = wl.prefill(0)
+    dt = wl.cfg.dtype
+    c.prefill(0, k, v, dt)
+    kn, vn, q = next(wl.steps(1))
+    c.append(kn, vn, dt)
+    out, _ = c.decode_attn(orc.rotate_query(q, dt))
+    Kraw = synth.bits_to_f32(np.concatenate([k, kn]), dt)[:, 0, :].astype(np.float64)
+    Vraw = synth.bits_to_f32(np.concatenate([v, vn]), dt)[:, 0, :].astype(np.float64)
+    qraw = synth.bits_to_f32(q, dt)[0].astype(np.float64)
+    ref = _sdpa64(qraw, np.repeat(Kraw[None], 4, 0), np.repeat(Vraw[None], 4, 0))
+    assert np.abs(out[0] - ref).max() < 2e-2
+
+
+def test_empty_sequence(orc):
+    c = orc.OracleCache(1, 4, 1, 4)
+    out, lse = c.decode_attn(np.zeros((1, 4, 128), np.float32))
+    assert not out.any() and np.all(np.isneginf(lse))
