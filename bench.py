@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the OScaR INT2 decode path on one MI355X.
+
+Workload (the headline configuration): Qwen3-8B-shaped single-sequence decode
+at 128K context -- batch 1, 32 query heads / 8 KV heads, head dim 128, bf16
+inputs, 131072 tokens after the first step (130944 INT2 + 128 fp16).  The
+cache is prefilled with 131071 synthetic tokens, then every timed step runs,
+for each of L distinct layer caches, the whole decode hot path:
+  append_kv   -- FHT + Omni-Token Scaling of the new Key, residual-window
+                 bookkeeping, INT2 flush of a 32-token block when due
+  decode_attn -- query FHT, split-K attention over the INT2 blocks and the
+                 fp16 window, cross-split LSE reduce.
+L copies (default 8, 806 MB) are cycled so the 256 MB Infinity Cache cannot
+serve a layer from a previous visit.
+
+Output: one JSON line.  value = context tokens attended per second (whole job),
+plus the per-layer microseconds, the roofline of the attention kernels and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
+
+
+def algorithmic_bytes(n: int, Q: int, hq: int, hkv: int) -> int:
+    """Bytes one decode_attn launch must move for one sequence: each INT2
+    (block, KV head) record (3072 B) + 64 B of token norms per block, each
+    fp16 window token (256 B K + 256 B V per KV head + 2 B norm), the bf16
+    query and the fp32 output."""
+    nb = Q // 32
+    r = n - Q
+    return nb * (hkv * 3072 + 64) + r * (hkv * 512 + 2) + hq * 128 * 2 + hq * 128 * 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--ctx", type=int, default=131072)
+    ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="query heads of the oracle sample (scaled to all heads)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, k, v, steps, hq, args):
+    """The oracle as it stands, single-threaded, on a bounded sample of the
+    same workload: its append of one step's token, then decode attention
+    for `cpu_heads` of the query heads over the full context, scaled to all
+    query heads."""
+    import oracle
+    cfg = wl.cfg
+    mb = (args.ctx + 4096) // 32
+    orc = oracle.OracleCache(1, cfg.hq, cfg.hkv, mb, mb)
+    orc.prefill(0, k, v, cfg.dtype)
+    kn, vn, q = steps[0]
+    t0 = time.perf_counter()
+    orc.append(kn, vn, cfg.dtype)
+    qr = oracle.rotate_query(q, cfg.dtype)
+    heads = list(range(0, hq, max(1, hq // args.cpu_heads)))[: args.cpu_heads]
+    for i in heads:
+        orc.decode_attn_one(qr, 0, i)
+    dt = time.perf_counter() - t0
+    scale = hq / len(heads)
+    t_step = dt * scale
+    n = orc.n(0)
+    return {"value": n / t_step, "unit": "ctx tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "one decode step of one layer at n=%d: append + attention for %d of "
+                      "%d query heads (timed %.2f s), scaled x%.1f to all heads"
+                      % (n, len(heads), hq, dt, scale),
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import int2_kv_cache_amd as ok
+    from int2_kv_cache_amd import synth
+
+    torch.cuda.set_device(0)
+    wl = synth.workload(2, ctx=args.ctx)
+    cfg = wl.cfg
+    L = args.layers
+    n_steps_total = args.warmup + args.steps
+    max_ctx = args.ctx + n_steps_total + 64
+    mb = (max_ctx + 31) // 32
+    geom = ok.make_geom(1, cfg.hq, cfg.hkv, mb, mb)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    t0 = time.perf_counter()
+    k, v = wl.prefill(0)
+    kd, vd = dev(k), dev(v)
+    caches = []
+    pre_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    pre_ms = []
+    for _ in range(L):
+        c = ok.DeviceCache(geom)
+        pre_ev[0].record()
+        ok.prefill_quantize(c, 0, kd, vd, cfg.dtype)
+        pre_ev[1].record()
+        torch.cuda.synchronize()
+        pre_ms.append(pre_ev[0].elapsed_time(pre_ev[1]))
+        caches.append(c)
+    del kd, vd
+    steps = list(wl.steps(n_steps_total))
+    kn_d = [dev(s[0]) for s in steps]
+    vn_d = [dev(s[1]) for s in steps]
+    q_d = [dev(s[2]) for s in steps]
+    S, nbytes = ok.decode_workspace_bytes(geom, max_ctx, args.splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(1, cfg.hq, 128, dtype=torch.float32, device="cuda")
+    lse = torch.empty(1, cfg.hq, dtype=torch.float32, device="cuda")
+    setup_s = time.perf_counter() - t0
+
+    def step(i, ev=None):
+        for li, c in enumerate(caches):
+            ok.append_kv(c, kn_d[i], vn_d[i], cfg.dtype)
+            if ev is not None:
+                ev[li][0].record()
+            ok.decode_attn(c, q_d[i], cfg.dtype, out, lse, ws, max_ctx, S, args.variant)
+            if ev is not None:
+                ev[li][1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n0 = int(caches[0].seq_state[0, 0].item())
+
+    # timed region: whole steps; attention launches bracketed by events on the
+    # stream they run on (torch's current stream, which the binding passes)
+    attn_ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)]
+               for _ in range(args.steps)]
+    t_beg, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_beg.record()
+    for s_i in range(args.steps):
+        step(args.warmup + s_i, attn_ev[s_i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_beg.elapsed_time(t_end)
+    attn_ms = [attn_ev[s][l][0].elapsed_time(attn_ev[s][l][1])
+               for s in range(args.steps) for l in range(L)]
+    st = caches[0].seq_state.cpu().numpy()[0]
+    flag = int(caches[0].error_flag.item())
+    assert flag == 0, "cache error flag %d" % flag
+    n1, Q1 = int(st[0]), int(st[1])
+
+    ms_per_step = total_ms / args.steps
+    us_per_layer = ms_per_step * 1000.0 / L
+    # context tokens attended in the timed region (every layer, every step)
+    ctx_tokens = sum(n0 + 1 + s for s in range(args.steps)) * L
+    value = ctx_tokens / (total_ms / 1000.0)
+    attn_us = float(np.mean(attn_ms)) * 1000.0
+    n_mid = n0 + 1 + args.steps // 2
+    q_mid = 32 * ((max(0, n_mid - 128) + 31) // 32)
+    bytes_attn = algorithmic_bytes(n_mid, q_mid, cfg.hq, cfg.hkv)
+    achieved = bytes_attn / (attn_us * 1e-6) / 1e9
+    res = {
+        "metric": "INT2 decode-attn µs/step, ctx tokens/s & % HBM peak; 128K ctx bs1, 16K bs48",
+        "value": value,
+        "unit": "ctx tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int2 cache, fp32 math" if args.variant == 1 else "int2 cache, fp16 mfma / fp32 acc",
+        "data": "synthetic (seeded; K outliers/sinks/log-normal norms, V and q N(0,1))",
+        "config": {"workload": "qwen3-8b-shape decode, 128K ctx, batch 1",
+                   "batch": 1, "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv,
+                   "head_dim": 128, "ctx_first_step": args.ctx, "layers_cycled": L,
+                   "splits": S, "variant": args.variant},
+        "us_per_layer_step": us_per_layer,
+        "attn_us": attn_us,
+        "append_plus_gaps_us": us_per_layer - attn_us,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_attn (split-K + LSE reduce)",
+                     "algorithmic_bytes": bytes_attn},
+        "prefill_ms_per_layer": float(np.median(pre_ms)),
+        "prefill_tokens_per_s": (args.ctx - 1) / (float(np.median(pre_ms)) / 1000.0),
+        "final_state": [n1, Q1],
+        "setup_s": setup_s,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(wl, k, v, steps, cfg.hq, args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

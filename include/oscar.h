@@ -1,0 +1,221 @@
+/*
+ * oscar.h -- C ABI of the MI355X (gfx950) OScaR INT2 KV-cache library.
+ *
+ * OScaR ("Omni-Scaled Canalized Rotation", arXiv 2605.19660) quantizes the KV
+ * cache to 2 bits in three steps: an online 128-point Hadamard rotation of
+ * each new Key and of the query, a per-token L2 normalisation of the rotated
+ * Key whose norm is kept, and KIVI-style INT2 quantization (Keys per channel
+ * over 32-token blocks, Values per token over 32-channel groups) with the
+ * newest 128 tokens kept in fp16.  Decode attention dequantizes, undoes the
+ * scaling and attends.  The three kernels of the method -- fused FHT +
+ * scaling, quantization, fused dequant + inverse scaling + attention -- are
+ * named in the structured summary "OScaR：面向大模型及多模态LLM极限KV缓存量化的
+ * 奥卡姆剃刀" (paper.rainbus.top), section 方法步骤详情, and in the reading
+ * notes "OScaR: The Occam's Razor for Extreme KV Cache Quantization in LLMs
+ * and Beyond" (yingwang.github.io), section End-to-End Flow.
+ *
+ * Conventions for every entry point:
+ *   - Plain pointers only.  "device" pointers are HIP device memory of the
+ *     current device; "host" pointers are ordinary host memory.
+ *   - The caller owns and allocates every buffer (sizes from
+ *     oscar_cache_layout / oscar_decode_workspace_bytes).  The library never
+ *     allocates, frees or synchronizes.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL is the default stream).  Results are visible after the
+ *     caller synchronizes that stream.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns OSCAR_EINVAL and enqueues nothing.  Device-side
+ *     conditions (block-table capacity, prefill into a non-empty sequence)
+ *     set sticky bits in *error_flag and skip the affected write.
+ *   - Calls on one stream are ordered; calls on different streams that touch
+ *     the same cache race.
+ *   - Only gfx950 is supported (OSCAR_EUNSUPPORTED otherwise).
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define OSCAR_API __attribute__((visibility("default")))
+#else
+#define OSCAR_API
+#endif
+
+#define OSCAR_HEAD_DIM 128       /* d */
+#define OSCAR_BLOCK_TOKENS 32    /* G: Key quantization block */
+#define OSCAR_RESIDUAL_TOKENS 128 /* R: fp16 residual window */
+#define OSCAR_V_GROUP 32         /* Value quantization group (channels) */
+#define OSCAR_RECORD_BYTES 3072  /* one (physical block, KV head) record */
+
+typedef enum {
+    OSCAR_OK = 0,
+    OSCAR_EINVAL = 1,       /* bad argument: null pointer, bad shape, misalignment */
+    OSCAR_EUNSUPPORTED = 2, /* device is not gfx950, or option not built */
+    OSCAR_ELAUNCH = 3,      /* the HIP runtime rejected a launch */
+    OSCAR_EWORKSPACE = 4    /* workspace smaller than oscar_decode_workspace_bytes */
+} oscar_status;
+
+typedef enum { OSCAR_FP16 = 0, OSCAR_BF16 = 1, OSCAR_FP32 = 2 } oscar_dtype;
+typedef enum { OSCAR_NORM_TOKEN = 0, OSCAR_NORM_HEAD = 1 } oscar_norm_scope;
+typedef enum { OSCAR_ROT_QUERY = 0, OSCAR_ROT_KEY = 1 } oscar_rot_mode;
+typedef enum {
+    OSCAR_ATTN_AUTO = 0, /* the fastest kernel built (the MFMA one) */
+    OSCAR_ATTN_VALU = 1, /* scalar-FMA dot products on the vector ALUs */
+    OSCAR_ATTN_MFMA = 2  /* GQA-group q.K^T and P.V tiles on the matrix cores */
+} oscar_attn_variant;
+
+/* error_flag bits */
+#define OSCAR_FLAG_CAPACITY 1u  /* a block index reached max_blocks_per_seq */
+#define OSCAR_FLAG_NONEMPTY 2u  /* prefill into a sequence with n != 0 */
+#define OSCAR_FLAG_BADSTATE 4u  /* a block id outside the pool, or an inconsistent
+                                   {n, Q}: the affected work is skipped */
+
+/* Cache geometry (host struct). */
+typedef struct {
+    int32_t batch;               /* B sequences */
+    int32_t num_q_heads;         /* Hq */
+    int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0, Hq/Hkv in {1,2,4,8} */
+    int32_t head_dim;            /* must be 128 */
+    int32_t norm_scope;          /* oscar_norm_scope; only TOKEN is built */
+    int32_t max_blocks_per_seq;  /* block-table row length */
+    int32_t num_physical_blocks; /* pool capacity */
+} oscar_cache_geom;
+
+/* Cache buffers (device pointers, caller-owned).  Layout, per the record
+ * layout of the packed cache ("packed cache" + "residual cache", popular
+ * science article on OScaR (animattoys.com), section 三):
+ *   pool        [num_physical_blocks][Hkv][3072] bytes, 256-B aligned.  Record:
+ *                 [0,1024)    K codes: channel c of token t at bits 2*(c&3) of
+ *                             byte 32*t + (c>>2)
+ *                 [1024,2048) V codes: slice 16*(t>>3) + (c&15) of 16 bytes at
+ *                             1024 + 16*slice; 32-bit word c>>5 of it; bit
+ *                             2*(4*((c>>4)&1) + ((t&7)>>1)) + 16*(t&1)
+ *                 [2048,2304) K step (delta) fp16 [128]
+ *                 [2304,2560) K zero point fp16 [128]
+ *                 [2560,3072) V (step, zero) fp16 pairs, [32 tokens][4 groups]
+ *   pool_norm   [num_physical_blocks][32] fp16 token norms
+ *   res_k       [B][Hkv][128 slots][128] fp16 rotated+scaled keys (k_hat)
+ *   res_v       [B][Hkv][128 channels][128 slots] fp16 values
+ *   res_norm    [B][128 slots] fp16 token norms
+ *   block_table [B][max_blocks_per_seq] int32 physical block ids (caller fills)
+ *   seq_state   [B][2] int32 = {n tokens, Q quantized tokens}; zero = empty
+ *   error_flag  [1] int32 sticky bits (OSCAR_FLAG_*); caller zeroes it
+ * Token t of a sequence lives in block t/32 (t < Q) or ring slot t % 128
+ * (Q <= t < n).  All buffers zero-initialised by the caller before first use. */
+typedef struct {
+    void *pool;
+    void *pool_norm;
+    void *res_k;
+    void *res_v;
+    void *res_norm;
+    int32_t *block_table;
+    int32_t *seq_state;
+    int32_t *error_flag;
+} oscar_cache;
+
+/* Byte sizes of each cache buffer for a geometry. */
+typedef struct {
+    size_t pool, pool_norm, res_k, res_v, res_norm, block_table, seq_state, error_flag;
+} oscar_cache_sizes;
+
+/* Host-only.  Fills *out with the byte size of every cache buffer.
+ * EINVAL on a null pointer or an unsupported geometry. */
+OSCAR_API oscar_status oscar_cache_layout(const oscar_cache_geom *geom, oscar_cache_sizes *out);
+
+/* Canalized Rotation and Omni-Token Scaling on a batch of tokens (summary
+ * "OScaR：…", 方法步骤详情 (1) and (2); reading notes §II Step One and
+ * Step Two).
+ *   x         device, [n_tokens][n_heads][128] fp16 or bf16 (dtype).
+ *   mode      QUERY: q_out[n_tokens][n_heads][128] fp32 = FHT(x) per head,
+ *                    exactly the oracle's fp32 butterfly (strides 1..64,
+ *                    then x 1/sqrt(128)); khat_out, norm_out unused.
+ *             KEY:   y = FHT(x) per head; ss = pairwise-tree sum of squares
+ *                    over all heads (TOKEN) or per head (HEAD); khat_out
+ *                    [n_tokens][n_heads][128] fp16 = fp16(y / sqrt(ss));
+ *                    norm_out fp16 [n_tokens] (TOKEN) or [n_tokens][n_heads].
+ *   n_heads   >= 1 (QUERY), 1..16 (KEY: the norm spans all heads of a token).
+ * Errors: EINVAL (null, n_tokens < 0, n_heads out of range, bad dtype). */
+OSCAR_API oscar_status oscar_rotate_scale(const void *x, oscar_dtype dtype, int32_t n_tokens,
+                                int32_t n_heads, oscar_rot_mode mode,
+                                oscar_norm_scope norm_scope, float *q_out,
+                                void *khat_out, void *norm_out, void *stream);
+
+/* Stateless INT2 quantize + pack of whole 32-token blocks (summary "OScaR：…",
+ * 方法步骤详情 ②, the quantization kernel handling Keys and Values together).
+ *   khat16, v16  device, [32*n_blocks][n_kv_heads][128] fp16.
+ *   knorm16      device, [32*n_blocks] fp16 token norms (TOKEN scope).
+ *   rec_out      device, [n_blocks][n_kv_heads][3072] records (layout above).
+ *   norm_out     device, [n_blocks][32] fp16.
+ * Keys: per channel over the block's 32 tokens; Values: per token over each
+ * 32-channel group; delta = (max-min)/3, zero = min, code =
+ * clamp(rint((x-zero)/delta), 0, 3) in IEEE fp32, delta == 0 -> code 0.
+ * Errors: EINVAL. */
+OSCAR_API oscar_status oscar_quant_pack(const void *khat16, const void *knorm16, const void *v16,
+                              int32_t n_blocks, int32_t n_kv_heads,
+                              oscar_norm_scope norm_scope, void *rec_out,
+                              void *norm_out, void *stream);
+
+/* One decode-step append for every sequence (popular-science article, 三:
+ * residual cache of the newest tokens in fp16, quantized a block at a time;
+ * summary 论文图表 (c)).  Per sequence b with state {n, Q}:
+ *   if n - Q == 128: quantize ring tokens Q..Q+31 into physical block
+ *                    block_table[b][Q/32] (or set OSCAR_FLAG_CAPACITY and
+ *                    drop the append if Q/32 >= max_blocks_per_seq); Q += 32;
+ *   rotate+scale k_new[b], store k_hat, norm and fp16(v_new[b]) in slot
+ *   n % 128; n += 1.
+ *   k_new, v_new  device, [B][Hkv][128] fp16 or bf16.
+ * Errors: EINVAL. */
+OSCAR_API oscar_status oscar_append_kv(const oscar_cache_geom *geom, const oscar_cache *cache,
+                             const void *k_new, const void *v_new, oscar_dtype dtype,
+                             void *stream);
+
+/* Bulk prefill of an empty sequence `seq` with n_tokens tokens (reading notes,
+ * End-to-End Flow: prefill Keys pass FHT, per-token scaling and INT2
+ * per-channel quantization before entering the cache).  The resulting cache
+ * state is byte-identical, on its valid region, to n_tokens appends.
+ *   k, v  device, [n_tokens][Hkv][128] fp16 or bf16.
+ * Errors: EINVAL (also when the blocks needed exceed max_blocks_per_seq);
+ * device: OSCAR_FLAG_NONEMPTY if the sequence already holds tokens. */
+OSCAR_API oscar_status oscar_prefill_quantize(const oscar_cache_geom *geom, const oscar_cache *cache,
+                                    int32_t seq, const void *k, const void *v,
+                                    int32_t n_tokens, oscar_dtype dtype, void *stream);
+
+/* Split count the library would pick for max_ctx (num_splits == 0) and the
+ * workspace bytes decode attention needs with that split count. */
+OSCAR_API oscar_status oscar_decode_workspace_bytes(const oscar_cache_geom *geom, int32_t max_ctx,
+                                          int32_t num_splits, int32_t *splits_out,
+                                          size_t *bytes);
+
+/* Split-K decode attention over the INT2 cache (summary "OScaR：…",
+ * 方法步骤详情 ③: fused dequantization, inverse scaling and attention;
+ * reading notes, End-to-End Flow).  For sequence b and query head i, with
+ * KV head h = i / (Hq/Hkv) and the n cached tokens (the step's own token
+ * included): out = softmax(q' K^T / sqrt(128)) V where q' = FHT(q) and
+ * K, V are the dequantized, un-scaled rows in the rotated basis.
+ *   q        device, [B][Hq][128]: fp16/bf16 raw queries (rotated in the
+ *            kernel), or fp32 already-rotated q' (dtype OSCAR_FP32).
+ *   out      device, [B][Hq][128] fp32 (rotated-V basis).
+ *   lse      device, [B][Hq] fp32 log-sum-exp of the scaled scores, or NULL.
+ *   workspace device, >= oscar_decode_workspace_bytes(...) bytes, 256-B aligned:
+ *            per-split partials (m, l, o); no contents carried between calls.
+ *   num_splits  0 = pick from max_ctx; else 1..1024 splits per (b, KV head).
+ *   max_ctx  an upper bound on every sequence's n (used to size the split).
+ * Errors: EINVAL, EWORKSPACE, ELAUNCH. */
+OSCAR_API oscar_status oscar_decode_attn(const oscar_cache_geom *geom, const oscar_cache *cache,
+                               const void *q, oscar_dtype q_dtype, float *out, float *lse,
+                               void *workspace, size_t ws_bytes, int32_t num_splits,
+                               int32_t max_ctx, oscar_attn_variant variant, void *stream);
+
+/* Static string for a status code. */
+OSCAR_API const char *oscar_status_str(oscar_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,176 @@
+// oscar_device.hpp -- device helpers of the gfx950 OScaR kernels.
+//
+// Sources cited by tag:
+//   [RN]  reading notes "OScaR: The Occam's Razor for Extreme KV Cache
+//         Quantization in LLMs and Beyond" (yingwang.github.io paper-reads)
+//   [SUM] structured summary "OScaR：面向大模型及多模态LLM极限KV缓存量化的奥卡姆剃刀"
+//         (paper.rainbus.top)
+//   [POP] popular-science article on OScaR (animattoys.com), sections 一 to 五
+//
+// Everything that decides a stored bit (rotation, norm, fp16 rounding, INT2
+// codes) is written with contraction off and IEEE-rounded divide and sqrt,
+// so it reproduces one fixed sequence of fp32 operations exactly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar {
+
+constexpr int kD = 128;       // head dim
+constexpr int kG = 32;        // Key block (tokens)
+constexpr int kR = 128;       // residual window (tokens)
+constexpr int kVG = 32;       // Value group (channels)
+constexpr int kRec = 3072;    // bytes per (physical block, KV head) record
+constexpr int kRecKCodes = 0, kRecVCodes = 1024, kRecKDelta = 2048, kRecKZero = 2304,
+              kRecVParam = 2560;
+
+// fp32(1/sqrt(128)); the orthonormal Hadamard matrix has entries +-1/sqrt(d)
+// ([RN] §II Step One: Canalized Rotation).
+constexpr float kFhtScale = 0x1.6a09e6p-4f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+// fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32 in the default mode).
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+__device__ __forceinline__ float in_to_f32(uint16_t x, int is_bf16) {
+  return is_bf16 ? bf16_to_f32(x) : f16_to_f32(x);
+}
+
+// 128-point fast Hadamard transform of one vector spread over a full wave:
+// lane l holds x[l] in `a` and x[l + 64] in `b`.  Butterflies with strides
+// 1, 2, 4, 8, 16, 32 pair lane l with lane l ^ h; stride 64 pairs the two
+// registers of one lane; then one multiply by 1/sqrt(128).  Same strides in
+// the same order as the plain butterfly definition, so every fp32 rounding is
+// the same: the upper element of each pair gets (lower - upper), the lower
+// gets (lower + upper) ([SUM] 前置知识 on FHT; [POP] 二; [RN] §II Step One).
+// All 64 lanes must be active.
+__device__ __forceinline__ void fht128_wave(float& a, float& b) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+    const float pa = __shfl_xor(a, h, 64);
+    const float pb = __shfl_xor(b, h, 64);
+    const bool upper = (lane & h) != 0;
+    a = upper ? (pa - a) : (a + pa);
+    b = upper ? (pb - b) : (b + pb);
+  }
+  const float lo = a + b, hi = a - b;
+  a = lo * kFhtScale;
+  b = hi * kFhtScale;
+}
+
+// Sum of squares of the wave's 128 values (layout of fht128_wave) by the
+// pairwise tree: level s adds element i + s into element i.  Levels 1..32
+// are lane butterflies (each lane of a pair ends with the same, commutative,
+// sum), level 64 adds the two registers.  Every lane returns the sum.
+__device__ __forceinline__ float wave_tree_sumsq(float a, float b) {
+#pragma clang fp contract(off)
+  float sa = a * a, sb = b * b;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    sa = sa + __shfl_xor(sa, s, 64);
+    sb = sb + __shfl_xor(sb, s, 64);
+  }
+  return sa + sb;
+}
+
+// Pairwise tree over up to 16 per-head partial sums (zero-padded to 16; the
+// extra levels only add +0, which leaves a sum of squares unchanged).
+__device__ __forceinline__ float tree16(const float* part, int n) {
+#pragma clang fp contract(off)
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = i < n ? part[i] : 0.0f;
+#pragma unroll
+  for (int s = 1; s < 16; s <<= 1)
+#pragma unroll
+    for (int i = 0; i + s < 16; i += 2 * s) v[i] = v[i] + v[i + s];
+  return v[0];
+}
+
+// fp32 product rounded to fp32 and kept there.  Without the empty asm the
+// backend may fuse a following fp16 conversion into one mixed-precision FMA
+// that rounds only once, which differs from rounding to fp32 first.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+  float p = a * b;
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
+// Correctly rounded fp32 square root for x >= 0.  v_sqrt_f32 is accurate to
+// 1 ulp; the result is then fixed among its neighbours s-, s, s+.  With u the
+// spacing of the neighbours, x - s*s+ and x - s-*s are integer multiples of u^2
+// (x is a multiple of u^2 since x ~ s^2), so one fused multiply-add gives their
+// exact sign: sqrt(x) lies above the midpoint of (s, s+) iff x - s*s+ > 0, and
+// below the midpoint of (s-, s) iff x - s-*s <= 0.  Tiny inputs are scaled by
+// 2^64 (and the root by 2^-32) to keep the residuals in the normal range.
+__device__ __forceinline__ float sqrt_rn(float x) {
+  if (!(x > 0.0f)) return x == 0.0f ? x : __builtin_nanf("");
+  const bool tiny = x < 0x1p-64f;
+  const float xs = tiny ? x * 0x1p64f : x;
+  float s = __builtin_amdgcn_sqrtf(xs);
+  const float sm = __uint_as_float(__float_as_uint(s) - 1u);
+  const float sp = __uint_as_float(__float_as_uint(s) + 1u);
+  if (__builtin_fmaf(-sm, s, xs) <= 0.0f)
+    s = sm;
+  else if (__builtin_fmaf(-s, sp, xs) > 0.0f)
+    s = sp;
+  return tiny ? s * 0x1p-32f : s;
+}
+
+// Omni-Token Scaling factors from a sum of squares: norm = sqrt(ss) and
+// r = 1/norm, both correctly rounded fp32; ss == 0 gives r = 0 ([RN] §II
+// Step Two; [POP] 三 on 1/sqrt(sum x^2)).
+__device__ __forceinline__ void scale_from_ss(float ss, float& norm, float& r) {
+  norm = sqrt_rn(ss);
+  r = ss > 0.0f ? __fdiv_rn(1.0f, norm) : 0.0f;
+}
+
+// INT2 min-max quantizer over 32 values (fp16-valued fp32): delta =
+// (max - min)/3, zero = min, code = clamp(rint((x - zero)/delta), 0, 3),
+// round half to even, delta == 0 -> code 0 ([SUM] 前置知识 on per-channel
+// quantization and 方法步骤详情; [RN] §I).  A zero minimum or maximum is
+// canonicalised to +0.  Codes are returned 2 bits each, value i at bits 2i.
+__device__ __forceinline__ uint64_t quant32(const float* x, float& delta, float& zero) {
+#pragma clang fp contract(off)
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+  mn = mn + 0.0f;
+  mx = mx + 0.0f;
+  const float d = __fdiv_rn(mx - mn, 3.0f);
+  uint64_t codes = 0;
+  if (d > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float r = rintf(__fdiv_rn(x[i] - mn, d));
+      const int q = r < 0.0f ? 0 : (r > 3.0f ? 3 : static_cast<int>(r));
+      codes |= static_cast<uint64_t>(q) << (2 * i);
+    }
+  }
+  delta = d;
+  zero = mn;
+  return codes;
+}
+
+// Packed record layout (see include/oscar.h).
+__device__ __forceinline__ int kcode_bitpos(int t, int c) {   // bit index in K codes
+  return 8 * (32 * t + (c >> 2)) + 2 * (c & 3);
+}
+__device__ __forceinline__ int vcode_bitpos(int t, int c) {   // bit index in V codes
+  const int slice = 16 * (t >> 3) + (c & 15), word = c >> 5, e = (c >> 4) & 1, k = t & 7;
+  return 32 * (4 * slice + word) + 2 * (4 * e + (k >> 1)) + 16 * (k & 1);
+}
+
+}  // namespace oscar

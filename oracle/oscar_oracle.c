@@ -223,6 +223,11 @@ void orc_quant_group32(const uint16_t *x16, size_t stride, float *delta,
         if (x[t] > mx)
             mx = x[t];
     }
+    /* -0 and +0 compare equal, so which of them a scan keeps depends on the
+     * scan order; adding +0 turns a zero minimum or maximum into +0 (reading:
+     * the stored zero point of a group whose minimum is zero is +0). */
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
     float d = (mx - mn) / 3.0f;
     for (int t = 0; t < 32; t++) {
         int q = 0;

@@ -1,0 +1,117 @@
+"""Shared helpers of the GPU parity tests: run the same seeded inputs through
+the HIP library (via the C ABI) and through the CPU oracle, and compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import int2_kv_cache_amd as ok
+import oracle
+from int2_kv_cache_amd import synth
+
+ATOL = 2e-3   # max-abs tolerance on attention outputs (fp32 accumulation)
+
+
+def dev_u16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def assert_same_bits(got: np.ndarray, want: np.ndarray, what: str = ""):
+    """Bit-exact comparison with a short report (count, first positions and
+    the largest difference in units of the last place)."""
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if np.array_equal(got, want):
+        return
+    bad = np.argwhere(got != want)
+    gi = got.astype(np.int64)[tuple(bad.T)]
+    wi = want.astype(np.int64)[tuple(bad.T)]
+    raise AssertionError("%s: %d of %d differ; first at %s got %s want %s; max |diff| %d"
+                         % (what, len(bad), got.size, bad[:4].tolist(), gi[:4].tolist(),
+                            wi[:4].tolist(), int(np.abs(gi - wi).max())))
+
+
+def blocks_needed(ctx: int) -> int:
+    return (max(0, ctx - 128) + 31) // 32 + 1
+
+
+def shuffled_table(batch: int, max_blocks: int, seed: int = 99) -> np.ndarray:
+    """A non-trivial block table: a random permutation of physical blocks."""
+    rng = np.random.default_rng(seed)
+    return rng.permutation(batch * max_blocks).astype(np.int32).reshape(batch, max_blocks)
+
+
+class Pair:
+    """The same cache on the GPU and in the oracle."""
+
+    def __init__(self, wl: synth.Workload, max_ctx: int | None = None, table=None):
+        cfg = wl.cfg
+        self.wl = wl
+        mctx = max_ctx or (max(wl.ctx_lens) + 8)
+        self.max_blocks = blocks_needed(mctx)
+        self.table = table if table is not None else shuffled_table(cfg.batch, self.max_blocks)
+        nphys = cfg.batch * self.max_blocks
+        self.geom = ok.make_geom(cfg.batch, cfg.hq, cfg.hkv, self.max_blocks, nphys)
+        self.gpu = ok.DeviceCache(self.geom, block_table=torch.from_numpy(self.table))
+        self.orc = oracle.OracleCache(cfg.batch, cfg.hq, cfg.hkv, self.max_blocks, nphys,
+                                      block_table=self.table)
+        self.dtype = cfg.dtype
+
+    def prefill(self, b: int, k: np.ndarray, v: np.ndarray, gpu_bulk: bool = True):
+        self.orc.prefill(b, k, v, self.dtype)
+        if len(k) == 0:
+            return
+        if gpu_bulk:
+            ok.prefill_quantize(self.gpu, b, dev_u16(k), dev_u16(v), self.dtype)
+        else:
+            raise NotImplementedError
+
+    def append(self, kn: np.ndarray, vn: np.ndarray):
+        self.orc.append(kn, vn, self.dtype)
+        ok.append_kv(self.gpu, dev_u16(kn), dev_u16(vn), self.dtype)
+
+    def compare_state(self):
+        """Bit-exact comparison of the valid cache region."""
+        torch.cuda.synchronize()
+        g = self.gpu
+        st = g.seq_state.cpu().numpy()
+        assert np.array_equal(st, self.orc.seq_state), (st, self.orc.seq_state)
+        assert int(g.error_flag.cpu()[0]) == int(self.orc.error_flag[0])
+        pool = g.pool.cpu().numpy()
+        pnorm = host_u16(g.pool_norm)
+        rk, rv, rn = host_u16(g.res_k), host_u16(g.res_v), host_u16(g.res_norm)
+        o = self.orc
+        for b in range(self.geom.batch):
+            n, Q = o.n(b), o.q(b)
+            phys = self.table[b, :Q // 32]
+            for j, p in enumerate(phys):
+                assert_same_bits(pool[p], o.pool[p], "seq %d block %d record" % (b, j))
+                assert_same_bits(pnorm[p], o.pool_norm[p], "seq %d block %d norms" % (b, j))
+            slots = np.array([t % 128 for t in range(Q, n)], dtype=np.int64)
+            if len(slots):
+                assert_same_bits(rk[b][:, slots, :], o.res_k[b][:, slots, :], "res_k seq %d" % b)
+                assert_same_bits(rv[b][:, :, slots], o.res_v[b][:, :, slots], "res_v seq %d" % b)
+                assert_same_bits(rn[b][slots], o.res_norm[b][slots], "res_norm seq %d" % b)
+
+    def attend(self, q: np.ndarray, variant=ok.ATTN_AUTO, splits=0, max_ctx=None,
+               q_dtype=None):
+        """GPU decode attention -> (out, lse) numpy."""
+        cfg = self.wl.cfg
+        mctx = max_ctx or (max(o for o in [self.orc.n(b) for b in range(cfg.batch)]) + 1)
+        S, nbytes = ok.decode_workspace_bytes(self.geom, mctx, splits)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        out = torch.empty(cfg.batch, cfg.hq, 128, dtype=torch.float32, device="cuda")
+        lse = torch.empty(cfg.batch, cfg.hq, dtype=torch.float32, device="cuda")
+        if q_dtype == ok.FP32:
+            qt = torch.from_numpy(np.ascontiguousarray(q, np.float32)).cuda()
+        else:
+            qt = dev_u16(q)
+        ok.decode_attn(self.gpu, qt, self.dtype if q_dtype is None else q_dtype, out, lse, ws,
+                       mctx, splits, variant)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy()

@@ -1,0 +1,61 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the
+header declares, and its host-only calls behave (no GPU compute here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int2_kv_cache_amd as ok
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "oscar.h")).read()
+    return sorted(set(re.findall(r"\b(oscar_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_api():
+    assert set(_declared()) == set(ok.API)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ok.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_cache_layout_sizes():
+    g = ok.make_geom(2, 32, 8, 100, 200)
+    s = ok.cache_layout(g)
+    assert s.pool == 200 * 8 * 3072
+    assert s.pool_norm == 200 * 32 * 2
+    assert s.res_k == s.res_v == 2 * 8 * 128 * 128 * 2
+    assert s.res_norm == 2 * 128 * 2
+    assert s.block_table == 2 * 100 * 4
+    assert s.seq_state == 2 * 2 * 4
+
+
+@pytest.mark.parametrize("bad", [
+    dict(head_dim=64), dict(num_q_heads=6, num_kv_heads=4), dict(num_kv_heads=17, num_q_heads=34),
+    dict(batch=0), dict(num_q_heads=24, num_kv_heads=8), dict(max_blocks_per_seq=0)])
+def test_cache_layout_rejects(bad):
+    args = dict(batch=1, num_q_heads=4, num_kv_heads=1, max_blocks_per_seq=4,
+                num_physical_blocks=4)
+    args.update(bad)
+    with pytest.raises(ok.OscarError) as e:
+        ok.cache_layout(ok.make_geom(**args))
+    assert e.value.status == ok.EINVAL
+
+
+def test_head_norm_scope_not_built():
+    g = ok.make_geom(1, 4, 1, 4, 4, norm_scope=ok.NORM_HEAD)
+    with pytest.raises(ok.OscarError) as e:
+        ok.cache_layout(g)
+    assert e.value.status == ok.EUNSUPPORTED
+
+
+def test_status_strings():
+    assert ok.status_str(ok.OK) == "ok"
+    assert "workspace" in ok.status_str(ok.EWORKSPACE)

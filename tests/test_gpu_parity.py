@@ -1,0 +1,204 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact for the rotation, the norms, the INT2 codes, the packed records,
+the residual window and the sequence state; max-abs <= 2e-3 for attention.
+"""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a gfx950 GPU")]
+
+if gpu_available():
+    import torch
+    import int2_kv_cache_amd as ok
+    import oracle
+    from int2_kv_cache_amd import synth
+    from _parity import ATOL, Pair, assert_same_bits, dev_u16, host_u16
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_rotate_query_bit_exact(dtype):
+    wl = synth.workload(1, ctx=64)
+    qs = [q for _, _, q in wl.steps(3)]
+    q = np.concatenate(qs)                       # [3, 32, 128]
+    if dtype == 0:
+        q = synth.to_fp16_bits(synth.bits_to_f32(q, 1))
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ok.rotate_scale(dev_u16(q), dtype, ok.ROT_QUERY, q_out=out)
+    torch.cuda.synchronize()
+    want = oracle.rotate_query(q, dtype)
+    assert_same_bits(out.cpu().numpy().view(np.uint32), want.view(np.uint32), "q'")
+
+
+@pytest.mark.parametrize("cfg,hkv", [(0, None), (2, None), (2, 5), (4, None)])
+def test_rotate_scale_key_bit_exact(cfg, hkv):
+    wl = synth.workload(cfg, ctx=300)
+    k, _ = wl.prefill(0, 200)
+    if hkv is not None:
+        k = np.ascontiguousarray(k[:, :hkv])
+    dt = wl.cfg.dtype
+    khat = torch.empty(k.shape, dtype=torch.int16, device="cuda")
+    norm = torch.empty(k.shape[0], dtype=torch.int16, device="cuda")
+    ok.rotate_scale(dev_u16(k), dt, ok.ROT_KEY, khat_out=khat, norm_out=norm)
+    torch.cuda.synchronize()
+    wk, wn = oracle.rotate_scale_key(k, dt)
+    assert_same_bits(host_u16(norm), wn, "norm")
+    assert_same_bits(host_u16(khat), wk, "k_hat")
+
+
+def test_rotate_scale_zero_token():
+    k = np.zeros((2, 8, 128), np.uint16)
+    khat = torch.ones(k.shape, dtype=torch.int16, device="cuda")
+    norm = torch.ones(2, dtype=torch.int16, device="cuda")
+    ok.rotate_scale(dev_u16(k), 1, ok.ROT_KEY, khat_out=khat, norm_out=norm)
+    torch.cuda.synchronize()
+    assert not khat.cpu().numpy().any() and not norm.cpu().numpy().any()
+
+
+@pytest.mark.parametrize("nb,hkv", [(1, 1), (5, 8), (3, 3)])
+def test_quant_pack_bit_exact(nb, hkv):
+    rng = np.random.default_rng(nb * 10 + hkv)
+    wl = synth.workload(2, ctx=32 * nb + 10)
+    k, v = wl.prefill(0, 32 * nb)
+    k, v = np.ascontiguousarray(k[:, :hkv]), np.ascontiguousarray(v[:, :hkv])
+    khat, knorm = oracle.rotate_scale_key(k, synth.BF16)
+    v16 = oracle.in_to_f16(v, synth.BF16)
+    # a few constant channels and exact ties
+    khat[:, 0, 5] = khat[0, 0, 5]
+    v16[:, 0, :32] = synth.to_fp16_bits(rng.integers(-2, 2, (32 * nb, 32)) * 0.5)
+    rec = torch.zeros(nb, hkv, 3072, dtype=torch.uint8, device="cuda")
+    nrm = torch.zeros(nb, 32, dtype=torch.int16, device="cuda")
+    ok.quant_pack(dev_u16(khat), dev_u16(knorm), dev_u16(v16), rec, nrm)
+    torch.cuda.synchronize()
+    wr, wn = oracle.quant_pack(khat, knorm, v16)
+    assert_same_bits(rec.cpu().numpy(), wr, "records")
+    assert_same_bits(host_u16(nrm), wn, "norms")
+
+
+@pytest.mark.parametrize("cfg,batch,steps", [(0, 1, 300), (1, 2, 200)])
+def test_append_sequence_bit_exact(cfg, batch, steps):
+    """Appends from an empty cache cross several window flushes."""
+    wl = synth.workload(cfg, ctx=steps + 1, batch=batch)
+    pr = Pair(wl, max_ctx=steps + 8)
+    for i, (kn, vn, _) in enumerate(wl.steps(steps)):
+        pr.append(kn, vn)
+        if i in (0, 127, 128, 129, 160, steps - 1):
+            pr.compare_state()
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 127, 128, 129, 160, 161, 1000, 1023])
+def test_prefill_equals_appends(n):
+    """Bulk prefill gives the bytes n oracle appends give."""
+    wl = synth.workload(1, ctx=n + 1)
+    pr = Pair(wl)
+    k, v = wl.prefill(0, n)
+    pr.prefill(0, k, v)
+    pr.compare_state()
+
+
+def test_prefill_then_appends_and_ragged_batch():
+    wl = synth.workload(2, ctx=None, batch=3)
+    wl.ctx_lens = [300, 1000, 161]
+    pr = Pair(wl)
+    for b in range(3):
+        k, v = wl.prefill(b)
+        pr.prefill(b, k, v)
+    pr.compare_state()
+    for kn, vn, _ in wl.steps(40):
+        pr.append(kn, vn)
+    pr.compare_state()
+
+
+def test_prefill_nonempty_flag_and_capacity():
+    wl = synth.workload(0, ctx=400)
+    pr = Pair(wl, max_ctx=200)       # capacity: blocks for 200 tokens
+    k, v = wl.prefill(0, 150)
+    pr.prefill(0, k, v)
+    ok.prefill_quantize(pr.gpu, 0, dev_u16(k), dev_u16(v), wl.cfg.dtype)
+    torch.cuda.synchronize()
+    assert int(pr.gpu.error_flag.cpu()[0]) == ok.FLAG_NONEMPTY
+    assert pr.gpu.seq_state.cpu().numpy()[0].tolist() == [150, 32]
+    pr.gpu.error_flag.zero_()
+    # too many blocks for the table: rejected on the host
+    with pytest.raises(ok.OscarError):
+        big_k, big_v = wl.prefill(0, 399)
+        ok.prefill_quantize(pr.gpu, 0, dev_u16(big_k), dev_u16(big_v), wl.cfg.dtype)
+    # appends past capacity set the flag and are dropped, as in the oracle
+    for kn, vn, _ in wl.steps(120):
+        pr.append(kn, vn)
+    pr.compare_state()
+    assert int(pr.gpu.error_flag.cpu()[0]) == ok.FLAG_CAPACITY
+
+
+def _attn_case(wl, splits_list, variants, steps=1):
+    pr = Pair(wl)
+    for b in range(wl.cfg.batch):
+        k, v = wl.prefill(b)
+        pr.prefill(b, k, v)
+    worst = 0.0
+    for kn, vn, q in wl.steps(steps):
+        pr.append(kn, vn)
+        want, wlse = pr.orc.decode_attn(oracle.rotate_query(q, wl.cfg.dtype))
+        for var in variants:
+            for S in splits_list:
+                got, glse = pr.attend(q, variant=var, splits=S)
+                err = np.abs(got - want).max()
+                worst = max(worst, err)
+                assert err <= ATOL, (var, S, err)
+                assert np.abs(glse - wlse).max() <= 1e-3 * max(1.0, np.abs(wlse).max())
+    return worst
+
+
+@pytest.mark.parametrize("variant", [1])
+def test_attention_tiny_config(variant):
+    wl = synth.workload(0)
+    _attn_case(wl, [0, 1, 2, 7], [variant], steps=2)
+
+
+@pytest.mark.parametrize("variant", [1])
+@pytest.mark.parametrize("ctx", [1, 33, 129, 161, 2000])
+def test_attention_llama_shape_small(variant, ctx):
+    wl = synth.workload(1, ctx=ctx)
+    _attn_case(wl, [0, 3], [variant])
+
+
+@pytest.mark.parametrize("variant", [1])
+def test_attention_ragged_batch(variant):
+    wl = synth.workload(3, batch=4, ctx=None)
+    wl.ctx_lens = [4000, 129, 1500, 8200]
+    _attn_case(wl, [0, 5], [variant])
+
+
+def test_attention_prerotated_query():
+    wl = synth.workload(1, ctx=700)
+    pr = Pair(wl)
+    k, v = wl.prefill(0)
+    pr.prefill(0, k, v)
+    kn, vn, q = next(wl.steps(1))
+    pr.append(kn, vn)
+    qr = oracle.rotate_query(q, wl.cfg.dtype)
+    want, _ = pr.orc.decode_attn(qr)
+    got, _ = pr.attend(qr, q_dtype=ok.FP32, variant=1)
+    assert np.abs(got - want).max() <= ATOL
+
+
+def test_abi_rejects_bad_arguments():
+    g = ok.make_geom(1, 4, 1, 4, 4, head_dim=64)
+    with pytest.raises(ok.OscarError) as e:
+        ok.cache_layout(g)
+    assert e.value.status == ok.EINVAL
+    g = ok.make_geom(1, 6, 4, 4, 4)
+    with pytest.raises(ok.OscarError):
+        ok.cache_layout(g)
+    wl = synth.workload(0, ctx=100)
+    pr = Pair(wl)
+    S, nbytes = ok.decode_workspace_bytes(pr.geom, 100, 0)
+    small = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
+    out = torch.empty(1, 4, 128, dtype=torch.float32, device="cuda")
+    q = torch.zeros(1, 4, 128, dtype=torch.int16, device="cuda")
+    with pytest.raises(ok.OscarError) as e:
+        ok.decode_attn(pr.gpu, q, 0, out, None, small, 100, 0)
+    assert e.value.status == ok.EWORKSPACE

@@ -141,3 +141,14 @@ def test_quant_pack_roundtrip(orc):
                     off = 2560 + 4 * (4 * t + g)
                     assert r[off:off + 4].view(np.uint16)[0] == _f16(d)[()]
                     assert r[off:off + 4].view(np.uint16)[1] == _f16(z)[()]
+
+
+def test_signed_zero_minimum_is_canonical(orc):
+    """A group whose minimum is zero stores zero point +0 whichever signed zero
+    comes first (a parallel min must give the same bytes as a scan)."""
+    for first in (-0.0, 0.0):
+        x = np.full(32, 1.0)
+        x[0] = first
+        x[1] = -first
+        d, z, codes = orc.quant_group32(_f16(x))
+        assert _f16(z)[()] == 0 and codes[0] == 0 and codes[1] == 0
