@@ -189,7 +189,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int2 cache, fp32 math" if args.variant == 1 else "int2 cache, fp16 mfma / fp32 acc",
+        "dtype": ("int2 cache; fp32 vector math" if args.variant == 1 else
+                  "int2 cache; fp16 MFMA operands, fp32 accumulate"),
         "data": "synthetic (seeded; K outliers/sinks/log-normal norms, V and q N(0,1))",
         "config": {"workload": "qwen3-8b-shape decode, 128K ctx, batch 1",
                    "batch": 1, "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv,

@@ -98,7 +98,7 @@ typedef struct {
  *                             2*(4*((c>>4)&1) + ((t&7)>>1)) + 16*(t&1)
  *                 [2048,2304) K step (delta) fp16 [128]
  *                 [2304,2560) K zero point fp16 [128]
- *                 [2560,3072) V (step, zero) fp16 pairs, [32 tokens][4 groups]
+ *                 [2560,3072) V (step, zero) fp16 pairs, [4 groups][32 tokens]
  *   pool_norm   [num_physical_blocks][32] fp16 token norms
  *   res_k       [B][Hkv][128 slots][128] fp16 rotated+scaled keys (k_hat)
  *   res_v       [B][Hkv][128 channels][128 slots] fp16 values

@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs A) {
         if (quant) {
           const int g = c >> 5;
           for (int t = 0; t < 32; ++t) {
-            const uint32_t pz = st32[kRecVParam / 4 + 4 * t + g];
+            const uint32_t pz = st32[kRecVParam / 4 + 32 * g + t];
             const float dv = f16_to_f32(static_cast<uint16_t>(pz & 0xffffu));
             const float zv = f16_to_f32(static_cast<uint16_t>(pz >> 16));
             const int bit = vcode_bitpos(t, c);
@@ -215,29 +215,471 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs A) {
   }
 }
 
+// ---------------------------------------------------------------- MFMA
+// The GQA group's q.K^T and P.V products as v_mfma_f32_16x16x32_f16 tiles
+// (gfx950: A 16x32, lane l holds row l%16, K elements 8*(l/16)..+7; B 32x16,
+// lane l holds column l%16, K elements 8*(l/16)..+7; C 16x16, lane l holds
+// column l%16, rows 4*(l/16)..+3).
+//
+// Key side, per 32-token block: S^T[token, col] = sum_k A[token, k] B[k, col]
+//   A = INT2 codes as fp16 1 + code/4 (exact; two codes per 32-bit register
+//       straight from the packed word by one shift and one and-or),
+//   B = 4 * q'_h * delta in two fp16 parts: column h holds the high part,
+//       column h + GRP the low part (q' * delta to ~22 bits).
+//   Then q'.(z + delta * code) = C_hi + C_lo + kappa_h, kappa_h = q'.z - 4 sum q'*delta.
+// Value side: o^T[channel, col] += sum_t A[channel, t] B[t, col]
+//   A = V codes as fp16 1 + code/4, B = 4 * p * delta_v (hi/lo columns), and
+//   the zero points and the 1 offset go to a per-(group, head) scalar
+//   Z += sum_t p (z_v - 4 delta_v).
+// Every per-block operand (B tiles, kappa, probabilities) is computed once
+// per wave, spread over its 64 lanes, and exchanged through the wave's LDS.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+// Code pair P of a packed word (codes at bits 2P and 2P+16) as the fp16 pair
+// (1 + lo/4, 1 + hi/4).
+template <int P>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w) {
+  constexpr int sh = 2 * P - 8;
+  const uint32_t t = sh >= 0 ? (w >> (sh >= 0 ? sh : 0)) : (w << (sh < 0 ? -sh : 0));
+  return (t & 0x03000300u) | 0x3C003C00u;
+}
+// A operand from the 4 code pairs 4E..4E+3 of w.
+template <int E>
+__device__ __forceinline__ u32x4 code_tile(uint32_t w) {
+  return u32x4{code_pair<4 * E>(w), code_pair<4 * E + 1>(w), code_pair<4 * E + 2>(w),
+               code_pair<4 * E + 3>(w)};
+}
+
+// fp32 -> packed fp16 pair, rounding toward zero (used for hi/lo splits,
+// where the low part carries the remainder).
+__device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ float h_lo(uint32_t x) { return f16_to_f32(static_cast<uint16_t>(x)); }
+__device__ __forceinline__ float h_hi(uint32_t x) { return f16_to_f32(static_cast<uint16_t>(x >> 16)); }
+
+// Split 8 fp32 values into fp16 high and low parts.
+__device__ __forceinline__ void split8(const float* w, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint32_t h = pk_rtz(w[2 * v], w[2 * v + 1]);
+    hi[v] = h;
+    lo[v] = pk_rtz(w[2 * v] - h_lo(h), w[2 * v + 1] - h_hi(h));
+  }
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  // LDS operations of one wave execute in order; this only stops the compiler
+  // from moving LDS accesses across the exchange points.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int GRP>
+struct MfmaWaveLds {
+  u32x4 bk[4][64];    // Key-side B tiles, one per 32-channel step
+  u32x4 bv[4][64];    // Value-side B tiles, one per Value group
+  float sc[GRP][32];  // combined raw scores of the block
+  float pr[GRP][32];  // probabilities of the block
+  float kap[GRP];
+  float fac[GRP];
+  float zs[4][GRP];
+};
+
+template <int GRP>
+struct MfmaLds {
+  float qs[GRP * kD];         // rotated query heads
+  u32x4 bq[4][64];            // q' hi/lo B tiles for fp16 window chunks
+  MfmaWaveLds<GRP> w[4];
+  float wm[4][GRP], wl[4][GRP];
+  float wo[4][GRP][kD];
+};
+
+template <int GRP>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs A) {
+  static_assert(GRP == 1 || GRP == 2 || GRP == 4 || GRP == 8, "group size");
+  constexpr int NCOL = 2 * GRP;                 // used B columns (hi + lo)
+  constexpr int TPL = GRP >= 2 ? GRP / 2 : 1;   // softmax tokens per lane
+  constexpr int LPH = 32 / TPL;                 // softmax lanes per head
+  constexpr int NCOMBO = 16 * GRP;              // alpha / W units per block
+  constexpr int NR = (NCOMBO + 63) / 64;        // units per lane
+  constexpr float kScale = kInvSqrtD * kLog2e;
+  __shared__ MfmaLds<GRP> S;
+
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, L = tid & 63;
+  MfmaWaveLds<GRP>& W = S.w[wave];
+  int n = A.seq_state[2 * b], Q = A.seq_state[2 * b + 1];
+  if (!(Q >= 0 && (Q & 31) == 0 && n >= Q && n - Q <= kR && Q / kG <= A.max_blocks)) {
+    if (tid == 0 && s == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
+    n = Q = 0;
+  }
+  const int nb = Q / kG, nr = (n - Q + kG - 1) / kG, U = nb + nr;
+  const int u0 = static_cast<int>((static_cast<long long>(s) * U) / A.splits);
+  const int u1 = static_cast<int>((static_cast<long long>(s + 1) * U) / A.splits);
+  const size_t bh = static_cast<size_t>(b) * A.hkv + h;
+
+  load_rotated_q<GRP>(A, b, h, S.qs);
+  // zero this wave's B tiles (columns >= NCOL stay zero for good)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    W.bk[k][L] = u32x4{0, 0, 0, 0};
+    W.bv[k][L] = u32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+  const int col = L & 15, g4 = L >> 4;
+  if (wave == 0) {
+    // q' hi/lo tiles for fp16 window chunks: step kk, lane (col, g4) holds
+    // channels 32*g4 + 8*kk + 0..7.
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 v = {0, 0, 0, 0};
+      if (col < NCOL) {
+        float x[8];
+        const float* q = S.qs + (col % GRP) * kD + 32 * g4 + 8 * kk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = q[i];
+        u32x4 hi, lo;
+        split8(x, hi, lo);
+        v = col < GRP ? hi : lo;
+      }
+      S.bq[kk][L] = v;
+    }
+  }
+  // Per-lane constants of the alpha units: unit c = L + 64 r -> head c >> 4,
+  // channel group (c >> 2) & 3, step c & 3; K slot i of the step is channel
+  // c0 + (i >> 1) + 8 (i & 1), c0 = 32 g + 16 (kk >> 1) + 4 (kk & 1).
+  float qa[NR][8];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int c = L + 64 * r;
+    const int hh = (c >> 4) % GRP, g = (c >> 2) & 3, kk = c & 3;
+    const int c0 = 32 * g + 16 * (kk >> 1) + 4 * (kk & 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qa[r][i] = 4.0f * S.qs[hh * kD + c0 + (i >> 1) + 8 * (i & 1)];
+  }
+  __syncthreads();
+
+  // running state
+  float m_run = -INFINITY, l_part = 0.0f;
+  float zacc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) zacc[r] = 0.0f;
+  f32x4 o[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int sm_head = L / LPH, sm_t0 = TPL * (L % LPH);
+  const bool sm_on = sm_head < GRP;
+
+  for (int u = u0 + wave; u < u1; u += 4) {
+    const bool quant = u < nb;
+    int t_valid = 32;
+    float nt[TPL];
+    const uint8_t* rec = nullptr;
+    int slot0 = 0;
+    if (quant) {
+      int p = A.block_table[static_cast<size_t>(b) * A.max_blocks + u];
+      if (p < 0 || p >= A.nphys) {
+        if (L == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
+        p = 0;
+      }
+      rec = A.pool + (static_cast<size_t>(p) * A.hkv + h) * kRec;
+      const uint16_t* nrm = A.pool_norm + static_cast<size_t>(p) * 32;
+#pragma unroll
+      for (int j = 0; j < TPL; ++j) nt[j] = f16_to_f32(nrm[(sm_t0 + j) & 31]);
+      // alpha units: q' * delta split into hi/lo B tiles, kappa partials
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int c = L + 64 * r;
+        if (c < NCOMBO) {
+          const int hh = c >> 4, g = (c >> 2) & 3, kk = c & 3;
+          const int c0 = 32 * g + 16 * (kk >> 1) + 4 * (kk & 1);
+          const u32x2 dl = *reinterpret_cast<const u32x2*>(rec + kRecKDelta + 2 * c0);
+          const u32x2 dh = *reinterpret_cast<const u32x2*>(rec + kRecKDelta + 2 * c0 + 16);
+          const u32x2 zl = *reinterpret_cast<const u32x2*>(rec + kRecKZero + 2 * c0);
+          const u32x2 zh = *reinterpret_cast<const u32x2*>(rec + kRecKZero + 2 * c0 + 16);
+          // slot i: (i>>1) indexes the 4 consecutive channels, (i&1) picks +8
+          const float dv[8] = {h_lo(dl[0]), h_lo(dh[0]), h_hi(dl[0]), h_hi(dh[0]),
+                               h_lo(dl[1]), h_lo(dh[1]), h_hi(dl[1]), h_hi(dh[1])};
+          const float zv[8] = {h_lo(zl[0]), h_lo(zh[0]), h_hi(zl[0]), h_hi(zh[0]),
+                               h_lo(zl[1]), h_lo(zh[1]), h_hi(zl[1]), h_hi(zh[1])};
+          float w8[8];
+          float kq = 0.0f, ka = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            w8[i] = qa[r][i] * dv[i];
+            ka += w8[i];
+            kq += qa[r][i] * zv[i];
+          }
+          u32x4 hi, lo;
+          split8(w8, hi, lo);
+          W.bk[kk][hh + 16 * g] = hi;
+          W.bk[kk][hh + GRP + 16 * g] = lo;
+          float kap = 0.25f * kq - ka;
+#pragma unroll
+          for (int m = 1; m < 16; m <<= 1) kap += __shfl_xor(kap, m, 64);
+          if ((c & 15) == 0) W.kap[hh] = kap;
+        }
+      }
+    } else {
+      const int tb = Q + kG * (u - nb);
+      t_valid = n - tb < 32 ? n - tb : 32;
+      slot0 = tb % kR;
+#pragma unroll
+      for (int j = 0; j < TPL; ++j)
+        nt[j] = f16_to_f32(A.res_norm[static_cast<size_t>(b) * kR + slot0 + ((sm_t0 + j) & 31)]);
+    }
+    wave_lds_fence();
+
+    // ---- q.K^T on the matrix cores
+    f32x4 cs[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int t = 16 * tau + col;
+      if (quant) {
+        const u32x2 kw = *reinterpret_cast<const u32x2*>(rec + kRecKCodes + 32 * t + 8 * g4);
+        acc = mfma_f16(code_tile<0>(kw[0]), W.bk[0][L], acc);
+        acc = mfma_f16(code_tile<1>(kw[0]), W.bk[1][L], acc);
+        acc = mfma_f16(code_tile<0>(kw[1]), W.bk[2][L], acc);
+        acc = mfma_f16(code_tile<1>(kw[1]), W.bk[3][L], acc);
+      } else {
+        const u32x4* kr = reinterpret_cast<const u32x4*>(
+            A.res_k + (bh * kR + slot0 + t) * kD + 32 * g4);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma_f16(kr[kk], S.bq[kk][L], acc);
+      }
+      cs[tau] = acc;
+    }
+    // combine the hi and lo columns; column h < GRP holds head h
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      f32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = cs[tau][j] + __shfl_xor(cs[tau][j], GRP, 64);
+      if (col < GRP) *reinterpret_cast<f32x4*>(&W.sc[col][16 * tau + 4 * g4]) = v;
+    }
+    wave_lds_fence();
+
+    // ---- online softmax (log2 domain), TPL tokens per lane
+    float sv[TPL];
+    float bm = -INFINITY;
+    if (sm_on) {
+      const float kp = quant ? W.kap[sm_head] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < TPL; ++j) {
+        const int t = sm_t0 + j;
+        sv[j] = t < t_valid ? (W.sc[sm_head][t] + kp) * nt[j] * kScale : -INFINITY;
+        bm = fmaxf(bm, sv[j]);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPH; m <<= 1) bm = fmaxf(bm, __shfl_xor(bm, m, 64));
+    const float m_new = fmaxf(m_run, bm);
+    const bool grow = sm_on && m_new > m_run;
+    const float f = grow ? exp2f(m_run - m_new) : 1.0f;  // m_run = -inf gives 0
+    if (sm_on) {
+      float ps = 0.0f;
+#pragma unroll
+      for (int j = 0; j < TPL; ++j) {
+        const float pj = sv[j] == -INFINITY ? 0.0f : exp2f(sv[j] - m_new);
+        W.pr[sm_head][sm_t0 + j] = pj;
+        ps += pj;
+      }
+      l_part = l_part * f + ps;
+      if ((L % LPH) == 0) W.fac[sm_head] = f;
+    }
+    m_run = m_new;
+    const bool any_grow = __any(grow);
+    wave_lds_fence();
+    if (any_grow) {
+      const float fo = col < NCOL ? W.fac[col % GRP] : 1.0f;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) o[ct] *= fo;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int c = L + 64 * r;
+        if (c < NCOMBO) zacc[r] *= W.fac[(c >> 2) % GRP];
+      }
+    }
+
+    // ---- P.V operands: W units c -> group c / (4 GRP), head (c >> 2) % GRP,
+    // token octet c & 3
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int c = L + 64 * r;
+      if (c < NCOMBO) {
+        const int gv = c / (4 * GRP), hh = (c >> 2) % GRP, g8 = c & 3;
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(&W.pr[hh][8 * g8]);
+        const f32x4 p1 = *reinterpret_cast<const f32x4*>(&W.pr[hh][8 * g8 + 4]);
+        const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        float w8[8];
+        if (quant) {
+          const u32x4* vp = reinterpret_cast<const u32x4*>(rec + kRecVParam + 4 * (32 * gv + 8 * g8));
+          const u32x4 v0 = vp[0], v1 = vp[1];
+          const uint32_t pz[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          float zsum = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float dvk = h_lo(pz[k]), zvk = h_hi(pz[k]);
+            w8[k] = 4.0f * pv[k] * dvk;
+            zsum += pv[k] * (zvk - 4.0f * dvk);
+          }
+          zacc[r] += zsum;
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) w8[k] = pv[k];
+        }
+        u32x4 hi, lo;
+        split8(w8, hi, lo);
+        W.bv[gv][hh + 16 * g8] = hi;
+        W.bv[gv][hh + GRP + 16 * g8] = lo;
+      }
+    }
+    wave_lds_fence();
+
+    // ---- P.V on the matrix cores: tile ct = channels 16 ct .. 16 ct + 15
+    if (quant) {
+      const u32x4 vw = *reinterpret_cast<const u32x4*>(rec + kRecVCodes + 16 * L);
+      const u32x4 b0 = W.bv[0][L], b1 = W.bv[1][L], b2 = W.bv[2][L], b3 = W.bv[3][L];
+      o[0] = mfma_f16(code_tile<0>(vw[0]), b0, o[0]);
+      o[1] = mfma_f16(code_tile<1>(vw[0]), b0, o[1]);
+      o[2] = mfma_f16(code_tile<0>(vw[1]), b1, o[2]);
+      o[3] = mfma_f16(code_tile<1>(vw[1]), b1, o[3]);
+      o[4] = mfma_f16(code_tile<0>(vw[2]), b2, o[4]);
+      o[5] = mfma_f16(code_tile<1>(vw[2]), b2, o[5]);
+      o[6] = mfma_f16(code_tile<0>(vw[3]), b3, o[6]);
+      o[7] = mfma_f16(code_tile<1>(vw[3]), b3, o[7]);
+    } else {
+      const u32x4 b0 = W.bv[0][L];
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const u32x4 va = *reinterpret_cast<const u32x4*>(
+            A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
+        o[ct] = mfma_f16(va, b0, o[ct]);
+      }
+    }
+  }
+
+  // ---- wave partial: l, Z, o for each head
+  float lsum = l_part;
+#pragma unroll
+  for (int m = 1; m < LPH; m <<= 1) lsum += __shfl_xor(lsum, m, 64);
+  if (sm_on && (L % LPH) == 0) {
+    S.wm[wave][sm_head] = m_run;
+    S.wl[wave][sm_head] = lsum;
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int c = L + 64 * r;
+    float z = zacc[r];
+    z += __shfl_xor(z, 1, 64);
+    z += __shfl_xor(z, 2, 64);
+    if (c < NCOMBO && (c & 3) == 0) W.zs[c / (4 * GRP)][(c >> 2) % GRP] = z;
+  }
+  wave_lds_fence();
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v = o[ct][j] + __shfl_xor(o[ct][j], GRP, 64);
+      if (col < GRP) S.wo[wave][col][16 * ct + 4 * g4 + j] = v + W.zs[ct >> 1][col];
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the 4 waves into this split's partial
+  const size_t pbase = (static_cast<size_t>(b) * A.hq + h * GRP) * A.splits;
+  for (int idx = tid; idx < GRP * kD; idx += 256) {
+    const int hh = idx >> 7, c = idx & 127;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, S.wm[w][hh]);
+    float Lw = 0.0f, Ow = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = S.wm[w][hh];
+        if (mw == -INFINITY) continue;
+        const float sc = exp2f(mw - M);
+        Lw += sc * S.wl[w][hh];
+        Ow += sc * S.wo[w][hh][c];
+      }
+    }
+    const size_t part = pbase + static_cast<size_t>(hh) * A.splits + s;
+    A.ws_o[part * kD + c] = Ow;
+    if (c == 0) A.ws_ml[part] = make_float2(M, Lw);
+  }
+}
+
 // ---------------------------------------------------------------- reduce
-// grid (Hq, B), 128 threads: merge the S partials of one query head.
-__global__ __launch_bounds__(128) void lse_reduce_kernel(const float2* __restrict__ ws_ml,
+// grid (Hq, B), 256 threads: merge the S partials of one query head.  Thread
+// t takes channels 4*(t&31)..+3 of the splits s = t>>5, t>>5 + 8, ...; the 8
+// split lanes are then summed through LDS.
+__global__ __launch_bounds__(256) void lse_reduce_kernel(const float2* __restrict__ ws_ml,
                                                          const float* __restrict__ ws_o, int hq,
                                                          int splits, float* __restrict__ out,
                                                          float* __restrict__ lse) {
-  const int i = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  __shared__ float red_m[256];
+  __shared__ float4 red_o[8][32];
+  __shared__ float red_l[8];
+  const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const size_t base = (static_cast<size_t>(b) * hq + i) * splits;
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_ml[base + s].x);
-  float L = 0.0f, acc = 0.0f;
+  for (int s = t; s < splits; s += 256) M = fmaxf(M, ws_ml[base + s].x);
+  red_m[t] = M;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) red_m[t] = fmaxf(red_m[t], red_m[t + w]);
+    __syncthreads();
+  }
+  M = red_m[0];
+  const int cg = t & 31, sl = t >> 5;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.0f;
   if (M != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
+    for (int s = sl; s < splits; s += 8) {
       const float2 ml = ws_ml[base + s];
-      if (ml.x == -INFINITY) continue;
-      const float w = exp2f(ml.x - M);
+      const float w = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
+      const float4 v = reinterpret_cast<const float4*>(ws_o + (base + s) * kD)[cg];
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
       L += w * ml.y;
-      acc += w * ws_o[(base + s) * kD + c];
     }
   }
-  out[(static_cast<size_t>(b) * hq + i) * kD + c] = M == -INFINITY ? 0.0f : acc / L;
-  if (lse && c == 0)
-    lse[static_cast<size_t>(b) * hq + i] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * 0.6931471805599453f;
+  red_o[sl][cg] = acc;
+  if (cg == 0) red_l[sl] = L;
+  __syncthreads();
+  if (t < 32) {
+    float4 a = red_o[0][t];
+    float Lt = red_l[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      const float4 v = red_o[k][t];
+      a.x += v.x;
+      a.y += v.y;
+      a.z += v.z;
+      a.w += v.w;
+      Lt += red_l[k];
+    }
+    const bool empty = M == -INFINITY;
+    const float inv = empty ? 0.0f : 1.0f / Lt;
+    reinterpret_cast<float4*>(out + (static_cast<size_t>(b) * hq + i) * kD)[t] =
+        make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    if (lse && t == 0)
+      lse[static_cast<size_t>(b) * hq + i] = empty ? -INFINITY : (M + log2f(Lt)) * 0.6931471805599453f;
+  }
 }
 
 int auto_splits(const oscar_cache_geom* g, int max_ctx) {
@@ -256,8 +698,11 @@ size_t workspace_bytes(const oscar_cache_geom* g, int splits) {
 }
 
 template <int GRP>
-void launch_valu(const AttnArgs& A, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL(attn_valu_kernel<GRP>, grid, dim3(256), 0, st, A);
+void launch_attn(const AttnArgs& A, dim3 grid, hipStream_t st, bool mfma) {
+  if (mfma)
+    hipLaunchKernelGGL(attn_mfma_kernel<GRP>, grid, dim3(256), 0, st, A);
+  else
+    hipLaunchKernelGGL(attn_valu_kernel<GRP>, grid, dim3(256), 0, st, A);
 }
 
 }  // namespace oscar
@@ -317,16 +762,16 @@ extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const os
   const dim3 grid(S, geom->num_kv_heads, geom->batch);
   hipStream_t hs = as_stream(stream);
   const int grp = geom->num_q_heads / geom->num_kv_heads;
-  (void)variant;
+  const bool mfma = variant != OSCAR_ATTN_VALU;
   switch (grp) {
-    case 1: launch_valu<1>(A, grid, hs); break;
-    case 2: launch_valu<2>(A, grid, hs); break;
-    case 4: launch_valu<4>(A, grid, hs); break;
-    default: launch_valu<8>(A, grid, hs); break;
+    case 1: launch_attn<1>(A, grid, hs, mfma); break;
+    case 2: launch_attn<2>(A, grid, hs, mfma); break;
+    case 4: launch_attn<4>(A, grid, hs, mfma); break;
+    default: launch_attn<8>(A, grid, hs, mfma); break;
   }
   st = launch_status();
   if (st != OSCAR_OK) return st;
-  hipLaunchKernelGGL(lse_reduce_kernel, dim3(geom->num_q_heads, geom->batch), dim3(128), 0, hs,
+  hipLaunchKernelGGL(lse_reduce_kernel, dim3(geom->num_q_heads, geom->batch), dim3(256), 0, hs,
                      A.ws_ml, A.ws_o, geom->num_q_heads, S, out, lse);
   return launch_status();
 }

@@ -42,7 +42,7 @@ __device__ __forceinline__ void quant_record_units(int tg, KGet kget, VGet vget,
       const int bit = vcode_bitpos(t, 32 * g + i);
       atomicOr(&img[256 + (bit >> 5)], static_cast<uint32_t>((codes >> (2 * i)) & 3u) << (bit & 31));
     }
-    reinterpret_cast<uint32_t*>(rec + kRecVParam)[4 * t + g] =
+    reinterpret_cast<uint32_t*>(rec + kRecVParam)[32 * g + t] =
         static_cast<uint32_t>(f32_to_f16(d)) | (static_cast<uint32_t>(f32_to_f16(z)) << 16);
   }
 }
@@ -288,9 +288,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(CacheArgs ca, int seq,
           uint32_t* vp = reinterpret_cast<uint32_t*>(rec + kRecVParam);
           if ((lane & 31) == 0) {
             const int g = lane >> 5;
-            vp[4 * tt + g] = static_cast<uint32_t>(f32_to_f16(da)) |
+            vp[32 * g + tt] = static_cast<uint32_t>(f32_to_f16(da)) |
                              (static_cast<uint32_t>(f32_to_f16(za)) << 16);
-            vp[4 * tt + 2 + g] = static_cast<uint32_t>(f32_to_f16(db)) |
+            vp[32 * (2 + g) + tt] = static_cast<uint32_t>(f32_to_f16(db)) |
                                  (static_cast<uint32_t>(f32_to_f16(zb)) << 16);
           }
         }

@@ -257,7 +257,9 @@ void orc_quant_group32(const uint16_t *x16, size_t stride, float *delta,
  *   puts the 8 codes of 8 consecutive tokens of one channel next to each
  *   other, which is the order a token-contracting matrix tile consumes.)
  * K step/zero: fp16 [128] each at 2048 / 2304.
- * V step/zero: fp16 pairs (step, zero) at 2560 + 4*(4*t + g), g = c >> 5.
+ * V step/zero: fp16 pairs (step, zero) at 2560 + 4*(32*g + t), g = c >> 5
+ *   (group-major, so the pairs of 8 consecutive tokens of one group are 32
+ *   contiguous bytes).
  */
 size_t orc_kcode_byte(int t, int c) { return (size_t)(32 * t + (c >> 2)); }
 int orc_kcode_shift(int t, int c)
@@ -328,8 +330,8 @@ static void quant_record(const uint16_t *khat, size_t k_tstride,
                 int c = g * ORC_VG + i;
                 rec[orc_vcode_byte(t, c)] |= (uint8_t)(codes[i] << orc_vcode_shift(t, c));
             }
-            put_u16(rec + ORC_REC_VPARAM + 4 * (4 * t + g), orc_f32_to_f16(d));
-            put_u16(rec + ORC_REC_VPARAM + 4 * (4 * t + g) + 2, orc_f32_to_f16(z));
+            put_u16(rec + ORC_REC_VPARAM + 4 * (32 * g + t), orc_f32_to_f16(d));
+            put_u16(rec + ORC_REC_VPARAM + 4 * (32 * g + t) + 2, orc_f32_to_f16(z));
         }
     }
 }
@@ -508,7 +510,7 @@ void orc_value_row(const orc_cache *c, int b, int h, int t, double *out)
         const uint8_t *rec = pool_rec(c, p, h);
         int tt = t % ORC_G;
         for (int ch = 0; ch < ORC_D; ch++) {
-            const uint8_t *pp = rec + ORC_REC_VPARAM + 4 * (4 * tt + ch / ORC_VG);
+            const uint8_t *pp = rec + ORC_REC_VPARAM + 4 * (32 * (ch / ORC_VG) + tt);
             double d = orc_f16_to_f32(get_u16(pp));
             double z = orc_f16_to_f32(get_u16(pp + 2));
             out[ch] = z + d * orc_vcode_get(rec, tt, ch);

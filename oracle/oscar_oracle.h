@@ -43,7 +43,7 @@ enum {
     ORC_REC_VCODES = 1024,  /* 1024 B: 32 tokens x 128 channels x 2 bit */
     ORC_REC_KDELTA = 2048,  /* 128 x fp16 step per channel */
     ORC_REC_KZERO = 2304,   /* 128 x fp16 zero point per channel */
-    ORC_REC_VPARAM = 2560   /* [32 tokens][4 groups] x (step, zero) fp16 */
+    ORC_REC_VPARAM = 2560   /* [4 groups][32 tokens] x (step, zero) fp16 */
 };
 
 /* The cache state.  Every array is caller-owned, zero-initialised. */

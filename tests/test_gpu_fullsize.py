@@ -1,0 +1,64 @@
+"""GPU parity at the workloads' full sizes, in the benchmark's launch
+configuration: whole-cache bit-exact comparison after prefill + one append,
+attention outputs on sampled query heads (the oracle computes them one by
+one), and the edge cases that only appear at size."""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a gfx950 GPU")]
+
+if gpu_available():
+    import torch
+    import int2_kv_cache_amd as ok
+    import oracle
+    from int2_kv_cache_amd import synth
+    from _parity import ATOL, Pair
+
+
+def _run(wl, heads, variants=(2, 1), bench_max_ctx=None):
+    pr = Pair(wl)
+    for b in range(wl.cfg.batch):
+        k, v = wl.prefill(b)
+        pr.prefill(b, k, v)
+    kn, vn, q = next(wl.steps(1))
+    pr.append(kn, vn)
+    pr.compare_state()
+    qr = oracle.rotate_query(q, wl.cfg.dtype)
+    res = {}
+    for var in variants:
+        got, glse = pr.attend(q, variant=var, max_ctx=bench_max_ctx)
+        for (b, i) in heads:
+            want, wlse = pr.orc.decode_attn_one(qr, b, i)
+            err = float(np.abs(got[b, i] - want).max())
+            assert err <= ATOL, (var, b, i, err)
+            assert abs(float(glse[b, i]) - float(wlse)) <= 1e-3 * max(1.0, abs(float(wlse)))
+            res[(var, b, i)] = err
+    return res
+
+
+def test_qwen3_8b_128k_bench_configuration():
+    """131071 prefilled tokens + 1 append: 130944 INT2 + 128 fp16; the split
+    count is the one bench.py uses (max_ctx = ctx + 105 steps + 64)."""
+    wl = synth.workload(2)
+    _run(wl, [(0, 0), (0, 5), (0, 17), (0, 31)], bench_max_ctx=131072 + 105 + 64)
+
+
+def test_llama_8b_32k():
+    wl = synth.workload(1)
+    _run(wl, [(0, 0), (0, 13), (0, 30)])
+
+
+def test_multimodal_64k_prefill_and_decode():
+    """Segments of x1 / x5 / x0.3 token norms plus 0.1% x30 tokens."""
+    wl = synth.workload(4)
+    _run(wl, [(0, 1), (0, 22)])
+
+
+def test_ragged_batch_8k_32k():
+    """Six sequences with contexts drawn from 8K..32K, block-table indexed."""
+    wl = synth.workload(3, batch=6)
+    wl.ctx_lens = wl.ctx_lens[:6]
+    _run(wl, [(b, (7 * b) % 32) for b in range(6)])

@@ -152,24 +152,38 @@ def _attn_case(wl, splits_list, variants, steps=1):
     return worst
 
 
-@pytest.mark.parametrize("variant", [1])
+VARIANTS = [1, 2]   # VALU, MFMA
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_attention_tiny_config(variant):
     wl = synth.workload(0)
     _attn_case(wl, [0, 1, 2, 7], [variant], steps=2)
 
 
-@pytest.mark.parametrize("variant", [1])
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("ctx", [1, 33, 129, 161, 2000])
 def test_attention_llama_shape_small(variant, ctx):
     wl = synth.workload(1, ctx=ctx)
     _attn_case(wl, [0, 3], [variant])
 
 
-@pytest.mark.parametrize("variant", [1])
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_attention_ragged_batch(variant):
     wl = synth.workload(3, batch=4, ctx=None)
     wl.ctx_lens = [4000, 129, 1500, 8200]
     _attn_case(wl, [0, 5], [variant])
+
+
+@pytest.mark.parametrize("grp", [1, 2, 8])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_attention_group_sizes(variant, grp):
+    """GQA groups of 1, 2 and 8 query heads per KV head (the workloads use 4)."""
+    wl = synth.workload(1, ctx=700)
+    hkv = 8 if grp <= 2 else 2
+    cfg = synth.Config("grp", 1, hkv * grp, hkv, 700, synth.BF16, 0.3, (4, 4), 1)
+    wl2 = synth.Workload(cfg, 77, [700], wl.outlier_idx[:hkv])
+    _attn_case(wl2, [0, 3], [variant], steps=1)
 
 
 def test_attention_prerotated_query():

@@ -138,7 +138,7 @@ def test_quant_pack_roundtrip(orc):
                     d, z, codes = orc.quant_group32(v16[32 * j + t, h, 32 * g:32 * g + 32])
                     got = [orc.vcode_get(r, t, 32 * g + i) for i in range(32)]
                     assert got == list(codes)
-                    off = 2560 + 4 * (4 * t + g)
+                    off = 2560 + 4 * (32 * g + t)
                     assert r[off:off + 4].view(np.uint16)[0] == _f16(d)[()]
                     assert r[off:off + 4].view(np.uint16)[1] == _f16(z)[()]
 
