@@ -56,7 +56,23 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="query heads of the oracle sample (scaled to all heads)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 times) and "
+                         "exit: the reference for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def copy_probe(mib: int):
+    """A plain device-to-device copy of known size, for calibrating the
+    FETCH_SIZE / WRITE_SIZE counters against the attention kernel's."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)   # elementwise kernel: reads and writes n*4 bytes
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n * 4, "calls": 5}), flush=True)
 
 
 def cpu_baseline(wl, k, v, steps, hq, args):
@@ -89,6 +105,9 @@ def cpu_baseline(wl, k, v, steps, hq, args):
 
 def main():
     args = parse()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "
               "(see DESIGN.md for how it would shard)", file=sys.stderr)

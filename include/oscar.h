@@ -94,8 +94,9 @@ typedef struct {
  *                 [0,1024)    K codes: channel c of token t at bits 2*(c&3) of
  *                             byte 32*t + (c>>2)
  *                 [1024,2048) V codes: slice 16*(t>>3) + (c&15) of 16 bytes at
- *                             1024 + 16*slice; 32-bit word c>>5 of it; bit
- *                             2*(4*((c>>4)&1) + ((t&7)>>1)) + 16*(t&1)
+ *                             1024 + 16*slice; 32-bit word c>>5 of it; bits
+ *                             2m, 2m+1 with m = 8*((c>>4)&1) + s(t&7), s(k)
+ *                             = k with its two low bits swapped
  *                 [2048,2304) K step (delta) fp16 [128]
  *                 [2304,2560) K zero point fp16 [128]
  *                 [2560,3072) V (step, zero) fp16 pairs, [4 groups][32 tokens]

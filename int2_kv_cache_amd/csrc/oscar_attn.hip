@@ -222,17 +222,21 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs A) {
 // column l%16, rows 4*(l/16)..+3).
 //
 // Key side, per 32-token block: S^T[token, col] = sum_k A[token, k] B[k, col]
-//   A = INT2 codes as fp16 1 + code/4 (exact; two codes per 32-bit register
-//       straight from the packed word by one shift and one and-or),
-//   B = 4 * q'_h * delta in two fp16 parts: column h holds the high part,
-//       column h + GRP the low part (q' * delta to ~22 bits).
-//   Then q'.(z + delta * code) = C_hi + C_lo + kappa_h, kappa_h = q'.z - 4 sum q'*delta.
-// Value side: o^T[channel, col] += sum_t A[channel, t] B[t, col]
-//   A = V codes as fp16 1 + code/4, B = 4 * p * delta_v (hi/lo columns), and
-//   the zero points and the 1 offset go to a per-(group, head) scalar
-//   Z += sum_t p (z_v - 4 delta_v).
-// Every per-block operand (B tiles, kappa, probabilities) is computed once
-// per wave, spread over its 64 lanes, and exchanged through the wave's LDS.
+//   A = INT2 codes as exact fp16 0..3: a packed word is split into its even
+//       and odd 2-bit fields (one and, one shift+and), and each byte of those
+//       converts to two fp16 codes with one fp4->fp16 instruction (the fields
+//       are e2m1 values code/2, scaled by 2);
+//   B = q'_h * delta in two fp16 parts: column h holds the high part, column
+//       h + GRP the low part, so q' * delta enters to ~22 bits.
+//   The score's zero-point term q'.z is a per-head scalar added afterwards.
+// Value side: o^T[channel, col] += sum_t A[channel, t] B[t, col] with
+//   A = V codes (fp16 0..3), B = p * delta_v (hi/lo columns); the zero points
+//   add a per-(group, head) scalar Z += sum_t p * z_v.
+// One MFMA step covers 8 consecutive channels (Key) or tokens (Value) in the
+// slot order s = 0,2,1,3,4,6,5,7 that the even/odd split produces.
+// Every per-block operand (B tiles, q'.z, probabilities) is computed once per
+// wave, spread over its 64 lanes, and exchanged through the wave's LDS.  The
+// next block's global data is loaded while the current one is processed.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -243,80 +247,213 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
                                                 __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
 }
 
-// Code pair P of a packed word (codes at bits 2P and 2P+16) as the fp16 pair
-// (1 + lo/4, 1 + hi/4).
-template <int P>
-__device__ __forceinline__ uint32_t code_pair(uint32_t w) {
-  constexpr int sh = 2 * P - 8;
-  const uint32_t t = sh >= 0 ? (w >> (sh >= 0 ? sh : 0)) : (w << (sh < 0 ? -sh : 0));
-  return (t & 0x03000300u) | 0x3C003C00u;
+template <int BYTE>
+__device__ __forceinline__ uint32_t fp4x2_to_f16x2(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, BYTE));
 }
-// A operand from the 4 code pairs 4E..4E+3 of w.
-template <int E>
-__device__ __forceinline__ u32x4 code_tile(uint32_t w) {
-  return u32x4{code_pair<4 * E>(w), code_pair<4 * E + 1>(w), code_pair<4 * E + 2>(w),
-               code_pair<4 * E + 3>(w)};
+// A operand of half H (positions 8H..8H+7) of a 16-code word, from its even
+// (e) and odd (o) 2-bit fields: slot i holds position 8H + s(i).
+template <int H>
+__device__ __forceinline__ u32x4 code_tile(uint32_t e, uint32_t o) {
+  return u32x4{fp4x2_to_f16x2<2 * H>(e), fp4x2_to_f16x2<2 * H>(o),
+               fp4x2_to_f16x2<2 * H + 1>(e), fp4x2_to_f16x2<2 * H + 1>(o)};
+}
+__device__ __forceinline__ uint32_t even_fields(uint32_t w) { return w & 0x33333333u; }
+__device__ __forceinline__ uint32_t odd_fields(uint32_t w) { return (w >> 2) & 0x33333333u; }
+__device__ __forceinline__ constexpr int slot_pos(int i) {
+  return (i & 4) | ((i & 1) << 1) | ((i >> 1) & 1);
 }
 
-// fp32 -> packed fp16 pair, rounding toward zero (used for hi/lo splits,
-// where the low part carries the remainder).
+// Cross-lane moves inside a row of 16 lanes (DPP): quad_perm [1,0,3,2] and
+// [2,3,0,1] swap neighbours and pairs, row_half_mirror and row_mirror reverse
+// 8 and 16 lanes, row_shl:n reads lane l + n.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  // bound_ctrl: a lane whose source is outside the row reads 0
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int dpp_row_shl(int n) { return 0x100 + n; }
+
+// max / sum over aligned groups of N lanes; every lane of a group gets the result
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  if (N >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+  if (N >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+  if (N >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  if (N >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+  if (N >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+  if (N >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if (N >= 2) v += dpp<kDppXor1>(v);
+  if (N >= 4) v += dpp<kDppXor2>(v);
+  if (N >= 8) v += dpp<kDppHalfMirror>(v);
+  if (N >= 16) v += dpp<kDppMirror>(v);
+  if (N >= 32) v += __shfl_xor(v, 16, 64);
+  if (N >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// fp32 -> packed fp16 pair, rounding toward zero (hi/lo splits: the low part
+// carries the remainder).
 __device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 __device__ __forceinline__ float h_lo(uint32_t x) { return f16_to_f32(static_cast<uint16_t>(x)); }
 __device__ __forceinline__ float h_hi(uint32_t x) { return f16_to_f32(static_cast<uint16_t>(x >> 16)); }
+__device__ __forceinline__ float h_at(const u32x4& v, int j) {
+  return (j & 1) ? h_hi(v[j >> 1]) : h_lo(v[j >> 1]);
+}
 
-// Split 8 fp32 values into fp16 high and low parts.
+// Low parts of a hi/lo split: fp16(w0 - hi.lo) into the low half and
+// fp16(w1 - hi.hi) into the high half, each from one fused mixed-precision
+// multiply-add (w * 1 - hi, rounded once to fp16).
+__device__ __forceinline__ uint32_t lo_pair(float w0, float w1, uint32_t hi) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(r)
+      : "v"(w0), "v"(w1), "v"(hi));
+  return r;
+}
+
 __device__ __forceinline__ void split8(const float* w, u32x4& hi, u32x4& lo) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const uint32_t h = pk_rtz(w[2 * v], w[2 * v + 1]);
     hi[v] = h;
-    lo[v] = pk_rtz(w[2 * v] - h_lo(h), w[2 * v + 1] - h_hi(h));
+    lo[v] = lo_pair(w[2 * v], w[2 * v + 1], h);
   }
 }
 
-__device__ __forceinline__ void wave_lds_fence() {
-  // LDS operations of one wave execute in order; this only stops the compiler
-  // from moving LDS accesses across the exchange points.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// hi/lo fp16 parts of the 8 products a[i] * b[i] (a fp32, b fp16):
+// hi = fp16 of the fp32 product (toward zero), lo = fp16(a*b - hi).
+__device__ __forceinline__ void split8_mul(const float* a, const _Float16* b, u32x4& hi,
+                                           u32x4& lo) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float w0 = __builtin_fmaf(a[2 * v], static_cast<float>(b[2 * v]), 0.0f);
+    const float w1 = __builtin_fmaf(a[2 * v + 1], static_cast<float>(b[2 * v + 1]), 0.0f);
+    const uint32_t h = pk_rtz(w0, w1);
+    hi[v] = h;
+    lo[v] = lo_pair(w0, w1, h);
+  }
 }
+__device__ __forceinline__ _Float16 hbits(uint32_t x, int hi) {
+  return __builtin_bit_cast(_Float16, static_cast<uint16_t>(hi ? (x >> 16) : x));
+}
+
+// LDS operations of one wave execute in order, so lanes exchanging data
+// through LDS only need the compiler to keep the accesses in program order.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+// B tiles are stored with their 16-byte rows permuted (XOR swizzle) so that
+// both the writers (lanes grouped by unit) and the readers (lane l reads row
+// l) touch 8 different 16-byte bank groups in every group of 8 lanes.
+__device__ __forceinline__ int bk_row(int x) { return x ^ (4 * ((x >> 4) & 1)); }
+__device__ __forceinline__ int bv_row(int x) { return x ^ (2 * ((x >> 4) & 3)); }
+constexpr int kRowPad = 36;  // score / probability rows: 32 floats + 4 of padding
 
 template <int GRP>
 struct MfmaWaveLds {
-  u32x4 bk[4][64];    // Key-side B tiles, one per 32-channel step
-  u32x4 bv[4][64];    // Value-side B tiles, one per Value group
-  float sc[GRP][32];  // combined raw scores of the block
-  float pr[GRP][32];  // probabilities of the block
-  float kap[GRP];
-  float fac[GRP];
+  u32x4 bk[4][64];          // Key-side B tiles, one per 8-channel step of each group
+  u32x4 bv[4][64];          // Value-side B tiles, one per Value group
+  float sc[GRP][kRowPad];   // combined raw scores of the block
+  float pr[GRP][kRowPad];   // probabilities of the block
+  float fac[GRP];           // rescale factor per head
   float zs[4][GRP];
 };
 
 template <int GRP>
-struct MfmaLds {
-  float qs[GRP * kD];         // rotated query heads
-  u32x4 bq[4][64];            // q' hi/lo B tiles for fp16 window chunks
-  MfmaWaveLds<GRP> w[4];
+struct MfmaMerge {
   float wm[4][GRP], wl[4][GRP];
   float wo[4][GRP][kD];
 };
 
 template <int GRP>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs A) {
+struct MfmaLds {
+  float qs[GRP * kD];  // rotated query heads
+  u32x4 bq[4][64];     // q' hi/lo B tiles for fp16 window chunks
+  union {
+    MfmaWaveLds<GRP> w[4];
+    MfmaMerge<GRP> m;
+  };
+};
+
+// Global data one lane needs for one INT2 block.
+// Unit assignments of one block's per-lane work (c = L + 64 r):
+//   alpha unit c: head c % GRP, channel group (c / GRP) & 3, step c / (4 GRP);
+//   W unit c:     token octet c & 3, head (c >> 2) % GRP, Value group
+//                 c / (4 GRP);
+//   softmax lane L: head L / LPH, tokens TPL * (L % LPH) .. +TPL-1, and the
+//                 zero-point channels CPL * (L % LPH) .. +CPL-1 of q'.z.
+template <int NR, int CPL>
+struct UnitRegs {
+  u32x2 kc[2];   // Key codes of tokens col, 16 + col: channels 32 g4 .. +31
+  u32x4 vc;      // Value codes: slice L
+  u32x4 dz[NR];  // delta of the alpha unit's 8 channels
+  u32x4 vp[NR][2];  // (delta_v, z_v) of the W unit's 8 tokens
+  u32x4 zz[(CPL + 7) / 8];  // zero points of the softmax lane's channels
+  u32x2 nrm;     // token norms of the softmax lane
+};
+
+template <int GRP, int NR, int TPL, int CPL>
+__device__ __forceinline__ void load_unit(UnitRegs<NR, CPL>& R, const uint8_t* rec,
+                                          const uint16_t* nrm, int L, int sm_t0, int sm_c0) {
+  constexpr int NCOMBO = 16 * GRP;
+  const int col = L & 15, g4 = L >> 4;
+  R.kc[0] = *reinterpret_cast<const u32x2*>(rec + kRecKCodes + 32 * col + 8 * g4);
+  R.kc[1] = *reinterpret_cast<const u32x2*>(rec + kRecKCodes + 32 * (16 + col) + 8 * g4);
+  R.vc = *reinterpret_cast<const u32x4*>(rec + kRecVCodes + 16 * L);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int c = L + 64 * r;
+    if (c < NCOMBO) {
+      const int c0 = 32 * ((c / GRP) & 3) + 8 * (c / (4 * GRP));
+      R.dz[r] = *reinterpret_cast<const u32x4*>(rec + kRecKDelta + 2 * c0);
+      const int gv = c / (4 * GRP), g8 = c & 3;
+      const u32x4* vp = reinterpret_cast<const u32x4*>(rec + kRecVParam + 4 * (32 * gv + 8 * g8));
+      R.vp[r][0] = vp[0];
+      R.vp[r][1] = vp[1];
+    }
+  }
+  if (CPL >= 8) {
+#pragma unroll
+    for (int j = 0; j < (CPL + 7) / 8; ++j)
+      R.zz[j] = *reinterpret_cast<const u32x4*>(rec + kRecKZero + 2 * (sm_c0 + 8 * j));
+  } else {
+    const u32x2 z2 = *reinterpret_cast<const u32x2*>(rec + kRecKZero + 2 * sm_c0);
+    R.zz[0] = u32x4{z2[0], z2[1], 0u, 0u};
+  }
+  if (TPL == 4)
+    R.nrm = *reinterpret_cast<const u32x2*>(nrm + sm_t0);
+  else if (TPL == 2)
+    R.nrm[0] = *reinterpret_cast<const uint32_t*>(nrm + sm_t0);
+  else
+    R.nrm[0] = nrm[sm_t0 & 31];
+}
+
+template <int GRP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void attn_mfma_kernel(AttnArgs A) {
   static_assert(GRP == 1 || GRP == 2 || GRP == 4 || GRP == 8, "group size");
   constexpr int NCOL = 2 * GRP;                 // used B columns (hi + lo)
   constexpr int TPL = GRP >= 2 ? GRP / 2 : 1;   // softmax tokens per lane
   constexpr int LPH = 32 / TPL;                 // softmax lanes per head
   constexpr int NCOMBO = 16 * GRP;              // alpha / W units per block
   constexpr int NR = (NCOMBO + 63) / 64;        // units per lane
+  constexpr int CPL = kD / LPH;                 // q'.z channels per softmax lane
   constexpr float kScale = kInvSqrtD * kLog2e;
   __shared__ MfmaLds<GRP> S;
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, L = tid & 63;
+  // wave index as a wave-uniform (scalar) value: unit indices and block-table
+  // reads then stay in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), L = tid & 63;
   MfmaWaveLds<GRP>& W = S.w[wave];
   int n = A.seq_state[2 * b], Q = A.seq_state[2 * b + 1];
   if (!(Q >= 0 && (Q & 31) == 0 && n >= Q && n - Q <= kR && Q / kG <= A.max_blocks)) {
@@ -327,19 +464,24 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs A) {
   const int u0 = static_cast<int>((static_cast<long long>(s) * U) / A.splits);
   const int u1 = static_cast<int>((static_cast<long long>(s + 1) * U) / A.splits);
   const size_t bh = static_cast<size_t>(b) * A.hkv + h;
+  // the block table is read-only here: read it through the constant address
+  // space so that its wave-uniform entries come in by scalar loads
+  typedef const __attribute__((address_space(4))) int ConstInt;
+  ConstInt* table = (ConstInt*)(A.block_table) + static_cast<size_t>(b) * A.max_blocks;
+  const int col = L & 15, g4 = L >> 4;
+  const int sm_head = L / LPH, sm_t0 = TPL * (L % LPH), sm_c0 = CPL * (L % LPH);
+  const bool sm_on = sm_head < GRP;
 
   load_rotated_q<GRP>(A, b, h, S.qs);
-  // zero this wave's B tiles (columns >= NCOL stay zero for good)
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     W.bk[k][L] = u32x4{0, 0, 0, 0};
     W.bv[k][L] = u32x4{0, 0, 0, 0};
   }
   __syncthreads();
-  const int col = L & 15, g4 = L >> 4;
   if (wave == 0) {
     // q' hi/lo tiles for fp16 window chunks: step kk, lane (col, g4) holds
-    // channels 32*g4 + 8*kk + 0..7.
+    // channels 32 g4 + 8 kk + 0..7 in natural order.
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       u32x4 v = {0, 0, 0, 0};
@@ -355,21 +497,22 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs A) {
       S.bq[kk][L] = v;
     }
   }
-  // Per-lane constants of the alpha units: unit c = L + 64 r -> head c >> 4,
-  // channel group (c >> 2) & 3, step c & 3; K slot i of the step is channel
-  // c0 + (i >> 1) + 8 (i & 1), c0 = 32 g + 16 (kk >> 1) + 4 (kk & 1).
+  // Alpha unit c: head c % GRP, channels c0 .. c0+7 with
+  // c0 = 32 ((c / GRP) & 3) + 8 (c / (4 GRP)); slot i holds channel c0 + s(i).
   float qa[NR][8];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int c = L + 64 * r;
-    const int hh = (c >> 4) % GRP, g = (c >> 2) & 3, kk = c & 3;
-    const int c0 = 32 * g + 16 * (kk >> 1) + 4 * (kk & 1);
+    const int hh = c % GRP, c0 = 32 * ((c / GRP) & 3) + 8 * ((c / (4 * GRP)) & 3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qa[r][i] = 4.0f * S.qs[hh * kD + c0 + (i >> 1) + 8 * (i & 1)];
+    for (int i = 0; i < 8; ++i) qa[r][i] = S.qs[hh * kD + c0 + slot_pos(i)];
   }
+  // the softmax lane's share of q'.z
+  float zq[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) zq[j] = sm_on ? S.qs[sm_head * kD + sm_c0 + j] : 0.0f;
   __syncthreads();
 
-  // running state
   float m_run = -INFINITY, l_part = 0.0f;
   float zacc[NR];
 #pragma unroll
@@ -377,104 +520,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs A) {
   f32x4 o[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int sm_head = L / LPH, sm_t0 = TPL * (L % LPH);
-  const bool sm_on = sm_head < GRP;
 
-  for (int u = u0 + wave; u < u1; u += 4) {
-    const bool quant = u < nb;
-    int t_valid = 32;
-    float nt[TPL];
-    const uint8_t* rec = nullptr;
-    int slot0 = 0;
-    if (quant) {
-      int p = A.block_table[static_cast<size_t>(b) * A.max_blocks + u];
-      if (p < 0 || p >= A.nphys) {
-        if (L == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
-        p = 0;
-      }
-      rec = A.pool + (static_cast<size_t>(p) * A.hkv + h) * kRec;
-      const uint16_t* nrm = A.pool_norm + static_cast<size_t>(p) * 32;
-#pragma unroll
-      for (int j = 0; j < TPL; ++j) nt[j] = f16_to_f32(nrm[(sm_t0 + j) & 31]);
-      // alpha units: q' * delta split into hi/lo B tiles, kappa partials
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int c = L + 64 * r;
-        if (c < NCOMBO) {
-          const int hh = c >> 4, g = (c >> 2) & 3, kk = c & 3;
-          const int c0 = 32 * g + 16 * (kk >> 1) + 4 * (kk & 1);
-          const u32x2 dl = *reinterpret_cast<const u32x2*>(rec + kRecKDelta + 2 * c0);
-          const u32x2 dh = *reinterpret_cast<const u32x2*>(rec + kRecKDelta + 2 * c0 + 16);
-          const u32x2 zl = *reinterpret_cast<const u32x2*>(rec + kRecKZero + 2 * c0);
-          const u32x2 zh = *reinterpret_cast<const u32x2*>(rec + kRecKZero + 2 * c0 + 16);
-          // slot i: (i>>1) indexes the 4 consecutive channels, (i&1) picks +8
-          const float dv[8] = {h_lo(dl[0]), h_lo(dh[0]), h_hi(dl[0]), h_hi(dh[0]),
-                               h_lo(dl[1]), h_lo(dh[1]), h_hi(dl[1]), h_hi(dh[1])};
-          const float zv[8] = {h_lo(zl[0]), h_lo(zh[0]), h_hi(zl[0]), h_hi(zh[0]),
-                               h_lo(zl[1]), h_lo(zh[1]), h_hi(zl[1]), h_hi(zh[1])};
-          float w8[8];
-          float kq = 0.0f, ka = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            w8[i] = qa[r][i] * dv[i];
-            ka += w8[i];
-            kq += qa[r][i] * zv[i];
-          }
-          u32x4 hi, lo;
-          split8(w8, hi, lo);
-          W.bk[kk][hh + 16 * g] = hi;
-          W.bk[kk][hh + GRP + 16 * g] = lo;
-          float kap = 0.25f * kq - ka;
-#pragma unroll
-          for (int m = 1; m < 16; m <<= 1) kap += __shfl_xor(kap, m, 64);
-          if ((c & 15) == 0) W.kap[hh] = kap;
-        }
-      }
-    } else {
-      const int tb = Q + kG * (u - nb);
-      t_valid = n - tb < 32 ? n - tb : 32;
-      slot0 = tb % kR;
-#pragma unroll
-      for (int j = 0; j < TPL; ++j)
-        nt[j] = f16_to_f32(A.res_norm[static_cast<size_t>(b) * kR + slot0 + ((sm_t0 + j) & 31)]);
-    }
-    wave_lds_fence();
-
-    // ---- q.K^T on the matrix cores
-    f32x4 cs[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int t = 16 * tau + col;
-      if (quant) {
-        const u32x2 kw = *reinterpret_cast<const u32x2*>(rec + kRecKCodes + 32 * t + 8 * g4);
-        acc = mfma_f16(code_tile<0>(kw[0]), W.bk[0][L], acc);
-        acc = mfma_f16(code_tile<1>(kw[0]), W.bk[1][L], acc);
-        acc = mfma_f16(code_tile<0>(kw[1]), W.bk[2][L], acc);
-        acc = mfma_f16(code_tile<1>(kw[1]), W.bk[3][L], acc);
-      } else {
-        const u32x4* kr = reinterpret_cast<const u32x4*>(
-            A.res_k + (bh * kR + slot0 + t) * kD + 32 * g4);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma_f16(kr[kk], S.bq[kk][L], acc);
-      }
-      cs[tau] = acc;
-    }
-    // combine the hi and lo columns; column h < GRP holds head h
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      f32x4 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = cs[tau][j] + __shfl_xor(cs[tau][j], GRP, 64);
-      if (col < GRP) *reinterpret_cast<f32x4*>(&W.sc[col][16 * tau + 4 * g4]) = v;
-    }
-    wave_lds_fence();
-
-    // ---- online softmax (log2 domain), TPL tokens per lane
+  // Online softmax of one block's raw scores (W.sc) in the log2 domain; also
+  // rescales the accumulators when a head's running maximum grows.
+  auto softmax_block = [&](const float* nt, float kp, int t_valid) {
     float sv[TPL];
     float bm = -INFINITY;
     if (sm_on) {
-      const float kp = quant ? W.kap[sm_head] : 0.0f;
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         const int t = sm_t0 + j;
@@ -482,16 +534,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs A) {
         bm = fmaxf(bm, sv[j]);
       }
     }
-#pragma unroll
-    for (int m = 1; m < LPH; m <<= 1) bm = fmaxf(bm, __shfl_xor(bm, m, 64));
+    bm = group_max<LPH>(bm);
     const float m_new = fmaxf(m_run, bm);
     const bool grow = sm_on && m_new > m_run;
-    const float f = grow ? exp2f(m_run - m_new) : 1.0f;  // m_run = -inf gives 0
+    const float f = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // -inf gives 0
     if (sm_on) {
       float ps = 0.0f;
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
-        const float pj = sv[j] == -INFINITY ? 0.0f : exp2f(sv[j] - m_new);
+        const float pj = sv[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[j] - m_new);
         W.pr[sm_head][sm_t0 + j] = pj;
         ps += pj;
       }
@@ -500,7 +551,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs A) {
     }
     m_run = m_new;
     const bool any_grow = __any(grow);
-    wave_lds_fence();
+    lds_order();
     if (any_grow) {
       const float fo = col < NCOL ? W.fac[col % GRP] : 1.0f;
 #pragma unroll
@@ -511,8 +562,80 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs A) {
         if (c < NCOMBO) zacc[r] *= W.fac[(c >> 2) % GRP];
       }
     }
+  };
 
-    // ---- P.V operands: W units c -> group c / (4 GRP), head (c >> 2) % GRP,
+  // combine the hi and lo columns of the q.K^T tiles into W.sc
+  auto store_scores = [&](const f32x4* cs) {
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      f32x4 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = cs[tau][j] + dpp<dpp_row_shl(GRP)>(cs[tau][j]);
+      if (col < GRP) *reinterpret_cast<f32x4*>(&W.sc[col][16 * tau + 4 * g4]) = v;
+    }
+    lds_order();
+  };
+
+  // ---------------- quantized blocks, software-pipelined one block ahead
+  const int nb_end = u1 < nb ? u1 : nb;
+  int u = u0 + wave;
+  // physical block ids are read two blocks ahead and checked when used
+  auto checked = [&](int p) {
+    if (p < 0 || p >= A.nphys) {
+      if (L == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
+      p = 0;
+    }
+    return p;
+  };
+  auto process_int2 = [&](const UnitRegs<NR, CPL>& cur) {
+    // alpha units: q' * delta as hi/lo B tiles
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int c = L + 64 * r;
+      if (c < NCOMBO) {
+        const int hh = c % GRP, g = (c / GRP) & 3, kk = (c / (4 * GRP)) & 3;
+        _Float16 d8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int j = slot_pos(i);
+          d8[i] = hbits(cur.dz[r][j >> 1], j & 1);
+        }
+        u32x4 hi, lo;
+        split8_mul(qa[r], d8, hi, lo);
+        W.bk[kk][bk_row(hh + 16 * g)] = hi;
+        W.bk[kk][bk_row(hh + GRP + 16 * g)] = lo;
+      }
+    }
+    // q'.z of the softmax lane's head (one row of lanes)
+    float kz = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) kz += zq[j] * static_cast<float>(hbits(cur.zz[j >> 3][(j & 7) >> 1], j & 1));
+    kz = group_sum<LPH>(kz);
+    lds_order();
+
+    // q.K^T on the matrix cores
+    f32x4 cs[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const uint32_t e0 = even_fields(cur.kc[tau][0]), o0 = odd_fields(cur.kc[tau][0]);
+      const uint32_t e1 = even_fields(cur.kc[tau][1]), o1 = odd_fields(cur.kc[tau][1]);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int row = bk_row(L);
+      acc = mfma_f16(code_tile<0>(e0, o0), W.bk[0][row], acc);
+      acc = mfma_f16(code_tile<1>(e0, o0), W.bk[1][row], acc);
+      acc = mfma_f16(code_tile<0>(e1, o1), W.bk[2][row], acc);
+      acc = mfma_f16(code_tile<1>(e1, o1), W.bk[3][row], acc);
+      cs[tau] = acc;
+    }
+    store_scores(cs);
+
+    float nt[TPL];
+#pragma unroll
+    for (int j = 0; j < TPL; ++j)
+      nt[j] = (j & 1) ? h_hi(cur.nrm[j >> 1]) : h_lo(cur.nrm[j >> 1]);
+    softmax_block(nt, kz, 32);
+
+    // P.V operands: W unit c -> group c / (4 GRP), head (c >> 2) % GRP,
     // token octet c & 3
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -522,97 +645,153 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs A) {
         const f32x4 p0 = *reinterpret_cast<const f32x4*>(&W.pr[hh][8 * g8]);
         const f32x4 p1 = *reinterpret_cast<const f32x4*>(&W.pr[hh][8 * g8 + 4]);
         const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-        float w8[8];
-        if (quant) {
-          const u32x4* vp = reinterpret_cast<const u32x4*>(rec + kRecVParam + 4 * (32 * gv + 8 * g8));
-          const u32x4 v0 = vp[0], v1 = vp[1];
-          const uint32_t pz[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          float zsum = 0.0f;
+        _Float16 d8[8];
+        float zsum = 0.0f;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const float dvk = h_lo(pz[k]), zvk = h_hi(pz[k]);
-            w8[k] = 4.0f * pv[k] * dvk;
-            zsum += pv[k] * (zvk - 4.0f * dvk);
-          }
-          zacc[r] += zsum;
-        } else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) w8[k] = pv[k];
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t pz = cur.vp[r][k >> 2][k & 3];
+          d8[k] = hbits(pz, 0);
+          zsum += pv[k] * static_cast<float>(hbits(pz, 1));
         }
+        zacc[r] += zsum;
+        u32x4 hi, lo;
+        split8_mul(pv, d8, hi, lo);
+        W.bv[gv][bv_row(hh + 16 * g8)] = hi;
+        W.bv[gv][bv_row(hh + GRP + 16 * g8)] = lo;
+      }
+    }
+    lds_order();
+
+    // P.V on the matrix cores: tile ct = channels 16 ct .. 16 ct + 15
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t e = even_fields(cur.vc[d]), od = odd_fields(cur.vc[d]);
+      const u32x4 bvd = W.bv[d][bv_row(L)];
+      o[2 * d] = mfma_f16(code_tile<0>(e, od), bvd, o[2 * d]);
+      o[2 * d + 1] = mfma_f16(code_tile<1>(e, od), bvd, o[2 * d + 1]);
+    }
+  };
+  // The wave's quantized blocks are u0 + wave + 4k, k < cnt.  Two register
+  // sets take turns: the next block loads into one while the other is
+  // processed.  The prefetch is issued unconditionally (after the last block
+  // it re-reads the current, cached one) so that the compiler can count the
+  // outstanding loads exactly and never waits for the prefetch early.
+  const int first = u0 + wave;
+  const int cnt = nb_end > first ? (nb_end - first + 3) / 4 : 0;
+  auto unit_rec = [&](int p) {
+    return A.pool + (static_cast<size_t>(p) * A.hkv + h) * kRec;
+  };
+  auto unit_nrm = [&](int p) { return A.pool_norm + static_cast<size_t>(p) * 32; };
+  auto block_at = [&](int k) { return table[first + 4 * (k < cnt ? k : cnt - 1)]; };
+  if (cnt > 0) {
+    UnitRegs<NR, CPL> ra, rb;
+    int p_cur = checked(block_at(0));
+    int p_nxt = block_at(1);
+    load_unit<GRP, NR, TPL, CPL>(ra, unit_rec(p_cur), unit_nrm(p_cur), L, sm_t0, sm_c0);
+    for (int k = 0; k < cnt; k += 2) {
+      const int p2 = block_at(k + 2);
+      p_nxt = checked(p_nxt);
+      load_unit<GRP, NR, TPL, CPL>(rb, unit_rec(p_nxt), unit_nrm(p_nxt), L, sm_t0, sm_c0);
+      process_int2(ra);
+      if (k + 1 >= cnt) break;
+      const int p3 = block_at(k + 3);
+      const int pa = checked(p2);
+      load_unit<GRP, NR, TPL, CPL>(ra, unit_rec(pa), unit_nrm(pa), L, sm_t0, sm_c0);
+      process_int2(rb);
+      p_nxt = p3;
+    }
+  }
+  u = first + 4 * cnt;
+
+  // ---------------- fp16 residual-window chunks
+  for (; u < u1; u += 4) {
+    const int tb = Q + kG * (u - nb);
+    const int t_valid = n - tb < 32 ? n - tb : 32;
+    const int slot0 = tb % kR;
+    f32x4 cs[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const u32x4* kr = reinterpret_cast<const u32x4*>(
+          A.res_k + (bh * kR + slot0 + 16 * tau + col) * kD + 32 * g4);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mfma_f16(kr[kk], S.bq[kk][L], acc);
+      cs[tau] = acc;
+    }
+    store_scores(cs);
+    float nt[TPL];
+#pragma unroll
+    for (int j = 0; j < TPL; ++j)
+      nt[j] = f16_to_f32(A.res_norm[static_cast<size_t>(b) * kR + slot0 + ((sm_t0 + j) & 31)]);
+    softmax_block(nt, 0.0f, t_valid);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int c = L + 64 * r;
+      if (c < NCOMBO) {
+        const int gv = c / (4 * GRP), hh = (c >> 2) % GRP, g8 = c & 3;
+        float w8[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w8[k] = W.pr[hh][8 * g8 + k];
         u32x4 hi, lo;
         split8(w8, hi, lo);
-        W.bv[gv][hh + 16 * g8] = hi;
-        W.bv[gv][hh + GRP + 16 * g8] = lo;
+        W.bv[gv][bv_row(hh + 16 * g8)] = hi;
+        W.bv[gv][bv_row(hh + GRP + 16 * g8)] = lo;
       }
     }
-    wave_lds_fence();
-
-    // ---- P.V on the matrix cores: tile ct = channels 16 ct .. 16 ct + 15
-    if (quant) {
-      const u32x4 vw = *reinterpret_cast<const u32x4*>(rec + kRecVCodes + 16 * L);
-      const u32x4 b0 = W.bv[0][L], b1 = W.bv[1][L], b2 = W.bv[2][L], b3 = W.bv[3][L];
-      o[0] = mfma_f16(code_tile<0>(vw[0]), b0, o[0]);
-      o[1] = mfma_f16(code_tile<1>(vw[0]), b0, o[1]);
-      o[2] = mfma_f16(code_tile<0>(vw[1]), b1, o[2]);
-      o[3] = mfma_f16(code_tile<1>(vw[1]), b1, o[3]);
-      o[4] = mfma_f16(code_tile<0>(vw[2]), b2, o[4]);
-      o[5] = mfma_f16(code_tile<1>(vw[2]), b2, o[5]);
-      o[6] = mfma_f16(code_tile<0>(vw[3]), b3, o[6]);
-      o[7] = mfma_f16(code_tile<1>(vw[3]), b3, o[7]);
-    } else {
-      const u32x4 b0 = W.bv[0][L];
+    lds_order();
+    const u32x4 b0 = W.bv[0][bv_row(L)];
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const u32x4 va = *reinterpret_cast<const u32x4*>(
-            A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
-        o[ct] = mfma_f16(va, b0, o[ct]);
-      }
+    for (int ct = 0; ct < 8; ++ct) {
+      const u32x4 va = *reinterpret_cast<const u32x4*>(
+          A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
+      o[ct] = mfma_f16(va, b0, o[ct]);
     }
   }
 
-  // ---- wave partial: l, Z, o for each head
-  float lsum = l_part;
-#pragma unroll
-  for (int m = 1; m < LPH; m <<= 1) lsum += __shfl_xor(lsum, m, 64);
-  if (sm_on && (L % LPH) == 0) {
-    S.wm[wave][sm_head] = m_run;
-    S.wl[wave][sm_head] = lsum;
-  }
+  // ---------------- this wave's partial: l, Z, o for each head
+  const float lsum = group_sum<LPH>(l_part);
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int c = L + 64 * r;
-    float z = zacc[r];
-    z += __shfl_xor(z, 1, 64);
-    z += __shfl_xor(z, 2, 64);
+    const float z = group_sum<4>(zacc[r]);
     if (c < NCOMBO && (c & 3) == 0) W.zs[c / (4 * GRP)][(c >> 2) % GRP] = z;
   }
-  wave_lds_fence();
+  lds_order();
+  float ov[8][4];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
+  for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float v = o[ct][j] + __shfl_xor(o[ct][j], GRP, 64);
-      if (col < GRP) S.wo[wave][col][16 * ct + 4 * g4 + j] = v + W.zs[ct >> 1][col];
-    }
+    for (int j = 0; j < 4; ++j)
+      ov[ct][j] = o[ct][j] + dpp<dpp_row_shl(GRP)>(o[ct][j]) + (col < GRP ? W.zs[ct >> 1][col] : 0.0f);
+  __syncthreads();  // every wave is done with its LDS tiles; reuse them for the merge
+  if (sm_on && (L % LPH) == 0) {
+    S.m.wm[wave][sm_head] = m_run;
+    S.m.wl[wave][sm_head] = lsum;
+  }
+  if (col < GRP) {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      *reinterpret_cast<f32x4*>(&S.m.wo[wave][col][16 * ct + 4 * g4]) =
+          f32x4{ov[ct][0], ov[ct][1], ov[ct][2], ov[ct][3]};
   }
   __syncthreads();
 
-  // ---- merge the 4 waves into this split's partial
+  // ---------------- merge the 4 waves into this split's partial
   const size_t pbase = (static_cast<size_t>(b) * A.hq + h * GRP) * A.splits;
   for (int idx = tid; idx < GRP * kD; idx += 256) {
     const int hh = idx >> 7, c = idx & 127;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, S.wm[w][hh]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, S.m.wm[w][hh]);
     float Lw = 0.0f, Ow = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float mw = S.wm[w][hh];
+        const float mw = S.m.wm[w][hh];
         if (mw == -INFINITY) continue;
         const float sc = exp2f(mw - M);
-        Lw += sc * S.wl[w][hh];
-        Ow += sc * S.wo[w][hh][c];
+        Lw += sc * S.m.wl[w][hh];
+        Ow += sc * S.m.wo[w][hh][c];
       }
     }
     const size_t part = pbase + static_cast<size_t>(hh) * A.splits + s;
@@ -683,9 +862,11 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(const float2* __restric
 }
 
 int auto_splits(const oscar_cache_geom* g, int max_ctx) {
+  // about three 4-wave workgroups per CU on 256 CUs, and at least 8 blocks
+  // per workgroup
   const int units = (max_ctx + kG - 1) / kG + 1;
   const int pairs = g->batch * g->num_kv_heads;
-  int s = (2048 + pairs - 1) / pairs;
+  int s = (768 + pairs - 1) / pairs;
   const int cap = units / 8 > 1 ? units / 8 : 1;
   if (s > cap) s = cap;
   if (s > 1024) s = 1024;

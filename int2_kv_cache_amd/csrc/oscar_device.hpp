@@ -170,7 +170,8 @@ __device__ __forceinline__ int kcode_bitpos(int t, int c) {   // bit index in K 
 }
 __device__ __forceinline__ int vcode_bitpos(int t, int c) {   // bit index in V codes
   const int slice = 16 * (t >> 3) + (c & 15), word = c >> 5, e = (c >> 4) & 1, k = t & 7;
-  return 32 * (4 * slice + word) + 2 * (4 * e + (k >> 1)) + 16 * (k & 1);
+  const int sk = (k & 4) | ((k & 1) << 1) | ((k >> 1) & 1);
+  return 32 * (4 * slice + word) + 2 * (8 * e + sk);
 }
 
 }  // namespace oscar

@@ -251,11 +251,13 @@ void orc_quant_group32(const uint16_t *x16, size_t stride, float *delta,
  *   16*(t >> 3) + (c & 15) holds tokens 8*(t>>3) .. +7 of channels
  *   c & 15, 16 + (c & 15), ..., 112 + (c & 15).  Inside a slice, 32-bit word
  *   d = c >> 5 holds the two 16-channel tiles 2d, 2d+1; the code of token
- *   slot k = t & 7 of tile e = (c >> 4) & 1 sits at bit
- *   2*(4e + (k >> 1)) + 16*(k & 1) of that little-endian word.
+ *   slot k = t & 7 of tile e = (c >> 4) & 1 sits at position
+ *   m = 8e + s(k) of that little-endian word (bits 2m, 2m+1), where s(k)
+ *   swaps the two low bits of k: s = 0,2,1,3,4,6,5,7.
  *   (The layout is this code's own choice; the pages do not define one.  It
- *   puts the 8 codes of 8 consecutive tokens of one channel next to each
- *   other, which is the order a token-contracting matrix tile consumes.)
+ *   puts the 8 codes of 8 consecutive tokens of one channel in one 16-bit
+ *   half word, in the order in which splitting the word into even and odd
+ *   2-bit fields yields consecutive token pairs.)
  * K step/zero: fp16 [128] each at 2048 / 2304.
  * V step/zero: fp16 pairs (step, zero) at 2560 + 4*(32*g + t), g = c >> 5
  *   (group-major, so the pairs of 8 consecutive tokens of one group are 32
@@ -268,18 +270,22 @@ int orc_kcode_shift(int t, int c)
     return 2 * (c & 3);
 }
 
+static int vcode_bit(int t, int c)
+{
+    int k = t & 7, e = (c >> 4) & 1;
+    int sk = (k & 4) | ((k & 1) << 1) | ((k >> 1) & 1);
+    return 2 * (8 * e + sk);
+}
+
 size_t orc_vcode_byte(int t, int c)
 {
-    int g = t >> 3, k = t & 7, ct = c >> 4, c16 = c & 15;
-    int slice = 16 * g + c16, d = ct >> 1, e = ct & 1;
-    int bit = 2 * (4 * e + (k >> 1)) + 16 * (k & 1);
-    return (size_t)(ORC_REC_VCODES + 16 * slice + 4 * d + (bit >> 3));
+    int g = t >> 3, c16 = c & 15, d = c >> 5;
+    int slice = 16 * g + c16;
+    return (size_t)(ORC_REC_VCODES + 16 * slice + 4 * d + (vcode_bit(t, c) >> 3));
 }
 int orc_vcode_shift(int t, int c)
 {
-    int k = t & 7, e = (c >> 4) & 1;
-    int bit = 2 * (4 * e + (k >> 1)) + 16 * (k & 1);
-    return bit & 7;
+    return vcode_bit(t, c) & 7;
 }
 
 int orc_kcode_get(const uint8_t *rec, int t, int c)
