@@ -30,10 +30,17 @@ FLAGS = [
 # in-source pragma, so the flag is set per file.
 EXACT = {"oscar_rotate.hip", "oscar_cache.hip", "oscar_abi.hip"}
 
+# The attention kernels never produce or test for NaN (scores are finite or
+# -inf): without NaN semantics a max with a cross-lane operand needs no
+# canonicalising instruction and fuses into one DPP instruction.
+NO_NAN = {"oscar_attn.hip"}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    extra = ["-ffp-contract=off"] if os.path.basename(src) in EXACT else []
+    name = os.path.basename(src)
+    extra = (["-ffp-contract=off"] if name in EXACT else []) + \
+        (["-fno-honor-nans"] if name in NO_NAN else [])
     cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -362,7 +362,7 @@ template <int GRP>
 struct MfmaWaveLds {
   u32x4 bk[4][64];          // Key-side B tiles, one per 8-channel step of each group
   u32x4 bv[4][64];          // Value-side B tiles, one per Value group
-  float sc[GRP][kRowPad];   // combined raw scores of the block
+  float sc[16][kRowPad];    // combined raw scores (rows >= GRP take unused columns)
   float pr[GRP][kRowPad];   // probabilities of the block
   float fac[GRP];           // rescale factor per head
   float zs[4][GRP];
@@ -377,7 +377,6 @@ struct MfmaMerge {
 template <int GRP>
 struct MfmaLds {
   float qs[GRP * kD];  // rotated query heads
-  u32x4 bq[4][64];     // q' hi/lo B tiles for fp16 window chunks
   union {
     MfmaWaveLds<GRP> w[4];
     MfmaMerge<GRP> m;
@@ -401,40 +400,78 @@ struct UnitRegs {
   u32x2 nrm;     // token norms of the softmax lane
 };
 
+// Byte offsets of a lane's loads inside a record (and its norm row), fixed
+// for the whole kernel: the record base is a wave-uniform (scalar) address.
+template <int NR>
+struct UnitOffs {
+  uint32_t kc0, kc1, vc, dz[NR], vp[NR], zz, nrm;
+};
+
+// Buffer resource over one record (or one norm row): loads then take the
+// scalar base and a 32-bit per-lane offset, with no per-load address math;
+// an offset past num_bytes reads zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, num_bytes, 0x00020000);
+}
+template <class T>
+__device__ __forceinline__ T ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(T) == 16)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  else if constexpr (sizeof(T) == 8)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  else if constexpr (sizeof(T) == 4)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  else
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
 template <int GRP, int NR, int TPL, int CPL>
-__device__ __forceinline__ void load_unit(UnitRegs<NR, CPL>& R, const uint8_t* rec,
-                                          const uint16_t* nrm, int L, int sm_t0, int sm_c0) {
+__device__ __forceinline__ void load_unit(UnitRegs<NR, CPL>& R, const UnitOffs<NR>& O,
+                                          __amdgpu_buffer_rsrc_t rec, __amdgpu_buffer_rsrc_t nrm,
+                                          int L) {
   constexpr int NCOMBO = 16 * GRP;
-  const int col = L & 15, g4 = L >> 4;
-  R.kc[0] = *reinterpret_cast<const u32x2*>(rec + kRecKCodes + 32 * col + 8 * g4);
-  R.kc[1] = *reinterpret_cast<const u32x2*>(rec + kRecKCodes + 32 * (16 + col) + 8 * g4);
-  R.vc = *reinterpret_cast<const u32x4*>(rec + kRecVCodes + 16 * L);
+  R.kc[0] = ld<u32x2>(rec, O.kc0);
+  R.kc[1] = ld<u32x2>(rec, O.kc1);
+  R.vc = ld<u32x4>(rec, O.vc);
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const int c = L + 64 * r;
-    if (c < NCOMBO) {
-      const int c0 = 32 * ((c / GRP) & 3) + 8 * (c / (4 * GRP));
-      R.dz[r] = *reinterpret_cast<const u32x4*>(rec + kRecKDelta + 2 * c0);
-      const int gv = c / (4 * GRP), g8 = c & 3;
-      const u32x4* vp = reinterpret_cast<const u32x4*>(rec + kRecVParam + 4 * (32 * gv + 8 * g8));
-      R.vp[r][0] = vp[0];
-      R.vp[r][1] = vp[1];
+    if (L + 64 * r < NCOMBO) {
+      R.dz[r] = ld<u32x4>(rec, O.dz[r]);
+      R.vp[r][0] = ld<u32x4>(rec, O.vp[r]);
+      R.vp[r][1] = ld<u32x4>(rec, O.vp[r] + 16);
     }
   }
   if (CPL >= 8) {
 #pragma unroll
-    for (int j = 0; j < (CPL + 7) / 8; ++j)
-      R.zz[j] = *reinterpret_cast<const u32x4*>(rec + kRecKZero + 2 * (sm_c0 + 8 * j));
+    for (int j = 0; j < (CPL + 7) / 8; ++j) R.zz[j] = ld<u32x4>(rec, O.zz + 16 * j);
   } else {
-    const u32x2 z2 = *reinterpret_cast<const u32x2*>(rec + kRecKZero + 2 * sm_c0);
+    const u32x2 z2 = ld<u32x2>(rec, O.zz);
     R.zz[0] = u32x4{z2[0], z2[1], 0u, 0u};
   }
   if (TPL == 4)
-    R.nrm = *reinterpret_cast<const u32x2*>(nrm + sm_t0);
+    R.nrm = ld<u32x2>(nrm, O.nrm);
   else if (TPL == 2)
-    R.nrm[0] = *reinterpret_cast<const uint32_t*>(nrm + sm_t0);
+    R.nrm[0] = ld<uint32_t>(nrm, O.nrm);
   else
-    R.nrm[0] = nrm[sm_t0 & 31];
+    R.nrm[0] = ld<uint16_t>(nrm, O.nrm);
+}
+
+constexpr int kRingWeight = 3;
+
+// Wave priority from its progress through a list of cnt blocks: a wave that
+// is behind the others of its SIMD gets the issue slots first, so that the
+// waves of a SIMD (which all hold about the same number of blocks) finish
+// together instead of the oldest wave running ahead.
+__device__ __forceinline__ void progress_prio(int k, int cnt) {
+  const int k4 = 4 * k;
+  if (k4 < cnt)
+    __builtin_amdgcn_s_setprio(3);
+  else if (k4 < 2 * cnt)
+    __builtin_amdgcn_s_setprio(2);
+  else if (k4 < 3 * cnt)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
 }
 
 template <int GRP>
@@ -451,52 +488,126 @@ void attn_mfma_kernel(AttnArgs A) {
   __shared__ MfmaLds<GRP> S;
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  // wave index as a wave-uniform (scalar) value: unit indices and block-table
-  // reads then stay in scalar registers
+  // wave index as a wave-uniform (scalar) value: unit indices and record
+  // addresses then stay in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), L = tid & 63;
   MfmaWaveLds<GRP>& W = S.w[wave];
+  // set-up (loads, query rotation, the window chunk) runs at the highest
+  // priority: the main loop lowers it as a wave progresses
+  __builtin_amdgcn_s_setprio(3);
   int n = A.seq_state[2 * b], Q = A.seq_state[2 * b + 1];
   if (!(Q >= 0 && (Q & 31) == 0 && n >= Q && n - Q <= kR && Q / kG <= A.max_blocks)) {
     if (tid == 0 && s == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
     n = Q = 0;
   }
-  const int nb = Q / kG, nr = (n - Q + kG - 1) / kG, U = nb + nr;
-  const int u0 = static_cast<int>((static_cast<long long>(s) * U) / A.splits);
-  const int u1 = static_cast<int>((static_cast<long long>(s + 1) * U) / A.splits);
+  // Splits partition the units by weight: an INT2 block weighs 1, a window
+  // chunk (16 KB of fp16 data against a 3 KB record) kRingWeight.
+  const int nb = Q / kG, nr = (n - Q + kG - 1) / kG;
+  const long long wt = nb + static_cast<long long>(kRingWeight) * nr;
+  auto unit_at = [&](long long w) {
+    return w <= nb ? static_cast<int>(w) : nb + static_cast<int>((w - nb + kRingWeight - 1) / kRingWeight);
+  };
+  const int u0 = unit_at(s * wt / A.splits), u1 = unit_at((s + 1) * wt / A.splits);
   const size_t bh = static_cast<size_t>(b) * A.hkv + h;
-  // the block table is read-only here: read it through the constant address
-  // space so that its wave-uniform entries come in by scalar loads
-  typedef const __attribute__((address_space(4))) int ConstInt;
-  ConstInt* table = (ConstInt*)(A.block_table) + static_cast<size_t>(b) * A.max_blocks;
   const int col = L & 15, g4 = L >> 4;
   const int sm_head = L / LPH, sm_t0 = TPL * (L % LPH), sm_c0 = CPL * (L % LPH);
   const bool sm_on = sm_head < GRP;
 
-  load_rotated_q<GRP>(A, b, h, S.qs);
+  // The wave's units are u = first + 4k.  The first cnt are INT2 blocks; at
+  // most one more (k = cnt) is a chunk of the fp16 window, since the window
+  // spans at most 4 consecutive units.
+  const int first = u0 + wave;
+  const int n_units = u1 > first ? (u1 - first + 3) / 4 : 0;
+  const int cnt = nb > first ? min(n_units, (nb - first + 3) / 4) : 0;
+  const bool has_ring = n_units > cnt;
+
+  // Physical block ids of the wave's INT2 blocks, 64 at a time: lane j holds
+  // block k0 + j; a block is then taken out with readlane (no scalar memory
+  // traffic inside the loop).  Invalid ids are flagged and replaced by 0.
+  const int* tab = A.block_table + static_cast<size_t>(b) * A.max_blocks + first;
+  auto load_ids = [&](int k0) {
+    int id = 0;
+    if (L < cnt - k0) id = tab[4 * (k0 + L)];
+    const bool bad = static_cast<unsigned>(id) >= static_cast<unsigned>(A.nphys);
+    if (__any(bad) && L == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
+    return bad ? 0 : id;
+  };
+  // The query heads of this wave (wave, wave + 4) load first: their latency
+  // overlaps the block-table read and the first record's.
+  constexpr int QPW = (GRP + 3) / 4;
+  float qx[QPW], qy[QPW];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    W.bk[k][L] = u32x4{0, 0, 0, 0};
-    W.bv[k][L] = u32x4{0, 0, 0, 0};
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // q' hi/lo tiles for fp16 window chunks: step kk, lane (col, g4) holds
-    // channels 32 g4 + 8 kk + 0..7 in natural order.
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4 v = {0, 0, 0, 0};
-      if (col < NCOL) {
-        float x[8];
-        const float* q = S.qs + (col % GRP) * kD + 32 * g4 + 8 * kk;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = q[i];
-        u32x4 hi, lo;
-        split8(x, hi, lo);
-        v = col < GRP ? hi : lo;
+  for (int j = 0; j < QPW; ++j) {
+    const int i = wave + 4 * j;
+    qx[j] = qy[j] = 0.0f;
+    if (i < GRP) {
+      const size_t base = (static_cast<size_t>(b) * A.hq + h * GRP + i) * kD;
+      if (A.q_mode == 2) {
+        qx[j] = static_cast<const float*>(A.q)[base + L];
+        qy[j] = static_cast<const float*>(A.q)[base + L + 64];
+      } else {
+        const uint16_t* q16 = static_cast<const uint16_t*>(A.q);
+        qx[j] = in_to_f32(q16[base + L], A.q_mode);
+        qy[j] = in_to_f32(q16[base + L + 64], A.q_mode);
       }
-      S.bq[kk][L] = v;
     }
   }
+  int idv = cnt > 0 ? load_ids(0) : 0;
+
+  UnitOffs<NR> off;
+  off.kc0 = kRecKCodes + 32 * col + 8 * g4;
+  off.kc1 = kRecKCodes + 32 * (16 + col) + 8 * g4;
+  off.vc = kRecVCodes + 16 * L;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int c = L + 64 * r;
+    off.dz[r] = kRecKDelta + 2 * (32 * ((c / GRP) & 3) + 8 * ((c / (4 * GRP)) & 3));
+    off.vp[r] = kRecVParam + 4 * (32 * ((c / (4 * GRP)) & 3) + 8 * (c & 3));
+  }
+  off.zz = kRecKZero + 2 * sm_c0;
+  off.nrm = 2 * (sm_t0 & 31);
+  auto unit_rec = [&](int p) {
+    return rsrc(A.pool + (static_cast<size_t>(p) * A.hkv + h) * kRec, kRec);
+  };
+  auto unit_nrm = [&](int p) { return rsrc(A.pool_norm + static_cast<size_t>(p) * 32, 64); };
+
+  // the window chunk and the first INT2 block load while the query is rotated
+  u32x4 rk[2][4], rv[8];
+  float rnt[TPL];
+  int ring_valid = 0, slot0 = 0;
+  if (has_ring) {
+    const int tb = Q + kG * (first + 4 * cnt - nb);
+    ring_valid = n - tb < 32 ? n - tb : 32;
+    slot0 = tb % kR;  // a multiple of 32: the chunk is 32 consecutive slots
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        rk[tau][kk] = *reinterpret_cast<const u32x4*>(
+            A.res_k + (bh * kR + slot0 + 16 * tau + col) * kD + 32 * g4 + 8 * kk);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      rv[ct] = *reinterpret_cast<const u32x4*>(A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
+#pragma unroll
+    for (int j = 0; j < TPL; ++j)
+      rnt[j] = f16_to_f32(A.res_norm[static_cast<size_t>(b) * kR + slot0 + ((sm_t0 + j) & 31)]);
+  }
+  UnitRegs<NR, CPL> ra, rb;
+  if (cnt > 0) {
+    const int p = __builtin_amdgcn_readlane(idv, 0);
+    load_unit<GRP, NR, TPL, CPL>(ra, off, unit_rec(p), unit_nrm(p), L);
+  }
+
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) {
+    const int i = wave + 4 * j;
+    if (i < GRP) {
+      if (A.q_mode != 2) fht128_wave(qx[j], qy[j]);
+      S.qs[i * kD + L] = qx[j];
+      S.qs[i * kD + L + 64] = qy[j];
+    }
+  }
+  __syncthreads();
   // Alpha unit c: head c % GRP, channels c0 .. c0+7 with
   // c0 = 32 ((c / GRP) & 3) + 8 (c / (4 GRP)); slot i holds channel c0 + s(i).
   float qa[NR][8];
@@ -511,7 +622,6 @@ void attn_mfma_kernel(AttnArgs A) {
   float zq[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) zq[j] = sm_on ? S.qs[sm_head * kD + sm_c0 + j] : 0.0f;
-  __syncthreads();
 
   float m_run = -INFINITY, l_part = 0.0f;
   float zacc[NR];
@@ -522,7 +632,8 @@ void attn_mfma_kernel(AttnArgs A) {
   for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Online softmax of one block's raw scores (W.sc) in the log2 domain; also
-  // rescales the accumulators when a head's running maximum grows.
+  // rescales the accumulators when a head's running maximum grows.  Every
+  // processed block has at least one valid token, so m_new is finite.
   auto softmax_block = [&](const float* nt, float kp, int t_valid) {
     float sv[TPL];
     float bm = -INFINITY;
@@ -542,17 +653,17 @@ void attn_mfma_kernel(AttnArgs A) {
       float ps = 0.0f;
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
-        const float pj = sv[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[j] - m_new);
+        const float pj = __builtin_amdgcn_exp2f(sv[j] - m_new);  // -inf gives 0
         W.pr[sm_head][sm_t0 + j] = pj;
         ps += pj;
       }
       l_part = l_part * f + ps;
-      if ((L % LPH) == 0) W.fac[sm_head] = f;
     }
     m_run = m_new;
-    const bool any_grow = __any(grow);
-    lds_order();
-    if (any_grow) {
+    if (__any(grow)) {
+      // rare after the first blocks: rescale the heads whose maximum grew
+      if (sm_on && (L % LPH) == 0) W.fac[sm_head] = f;
+      lds_order();
       const float fo = col < NCOL ? W.fac[col % GRP] : 1.0f;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) o[ct] *= fo;
@@ -562,31 +673,86 @@ void attn_mfma_kernel(AttnArgs A) {
         if (c < NCOMBO) zacc[r] *= W.fac[(c >> 2) % GRP];
       }
     }
+    lds_order();
   };
 
-  // combine the hi and lo columns of the q.K^T tiles into W.sc
+  // combine the hi and lo columns of the q.K^T tiles into W.sc (every lane
+  // stores; rows GRP..15 receive the unused columns)
   auto store_scores = [&](const f32x4* cs) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       f32x4 v;
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = cs[tau][j] + dpp<dpp_row_shl(GRP)>(cs[tau][j]);
-      if (col < GRP) *reinterpret_cast<f32x4*>(&W.sc[col][16 * tau + 4 * g4]) = v;
+      *reinterpret_cast<f32x4*>(&W.sc[col][16 * tau + 4 * g4]) = v;
     }
     lds_order();
   };
 
-  // ---------------- quantized blocks, software-pipelined one block ahead
-  const int nb_end = u1 < nb ? u1 : nb;
-  int u = u0 + wave;
-  // physical block ids are read two blocks ahead and checked when used
-  auto checked = [&](int p) {
-    if (p < 0 || p >= A.nphys) {
-      if (L == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
-      p = 0;
+  // P.V operands of one block from W.pr: W unit c -> group c / (4 GRP),
+  // head (c >> 2) % GRP, token octet c & 3
+  auto pv_tiles = [&](const UnitRegs<NR, CPL>* cur) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int c = L + 64 * r;
+      if (c < NCOMBO) {
+        const int gv = c / (4 * GRP), hh = (c >> 2) % GRP, g8 = c & 3;
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(&W.pr[hh][8 * g8]);
+        const f32x4 p1 = *reinterpret_cast<const f32x4*>(&W.pr[hh][8 * g8 + 4]);
+        const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        u32x4 hi, lo;
+        if (cur) {
+          _Float16 d8[8];
+          float zsum = 0.0f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t pz = cur->vp[r][k >> 2][k & 3];
+            d8[k] = hbits(pz, 0);
+            zsum += pv[k] * static_cast<float>(hbits(pz, 1));
+          }
+          zacc[r] += zsum;
+          split8_mul(pv, d8, hi, lo);
+        } else {
+          split8(pv, hi, lo);
+        }
+        W.bv[gv][bv_row(hh + 16 * g8)] = hi;
+        W.bv[gv][bv_row(hh + GRP + 16 * g8)] = lo;
+      }
     }
-    return p;
+    lds_order();
   };
+
+  // ---------------- the fp16 window chunk (its data is already loaded)
+  if (has_ring) {
+    // q' hi/lo B tiles, channels 32 g4 + 8 kk + 0..7 in natural order
+    u32x4 bq[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      float x[8];
+      const float* q = S.qs + (col % GRP) * kD + 32 * g4 + 8 * kk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = q[i];
+      u32x4 hi, lo;
+      split8(x, hi, lo);
+      bq[kk] = col < GRP ? hi : lo;  // columns >= 2 GRP are unused
+    }
+    f32x4 cs[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mfma_f16(rk[tau][kk], bq[kk], acc);
+      cs[tau] = acc;
+    }
+    store_scores(cs);
+    softmax_block(rnt, 0.0f, ring_valid);
+    pv_tiles(nullptr);
+    const u32x4 b0 = W.bv[0][bv_row(L)];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) o[ct] = mfma_f16(rv[ct], b0, o[ct]);
+  }
+
+  // ---------------- quantized blocks, software-pipelined one block ahead
   auto process_int2 = [&](const UnitRegs<NR, CPL>& cur) {
     // alpha units: q' * delta as hi/lo B tiles
 #pragma unroll
@@ -634,33 +800,7 @@ void attn_mfma_kernel(AttnArgs A) {
     for (int j = 0; j < TPL; ++j)
       nt[j] = (j & 1) ? h_hi(cur.nrm[j >> 1]) : h_lo(cur.nrm[j >> 1]);
     softmax_block(nt, kz, 32);
-
-    // P.V operands: W unit c -> group c / (4 GRP), head (c >> 2) % GRP,
-    // token octet c & 3
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int c = L + 64 * r;
-      if (c < NCOMBO) {
-        const int gv = c / (4 * GRP), hh = (c >> 2) % GRP, g8 = c & 3;
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(&W.pr[hh][8 * g8]);
-        const f32x4 p1 = *reinterpret_cast<const f32x4*>(&W.pr[hh][8 * g8 + 4]);
-        const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-        _Float16 d8[8];
-        float zsum = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const uint32_t pz = cur.vp[r][k >> 2][k & 3];
-          d8[k] = hbits(pz, 0);
-          zsum += pv[k] * static_cast<float>(hbits(pz, 1));
-        }
-        zacc[r] += zsum;
-        u32x4 hi, lo;
-        split8_mul(pv, d8, hi, lo);
-        W.bv[gv][bv_row(hh + 16 * g8)] = hi;
-        W.bv[gv][bv_row(hh + GRP + 16 * g8)] = lo;
-      }
-    }
-    lds_order();
+    pv_tiles(&cur);
 
     // P.V on the matrix cores: tile ct = channels 16 ct .. 16 ct + 15
 #pragma unroll
@@ -671,82 +811,26 @@ void attn_mfma_kernel(AttnArgs A) {
       o[2 * d + 1] = mfma_f16(code_tile<1>(e, od), bvd, o[2 * d + 1]);
     }
   };
-  // The wave's quantized blocks are u0 + wave + 4k, k < cnt.  Two register
-  // sets take turns: the next block loads into one while the other is
-  // processed.  The prefetch is issued unconditionally (after the last block
-  // it re-reads the current, cached one) so that the compiler can count the
-  // outstanding loads exactly and never waits for the prefetch early.
-  const int first = u0 + wave;
-  const int cnt = nb_end > first ? (nb_end - first + 3) / 4 : 0;
-  auto unit_rec = [&](int p) {
-    return A.pool + (static_cast<size_t>(p) * A.hkv + h) * kRec;
+  // Two register sets take turns: block k + 1 loads into one while block k
+  // in the other is processed.  The prefetch is issued unconditionally
+  // (after the last block it re-reads the last, cached one) so that the
+  // compiler can count the outstanding loads exactly and never waits for the
+  // prefetch early.
+  auto prefetch = [&](UnitRegs<NR, CPL>& R, int k) {
+    const int kp = k < cnt ? k : cnt - 1;
+    if (k < cnt && (k & 63) == 0) idv = load_ids(k);
+    const int p = __builtin_amdgcn_readlane(idv, kp & 63);
+    load_unit<GRP, NR, TPL, CPL>(R, off, unit_rec(p), unit_nrm(p), L);
   };
-  auto unit_nrm = [&](int p) { return A.pool_norm + static_cast<size_t>(p) * 32; };
-  auto block_at = [&](int k) { return table[first + 4 * (k < cnt ? k : cnt - 1)]; };
-  if (cnt > 0) {
-    UnitRegs<NR, CPL> ra, rb;
-    int p_cur = checked(block_at(0));
-    int p_nxt = block_at(1);
-    load_unit<GRP, NR, TPL, CPL>(ra, unit_rec(p_cur), unit_nrm(p_cur), L, sm_t0, sm_c0);
-    for (int k = 0; k < cnt; k += 2) {
-      const int p2 = block_at(k + 2);
-      p_nxt = checked(p_nxt);
-      load_unit<GRP, NR, TPL, CPL>(rb, unit_rec(p_nxt), unit_nrm(p_nxt), L, sm_t0, sm_c0);
-      process_int2(ra);
-      if (k + 1 >= cnt) break;
-      const int p3 = block_at(k + 3);
-      const int pa = checked(p2);
-      load_unit<GRP, NR, TPL, CPL>(ra, unit_rec(pa), unit_nrm(pa), L, sm_t0, sm_c0);
-      process_int2(rb);
-      p_nxt = p3;
-    }
+  for (int k = 0; k < cnt; k += 2) {
+    progress_prio(k, cnt);
+    prefetch(rb, k + 1);
+    process_int2(ra);
+    if (k + 1 >= cnt) break;
+    prefetch(ra, k + 2);
+    process_int2(rb);
   }
-  u = first + 4 * cnt;
-
-  // ---------------- fp16 residual-window chunks
-  for (; u < u1; u += 4) {
-    const int tb = Q + kG * (u - nb);
-    const int t_valid = n - tb < 32 ? n - tb : 32;
-    const int slot0 = tb % kR;
-    f32x4 cs[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const u32x4* kr = reinterpret_cast<const u32x4*>(
-          A.res_k + (bh * kR + slot0 + 16 * tau + col) * kD + 32 * g4);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = mfma_f16(kr[kk], S.bq[kk][L], acc);
-      cs[tau] = acc;
-    }
-    store_scores(cs);
-    float nt[TPL];
-#pragma unroll
-    for (int j = 0; j < TPL; ++j)
-      nt[j] = f16_to_f32(A.res_norm[static_cast<size_t>(b) * kR + slot0 + ((sm_t0 + j) & 31)]);
-    softmax_block(nt, 0.0f, t_valid);
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int c = L + 64 * r;
-      if (c < NCOMBO) {
-        const int gv = c / (4 * GRP), hh = (c >> 2) % GRP, g8 = c & 3;
-        float w8[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) w8[k] = W.pr[hh][8 * g8 + k];
-        u32x4 hi, lo;
-        split8(w8, hi, lo);
-        W.bv[gv][bv_row(hh + 16 * g8)] = hi;
-        W.bv[gv][bv_row(hh + GRP + 16 * g8)] = lo;
-      }
-    }
-    lds_order();
-    const u32x4 b0 = W.bv[0][bv_row(L)];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const u32x4 va = *reinterpret_cast<const u32x4*>(
-          A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
-      o[ct] = mfma_f16(va, b0, o[ct]);
-    }
-  }
+  __builtin_amdgcn_s_setprio(0);
 
   // ---------------- this wave's partial: l, Z, o for each head
   const float lsum = group_sum<LPH>(l_part);
@@ -802,55 +886,80 @@ void attn_mfma_kernel(AttnArgs A) {
 
 // ---------------------------------------------------------------- reduce
 // grid (Hq, B), 256 threads: merge the S partials of one query head.  Thread
-// t takes channels 4*(t&31)..+3 of the splits s = t>>5, t>>5 + 8, ...; the 8
-// split lanes are then summed through LDS.
+// t takes channels 4*(t&31)..+3 of the splits s = t>>5 + 8j; it loads up to
+// 16 of them at once and folds them into a running (max, sum, o) of its own;
+// the 8 split lanes of a channel quad are then merged through LDS.
 __global__ __launch_bounds__(256) void lse_reduce_kernel(const float2* __restrict__ ws_ml,
                                                          const float* __restrict__ ws_o, int hq,
                                                          int splits, float* __restrict__ out,
                                                          float* __restrict__ lse) {
-  __shared__ float red_m[256];
+  constexpr int kBatch = 16;
   __shared__ float4 red_o[8][32];
-  __shared__ float red_l[8];
+  __shared__ float red_m[8], red_l[8];
   const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const size_t base = (static_cast<size_t>(b) * hq + i) * splits;
-  float M = -INFINITY;
-  for (int s = t; s < splits; s += 256) M = fmaxf(M, ws_ml[base + s].x);
-  red_m[t] = M;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (t < w) red_m[t] = fmaxf(red_m[t], red_m[t + w]);
-    __syncthreads();
-  }
-  M = red_m[0];
   const int cg = t & 31, sl = t >> 5;
+  float m = -INFINITY, l = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float L = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = sl; s < splits; s += 8) {
-      const float2 ml = ws_ml[base + s];
-      const float w = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
-      const float4 v = reinterpret_cast<const float4*>(ws_o + (base + s) * kD)[cg];
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
-      L += w * ml.y;
+  for (int s0 = sl; s0 < splits; s0 += 8 * kBatch) {
+    float2 ml[kBatch];
+    float4 v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int sj = s0 + 8 * j;
+      if (sj < splits) {
+        ml[j] = ws_ml[base + sj];
+        v[j] = reinterpret_cast<const float4*>(ws_o + (base + sj) * kD)[cg];
+      } else {
+        ml[j] = make_float2(-INFINITY, 0.0f);
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
+    float mb = m;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, ml[j].x);
+    if (mb == -INFINITY) continue;
+    const float f = exp2f(m - mb);  // m == -inf gives 0
+    l *= f;
+    acc.x *= f;
+    acc.y *= f;
+    acc.z *= f;
+    acc.w *= f;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float w = ml[j].x == -INFINITY ? 0.0f : exp2f(ml[j].x - mb);
+      acc.x += w * v[j].x;
+      acc.y += w * v[j].y;
+      acc.z += w * v[j].z;
+      acc.w += w * v[j].w;
+      l += w * ml[j].y;
+    }
+    m = mb;
   }
   red_o[sl][cg] = acc;
-  if (cg == 0) red_l[sl] = L;
+  if (cg == 0) {
+    red_m[sl] = m;
+    red_l[sl] = l;
+  }
   __syncthreads();
   if (t < 32) {
-    float4 a = red_o[0][t];
-    float Lt = red_l[0];
+    float M = -INFINITY;
 #pragma unroll
-    for (int k = 1; k < 8; ++k) {
-      const float4 v = red_o[k][t];
-      a.x += v.x;
-      a.y += v.y;
-      a.z += v.z;
-      a.w += v.w;
-      Lt += red_l[k];
+    for (int k = 0; k < 8; ++k) M = fmaxf(M, red_m[k]);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float Lt = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (red_m[k] == -INFINITY) continue;
+        const float w = exp2f(red_m[k] - M);
+        const float4 v = red_o[k][t];
+        a.x += w * v.x;
+        a.y += w * v.y;
+        a.z += w * v.z;
+        a.w += w * v.w;
+        Lt += w * red_l[k];
+      }
     }
     const bool empty = M == -INFINITY;
     const float inv = empty ? 0.0f : 1.0f / Lt;
