@@ -356,32 +356,15 @@ __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 // l) touch 8 different 16-byte bank groups in every group of 8 lanes.
 __device__ __forceinline__ int bk_row(int x) { return x ^ (4 * ((x >> 4) & 1)); }
 __device__ __forceinline__ int bv_row(int x) { return x ^ (2 * ((x >> 4) & 3)); }
+// A B tile keeps only its NCOL used columns: row c + NCOL g4 holds column c
+// of K step g4, and lane (col, g4) reads row (col % NCOL) + NCOL g4 (lanes of
+// the unused columns read a duplicate).  Rows are permuted as above so that
+// the writers' and readers' 16-byte accesses fall in distinct bank groups.
+template <int NCOL>
+__device__ __forceinline__ int brow_k(int x) { return bk_row(x); }
+template <int NCOL>
+__device__ __forceinline__ int brow_v(int x) { return NCOL == 16 ? bv_row(x) : bk_row(x); }
 constexpr int kRowPad = 36;  // score / probability rows: 32 floats + 4 of padding
-
-template <int GRP>
-struct MfmaWaveLds {
-  u32x4 bk[4][64];          // Key-side B tiles, one per 8-channel step of each group
-  u32x4 bv[4][64];          // Value-side B tiles, one per Value group
-  float sc[16][kRowPad];    // combined raw scores (rows >= GRP take unused columns)
-  float pr[GRP][kRowPad];   // probabilities of the block
-  float fac[GRP];           // rescale factor per head
-  float zs[4][GRP];
-};
-
-template <int GRP>
-struct MfmaMerge {
-  float wm[4][GRP], wl[4][GRP];
-  float wo[4][GRP][kD];
-};
-
-template <int GRP>
-struct MfmaLds {
-  float qs[GRP * kD];  // rotated query heads
-  union {
-    MfmaWaveLds<GRP> w[4];
-    MfmaMerge<GRP> m;
-  };
-};
 
 // Global data one lane needs for one INT2 block.
 // Unit assignments of one block's per-lane work (c = L + 64 r):
@@ -425,36 +408,87 @@ __device__ __forceinline__ T ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
 }
 
+// One LDS stage of the record pipeline: the record's 3072 bytes, then its
+// norm row (64 bytes; the DMA writes 256, lanes past the row reading zero).
+constexpr int kStage = kRec + 256;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct HBM -> LDS copy of one record and its norm row into a stage: lane l
+// moves bytes 16 l .. 16 l + 15 of each kilobyte (no registers involved).
+// Written as inline assembly so that the compiler does not track these LDS
+// writes (its tracking waits for every copy in flight before any LDS access
+// it cannot prove disjoint); the stage readers wait with vmcnt_le4 instead.
+// M0 holds the stage's LDS address.
+__device__ __forceinline__ void dma_unit(__amdgpu_buffer_rsrc_t rec, __amdgpu_buffer_rsrc_t nrm,
+                                         const uint8_t* st, int L) {
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)st));
+  const uint32_t v0 = 16 * L, v1 = 16 * L + 1024, v2 = 16 * L + 2048, vn = 4 * L;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+      "s_add_u32 m0, %0, 0x400\n\t"
+      "buffer_load_dwordx4 %2, %5, 0 offen lds\n\t"
+      "s_add_u32 m0, %0, 0x800\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+      "s_add_u32 m0, %0, 0xc00\n\t"
+      "buffer_load_dword %4, %6, 0 offen lds"
+      :
+      : "s"(base), "v"(v0), "v"(v1), "v"(v2), "v"(vn), "s"(rec), "s"(nrm)
+      : "memory", "m0", "scc");
+}
+// Wait until at most the 4 newest vector-memory loads are in flight: the
+// copy of the next block (4 instructions) may still run, every older one
+// (the block about to be read) has landed in LDS.
+__device__ __forceinline__ void vmcnt_le4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+
+// The lane's operands of one block, from a stage.
+template <class T>
+__device__ __forceinline__ T lds_ld(const uint8_t* st, uint32_t off) {
+  return *reinterpret_cast<const T*>(st + off);
+}
+// Key part (codes, steps, zero points, norms) and Value part (codes,
+// steps and zero points) of a block: the Key part is dead once the block's
+// softmax is done, the Value part once its P.V is issued, so the next block
+// is read into the same registers in two halves.
 template <int GRP, int NR, int TPL, int CPL>
-__device__ __forceinline__ void load_unit(UnitRegs<NR, CPL>& R, const UnitOffs<NR>& O,
-                                          __amdgpu_buffer_rsrc_t rec, __amdgpu_buffer_rsrc_t nrm,
-                                          int L) {
+__device__ __forceinline__ void read_kpart(UnitRegs<NR, CPL>& R, const UnitOffs<NR>& O,
+                                           const uint8_t* st, int L) {
   constexpr int NCOMBO = 16 * GRP;
-  R.kc[0] = ld<u32x2>(rec, O.kc0);
-  R.kc[1] = ld<u32x2>(rec, O.kc1);
-  R.vc = ld<u32x4>(rec, O.vc);
+  R.kc[0] = lds_ld<u32x2>(st, O.kc0);
+  R.kc[1] = lds_ld<u32x2>(st, O.kc1);
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    if (L + 64 * r < NCOMBO) {
-      R.dz[r] = ld<u32x4>(rec, O.dz[r]);
-      R.vp[r][0] = ld<u32x4>(rec, O.vp[r]);
-      R.vp[r][1] = ld<u32x4>(rec, O.vp[r] + 16);
-    }
-  }
+  for (int r = 0; r < NR; ++r)
+    if (L + 64 * r < NCOMBO) R.dz[r] = lds_ld<u32x4>(st, O.dz[r]);
   if (CPL >= 8) {
 #pragma unroll
-    for (int j = 0; j < (CPL + 7) / 8; ++j) R.zz[j] = ld<u32x4>(rec, O.zz + 16 * j);
+    for (int j = 0; j < (CPL + 7) / 8; ++j) R.zz[j] = lds_ld<u32x4>(st, O.zz + 16 * j);
   } else {
-    const u32x2 z2 = ld<u32x2>(rec, O.zz);
+    const u32x2 z2 = lds_ld<u32x2>(st, O.zz);
     R.zz[0] = u32x4{z2[0], z2[1], 0u, 0u};
   }
   if (TPL == 4)
-    R.nrm = ld<u32x2>(nrm, O.nrm);
+    R.nrm = lds_ld<u32x2>(st, kRec + O.nrm);
   else if (TPL == 2)
-    R.nrm[0] = ld<uint32_t>(nrm, O.nrm);
+    R.nrm[0] = lds_ld<uint32_t>(st, kRec + O.nrm);
   else
-    R.nrm[0] = ld<uint16_t>(nrm, O.nrm);
+    R.nrm[0] = lds_ld<uint16_t>(st, kRec + O.nrm);
 }
+template <int GRP, int NR, int TPL, int CPL>
+__device__ __forceinline__ void read_vpart(UnitRegs<NR, CPL>& R, const UnitOffs<NR>& O,
+                                           const uint8_t* st, int L) {
+  constexpr int NCOMBO = 16 * GRP;
+  R.vc = lds_ld<u32x4>(st, O.vc);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (L + 64 * r < NCOMBO) {
+      R.vp[r][0] = lds_ld<u32x4>(st, O.vp[r]);
+      R.vp[r][1] = lds_ld<u32x4>(st, O.vp[r] + 16);
+    }
+  }
+}
+
+// Wait for the wave's outstanding LDS operations (lgkmcnt(0) on gfx9).
+__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 constexpr int kRingWeight = 3;
 
@@ -485,13 +519,31 @@ void attn_mfma_kernel(AttnArgs A) {
   constexpr int NR = (NCOMBO + 63) / 64;        // units per lane
   constexpr int CPL = kD / LPH;                 // q'.z channels per softmax lane
   constexpr float kScale = kInvSqrtD * kLog2e;
-  __shared__ MfmaLds<GRP> S;
+  // LDS, one array per use: the compiler tells distinct arrays apart from
+  // the stages' DMA writes and waits for those only where a stage is read.
+  __shared__ float qs[GRP * kD];                         // rotated query heads
+  __shared__ u32x4 lds_bk[4][4][8 * GRP];                // per wave: Key-side B tiles
+  __shared__ u32x4 lds_bv[4][4][8 * GRP];                // per wave: Value-side B tiles
+  __shared__ float lds_sc[4][2 * GRP][kRowPad];          // per wave: combined raw scores
+  __shared__ float lds_pr[4][GRP][kRowPad];              // per wave: probabilities
+  __shared__ float lds_fac[4][GRP];                      // per wave: rescale factors
+  __shared__ float lds_zs[4][4][GRP];                    // per wave: Value zero-point sums
+  __shared__ float lds_ml[2][4][GRP];                    // per wave: final (m, l)
+  // the two stages of each wave's record pipeline; after the loop they hold
+  // the waves' partial outputs for the merge
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[4][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[4][kStage];
 
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   // wave index as a wave-uniform (scalar) value: unit indices and record
   // addresses then stay in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), L = tid & 63;
-  MfmaWaveLds<GRP>& W = S.w[wave];
+  u32x4 (&Wbk)[4][8 * GRP] = lds_bk[wave];
+  u32x4 (&Wbv)[4][8 * GRP] = lds_bv[wave];
+  float (&Wsc)[2 * GRP][kRowPad] = lds_sc[wave];
+  float (&Wpr)[GRP][kRowPad] = lds_pr[wave];
+  float (&Wfac)[GRP] = lds_fac[wave];
+  float (&Wzs)[4][GRP] = lds_zs[wave];
   // set-up (loads, query rotation, the window chunk) runs at the highest
   // priority: the main loop lowers it as a wave progresses
   __builtin_amdgcn_s_setprio(3);
@@ -512,6 +564,7 @@ void attn_mfma_kernel(AttnArgs A) {
   const int col = L & 15, g4 = L >> 4;
   const int sm_head = L / LPH, sm_t0 = TPL * (L % LPH), sm_c0 = CPL * (L % LPH);
   const bool sm_on = sm_head < GRP;
+  const int krow = brow_k<NCOL>((col % NCOL) + NCOL * g4), vrow = brow_v<NCOL>((col % NCOL) + NCOL * g4);
 
   // The wave's units are u = first + 4k.  The first cnt are INT2 blocks; at
   // most one more (k = cnt) is a chunk of the fp16 window, since the window
@@ -592,10 +645,20 @@ void attn_mfma_kernel(AttnArgs A) {
     for (int j = 0; j < TPL; ++j)
       rnt[j] = f16_to_f32(A.res_norm[static_cast<size_t>(b) * kR + slot0 + ((sm_t0 + j) & 31)]);
   }
-  UnitRegs<NR, CPL> ra, rb;
+  // Block j of the wave goes through stage j % 2.  Its DMA is issued two
+  // blocks ahead (unconditionally: past the end it re-reads the last block)
+  // so that two records are in flight while one is processed.
+  uint8_t* st0 = stage0[wave];
+  uint8_t* st1 = stage1[wave];
+  auto dma_block = [&](int j, uint8_t* st) {
+    const int jc = j < cnt ? j : cnt - 1;
+    if (j < cnt && j > 0 && (j & 63) == 0) idv = load_ids(j);
+    const int p = __builtin_amdgcn_readlane(idv, jc & 63);
+    dma_unit(unit_rec(p), unit_nrm(p), st, L);
+  };
   if (cnt > 0) {
-    const int p = __builtin_amdgcn_readlane(idv, 0);
-    load_unit<GRP, NR, TPL, CPL>(ra, off, unit_rec(p), unit_nrm(p), L);
+    dma_block(0, st0);
+    dma_block(1, st1);
   }
 
 #pragma unroll
@@ -603,45 +666,29 @@ void attn_mfma_kernel(AttnArgs A) {
     const int i = wave + 4 * j;
     if (i < GRP) {
       if (A.q_mode != 2) fht128_wave(qx[j], qy[j]);
-      S.qs[i * kD + L] = qx[j];
-      S.qs[i * kD + L + 64] = qy[j];
+      qs[i * kD + L] = qx[j];
+      qs[i * kD + L + 64] = qy[j];
     }
   }
   __syncthreads();
-  // Alpha unit c: head c % GRP, channels c0 .. c0+7 with
-  // c0 = 32 ((c / GRP) & 3) + 8 (c / (4 GRP)); slot i holds channel c0 + s(i).
-  float qa[NR][8];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const int c = L + 64 * r;
-    const int hh = c % GRP, c0 = 32 * ((c / GRP) & 3) + 8 * ((c / (4 * GRP)) & 3);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qa[r][i] = S.qs[hh * kD + c0 + slot_pos(i)];
-  }
-  // the softmax lane's share of q'.z
-  float zq[CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) zq[j] = sm_on ? S.qs[sm_head * kD + sm_c0 + j] : 0.0f;
-
   float m_run = -INFINITY, l_part = 0.0f;
   float zacc[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) zacc[r] = 0.0f;
-  f32x4 o[8];
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 o[8];  // set by the window chunk or zeroed before the INT2 blocks
 
-  // Online softmax of one block's raw scores (W.sc) in the log2 domain; also
-  // rescales the accumulators when a head's running maximum grows.  Every
-  // processed block has at least one valid token, so m_new is finite.
-  auto softmax_block = [&](const float* nt, float kp, int t_valid) {
+  // Online softmax of one block's raw scores (Wsc) in the log2 domain; also
+  // rescales the accumulators when a head's running maximum grows (nothing to
+  // rescale in a wave's first block).  Every processed block has at least one
+  // valid token, so m_new is finite.
+  auto softmax_block = [&](const float* nt, float kp, int t_valid, bool first) {
     float sv[TPL];
     float bm = -INFINITY;
     if (sm_on) {
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         const int t = sm_t0 + j;
-        sv[j] = t < t_valid ? (W.sc[sm_head][t] + kp) * nt[j] * kScale : -INFINITY;
+        sv[j] = t < t_valid ? (Wsc[sm_head][t] + kp) * nt[j] * kScale : -INFINITY;
         bm = fmaxf(bm, sv[j]);
       }
     }
@@ -654,42 +701,42 @@ void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         const float pj = __builtin_amdgcn_exp2f(sv[j] - m_new);  // -inf gives 0
-        W.pr[sm_head][sm_t0 + j] = pj;
+        Wpr[sm_head][sm_t0 + j] = pj;
         ps += pj;
       }
       l_part = l_part * f + ps;
     }
     m_run = m_new;
-    if (__any(grow)) {
+    if (!first && __any(grow)) {
       // rare after the first blocks: rescale the heads whose maximum grew
-      if (sm_on && (L % LPH) == 0) W.fac[sm_head] = f;
+      if (sm_on && (L % LPH) == 0) Wfac[sm_head] = f;
       lds_order();
-      const float fo = col < NCOL ? W.fac[col % GRP] : 1.0f;
+      const float fo = col < NCOL ? Wfac[col % GRP] : 1.0f;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) o[ct] *= fo;
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const int c = L + 64 * r;
-        if (c < NCOMBO) zacc[r] *= W.fac[(c >> 2) % GRP];
+        if (c < NCOMBO) zacc[r] *= Wfac[(c >> 2) % GRP];
       }
     }
     lds_order();
   };
 
-  // combine the hi and lo columns of the q.K^T tiles into W.sc (every lane
-  // stores; rows GRP..15 receive the unused columns)
+  // combine the hi and lo columns of the q.K^T tiles into Wsc (rows
+  // GRP..NCOL-1 receive sums with unused columns)
   auto store_scores = [&](const f32x4* cs) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       f32x4 v;
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = cs[tau][j] + dpp<dpp_row_shl(GRP)>(cs[tau][j]);
-      *reinterpret_cast<f32x4*>(&W.sc[col][16 * tau + 4 * g4]) = v;
+      if (col < NCOL) *reinterpret_cast<f32x4*>(&Wsc[col][16 * tau + 4 * g4]) = v;
     }
     lds_order();
   };
 
-  // P.V operands of one block from W.pr: W unit c -> group c / (4 GRP),
+  // P.V operands of one block from Wpr: W unit c -> group c / (4 GRP),
   // head (c >> 2) % GRP, token octet c & 3
   auto pv_tiles = [&](const UnitRegs<NR, CPL>* cur) {
 #pragma unroll
@@ -697,8 +744,8 @@ void attn_mfma_kernel(AttnArgs A) {
       const int c = L + 64 * r;
       if (c < NCOMBO) {
         const int gv = c / (4 * GRP), hh = (c >> 2) % GRP, g8 = c & 3;
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(&W.pr[hh][8 * g8]);
-        const f32x4 p1 = *reinterpret_cast<const f32x4*>(&W.pr[hh][8 * g8 + 4]);
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(&Wpr[hh][8 * g8]);
+        const f32x4 p1 = *reinterpret_cast<const f32x4*>(&Wpr[hh][8 * g8 + 4]);
         const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
         u32x4 hi, lo;
         if (cur) {
@@ -715,8 +762,8 @@ void attn_mfma_kernel(AttnArgs A) {
         } else {
           split8(pv, hi, lo);
         }
-        W.bv[gv][bv_row(hh + 16 * g8)] = hi;
-        W.bv[gv][bv_row(hh + GRP + 16 * g8)] = lo;
+        Wbv[gv][brow_v<NCOL>(hh + NCOL * g8)] = hi;
+        Wbv[gv][brow_v<NCOL>(hh + GRP + NCOL * g8)] = lo;
       }
     }
     lds_order();
@@ -729,7 +776,7 @@ void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       float x[8];
-      const float* q = S.qs + (col % GRP) * kD + 32 * g4 + 8 * kk;
+      const float* q = qs + (col % GRP) * kD + 32 * g4 + 8 * kk;
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = q[i];
       u32x4 hi, lo;
@@ -745,15 +792,33 @@ void attn_mfma_kernel(AttnArgs A) {
       cs[tau] = acc;
     }
     store_scores(cs);
-    softmax_block(rnt, 0.0f, ring_valid);
+    softmax_block(rnt, 0.0f, ring_valid, true);
     pv_tiles(nullptr);
-    const u32x4 b0 = W.bv[0][bv_row(L)];
+    const u32x4 b0 = Wbv[0][vrow];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) o[ct] = mfma_f16(rv[ct], b0, o[ct]);
+    for (int ct = 0; ct < 8; ++ct) o[ct] = mfma_f16(rv[ct], b0, f32x4{0.f, 0.f, 0.f, 0.f});
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // Alpha unit c: head c % GRP, channels c0 .. c0+7 with
+  // c0 = 32 ((c / GRP) & 3) + 8 (c / (4 GRP)); slot i holds channel c0 + s(i).
+  float qa[NR][8];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int c = L + 64 * r;
+    const int hh = c % GRP, c0 = 32 * ((c / GRP) & 3) + 8 * ((c / (4 * GRP)) & 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qa[r][i] = qs[hh * kD + c0 + slot_pos(i)];
+  }
+  // the softmax lane's share of q'.z
+  float zq[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) zq[j] = sm_on ? qs[sm_head * kD + sm_c0 + j] : 0.0f;
+
 
   // ---------------- quantized blocks, software-pipelined one block ahead
-  auto process_int2 = [&](const UnitRegs<NR, CPL>& cur) {
+  auto process_int2 = [&](const UnitRegs<NR, CPL>& cur, auto&& after_qk, auto&& after_softmax) {
     // alpha units: q' * delta as hi/lo B tiles
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -768,8 +833,8 @@ void attn_mfma_kernel(AttnArgs A) {
         }
         u32x4 hi, lo;
         split8_mul(qa[r], d8, hi, lo);
-        W.bk[kk][bk_row(hh + 16 * g)] = hi;
-        W.bk[kk][bk_row(hh + GRP + 16 * g)] = lo;
+        Wbk[kk][brow_k<NCOL>(hh + NCOL * g)] = hi;
+        Wbk[kk][brow_k<NCOL>(hh + GRP + NCOL * g)] = lo;
       }
     }
     // q'.z of the softmax lane's head (one row of lanes)
@@ -786,49 +851,65 @@ void attn_mfma_kernel(AttnArgs A) {
       const uint32_t e0 = even_fields(cur.kc[tau][0]), o0 = odd_fields(cur.kc[tau][0]);
       const uint32_t e1 = even_fields(cur.kc[tau][1]), o1 = odd_fields(cur.kc[tau][1]);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int row = bk_row(L);
-      acc = mfma_f16(code_tile<0>(e0, o0), W.bk[0][row], acc);
-      acc = mfma_f16(code_tile<1>(e0, o0), W.bk[1][row], acc);
-      acc = mfma_f16(code_tile<0>(e1, o1), W.bk[2][row], acc);
-      acc = mfma_f16(code_tile<1>(e1, o1), W.bk[3][row], acc);
+      acc = mfma_f16(code_tile<0>(e0, o0), Wbk[0][krow], acc);
+      acc = mfma_f16(code_tile<1>(e0, o0), Wbk[1][krow], acc);
+      acc = mfma_f16(code_tile<0>(e1, o1), Wbk[2][krow], acc);
+      acc = mfma_f16(code_tile<1>(e1, o1), Wbk[3][krow], acc);
       cs[tau] = acc;
     }
+    after_qk();
     store_scores(cs);
 
     float nt[TPL];
 #pragma unroll
     for (int j = 0; j < TPL; ++j)
       nt[j] = (j & 1) ? h_hi(cur.nrm[j >> 1]) : h_lo(cur.nrm[j >> 1]);
-    softmax_block(nt, kz, 32);
+    softmax_block(nt, kz, 32, false);
+    after_softmax();
     pv_tiles(&cur);
 
     // P.V on the matrix cores: tile ct = channels 16 ct .. 16 ct + 15
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const uint32_t e = even_fields(cur.vc[d]), od = odd_fields(cur.vc[d]);
-      const u32x4 bvd = W.bv[d][bv_row(L)];
+      const u32x4 bvd = Wbv[d][vrow];
       o[2 * d] = mfma_f16(code_tile<0>(e, od), bvd, o[2 * d]);
       o[2 * d + 1] = mfma_f16(code_tile<1>(e, od), bvd, o[2 * d + 1]);
     }
   };
-  // Two register sets take turns: block k + 1 loads into one while block k
-  // in the other is processed.  The prefetch is issued unconditionally
-  // (after the last block it re-reads the last, cached one) so that the
-  // compiler can count the outstanding loads exactly and never waits for the
-  // prefetch early.
-  auto prefetch = [&](UnitRegs<NR, CPL>& R, int k) {
-    const int kp = k < cnt ? k : cnt - 1;
-    if (k < cnt && (k & 63) == 0) idv = load_ids(k);
-    const int p = __builtin_amdgcn_readlane(idv, kp & 63);
-    load_unit<GRP, NR, TPL, CPL>(R, off, unit_rec(p), unit_nrm(p), L);
+  // One register set: block k + 1 is read from its stage into it in two
+  // halves while block k is processed (Key part after k's softmax, Value part
+  // after k's P.V); block k's stage is refilled with block k + 2 once k's
+  // Q.K^T has been issued.  Copies of blocks k + 1 and k + 2 are in flight
+  // during most of block k.
+  UnitRegs<NR, CPL> ru;
+  // Every load issued so far has landed (blocks 0 and 1 included): a wait
+  // the compiler sees on every path into the loop, so that it keeps no stale
+  // wait for earlier register loads inside the loop, where a full wait would
+  // also stall on the copies in flight.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  if (cnt > 0) {
+    read_kpart<GRP, NR, TPL, CPL>(ru, off, st0, L);
+    read_vpart<GRP, NR, TPL, CPL>(ru, off, st0, L);
+  }
+  auto step = [&](int k, uint8_t* stc, uint8_t* stn) {
+    progress_prio(k, cnt);
+    process_int2(
+        ru,
+        [&]() {
+          lds_wait();  // block k's stage has been read completely
+          dma_block(k + 2, stc);
+        },
+        [&]() {
+          vmcnt_le4();  // block k + 1's copy has landed (k + 2's may still run)
+          read_kpart<GRP, NR, TPL, CPL>(ru, off, stn, L);
+        });
+    read_vpart<GRP, NR, TPL, CPL>(ru, off, stn, L);
   };
   for (int k = 0; k < cnt; k += 2) {
-    progress_prio(k, cnt);
-    prefetch(rb, k + 1);
-    process_int2(ra);
+    step(k, st0, st1);
     if (k + 1 >= cnt) break;
-    prefetch(ra, k + 2);
-    process_int2(rb);
+    step(k + 1, st1, st0);
   }
   __builtin_amdgcn_s_setprio(0);
 
@@ -838,7 +919,7 @@ void attn_mfma_kernel(AttnArgs A) {
   for (int r = 0; r < NR; ++r) {
     const int c = L + 64 * r;
     const float z = group_sum<4>(zacc[r]);
-    if (c < NCOMBO && (c & 3) == 0) W.zs[c / (4 * GRP)][(c >> 2) % GRP] = z;
+    if (c < NCOMBO && (c & 3) == 0) Wzs[c / (4 * GRP)][(c >> 2) % GRP] = z;
   }
   lds_order();
   float ov[8][4];
@@ -846,16 +927,23 @@ void attn_mfma_kernel(AttnArgs A) {
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      ov[ct][j] = o[ct][j] + dpp<dpp_row_shl(GRP)>(o[ct][j]) + (col < GRP ? W.zs[ct >> 1][col] : 0.0f);
-  __syncthreads();  // every wave is done with its LDS tiles; reuse them for the merge
+      ov[ct][j] = o[ct][j] + dpp<dpp_row_shl(GRP)>(o[ct][j]) + (col < GRP ? Wzs[ct >> 1][col] : 0.0f);
+  // the stages take the waves' partial outputs: head hh of wave w at
+  // (hh < 4 ? stage0 : stage1)[w] + 512 (hh % 4) bytes, once every copy into
+  // them has landed
+  auto wo_at = [&](int w, int hh) {
+    return reinterpret_cast<float*>((hh < 4 ? stage0[w] : stage1[w]) + 512 * (hh & 3));
+  };
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   if (sm_on && (L % LPH) == 0) {
-    S.m.wm[wave][sm_head] = m_run;
-    S.m.wl[wave][sm_head] = lsum;
+    lds_ml[0][wave][sm_head] = m_run;
+    lds_ml[1][wave][sm_head] = lsum;
   }
   if (col < GRP) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
-      *reinterpret_cast<f32x4*>(&S.m.wo[wave][col][16 * ct + 4 * g4]) =
+      *reinterpret_cast<f32x4*>(wo_at(wave, col) + 16 * ct + 4 * g4) =
           f32x4{ov[ct][0], ov[ct][1], ov[ct][2], ov[ct][3]};
   }
   __syncthreads();
@@ -866,16 +954,16 @@ void attn_mfma_kernel(AttnArgs A) {
     const int hh = idx >> 7, c = idx & 127;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, S.m.wm[w][hh]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, lds_ml[0][w][hh]);
     float Lw = 0.0f, Ow = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float mw = S.m.wm[w][hh];
+        const float mw = lds_ml[0][w][hh];
         if (mw == -INFINITY) continue;
         const float sc = exp2f(mw - M);
-        Lw += sc * S.m.wl[w][hh];
-        Ow += sc * S.m.wo[w][hh][c];
+        Lw += sc * lds_ml[1][w][hh];
+        Ow += sc * wo_at(w, hh)[c];
       }
     }
     const size_t part = pbase + static_cast<size_t>(hh) * A.splits + s;
