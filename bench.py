@@ -32,6 +32,26 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
+ATTN_SRC = os.path.join(ROOT, "int2_kv_cache_amd", "csrc", "oscar_attn.hip")
+PROFILE = os.path.join(ROOT, "profiles", "decode_attn_qwen3-8b-128k.md")
+
+
+def counter_traffic():
+    """HBM bytes of one attention launch from the committed rocprofv3 counters
+    (FETCH_SIZE / WRITE_SIZE, scaled by the same counters on a plain copy),
+    or None when the attention source has changed since they were taken."""
+    import hashlib
+    try:
+        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+        line = [l for l in open(PROFILE) if l.startswith("counters:")][0]
+    except (OSError, IndexError):
+        return None
+    kv = dict(tok.split("=") for tok in line.split()[1:])
+    if kv.get("src") != src:
+        return None
+    kib = float(kv["fetch_kib"]) * float(kv["fetch_factor"]) + \
+        float(kv["write_kib"]) * float(kv["write_factor"])
+    return kib * 1024.0
 
 
 def algorithmic_bytes(n: int, Q: int, hq: int, hkv: int) -> int:
@@ -219,8 +239,9 @@ def main():
         "attn_us": attn_us,
         "append_plus_gaps_us": us_per_layer - attn_us,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode_attn (split-K + LSE reduce)",
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counter_traffic(),
+                     "kernel": "decode_attn (split-K attention + LSE reduce, timed together)",
                      "algorithmic_bytes": bytes_attn},
         "prefill_ms_per_layer": float(np.median(pre_ms)),
         "prefill_tokens_per_s": (args.ctx - 1) / (float(np.median(pre_ms)) / 1000.0),
