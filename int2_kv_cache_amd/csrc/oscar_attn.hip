@@ -522,10 +522,13 @@ void attn_mfma_kernel(AttnArgs A) {
   // LDS, one array per use: the compiler tells distinct arrays apart from
   // the stages' DMA writes and waits for those only where a stage is read.
   __shared__ float qs[GRP * kD];                         // rotated query heads
-  __shared__ u32x4 lds_bk[4][4][8 * GRP];                // per wave: Key-side B tiles
-  __shared__ u32x4 lds_bv[4][4][8 * GRP];                // per wave: Value-side B tiles
-  __shared__ float lds_sc[4][2 * GRP][kRowPad];          // per wave: combined raw scores
-  __shared__ float lds_pr[4][GRP][kRowPad];              // per wave: probabilities
+  // per wave: one tile region, used in turn by a block's Key-side B tiles,
+  // its combined scores and probabilities, and its Value-side B tiles (each
+  // user's last reads precede the next user's writes in the wave's program
+  // order, and a wave's LDS operations complete in order)
+  constexpr int kTileBytes = 4 * 8 * GRP * 16;
+  static_assert(2 * GRP * kRowPad * 4 <= kTileBytes, "scores and probabilities fit a tile");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_tile[4][kTileBytes];
   __shared__ float lds_fac[4][GRP];                      // per wave: rescale factors
   __shared__ float lds_zs[4][4][GRP];                    // per wave: Value zero-point sums
   __shared__ float lds_ml[2][4][GRP];                    // per wave: final (m, l)
@@ -538,10 +541,12 @@ void attn_mfma_kernel(AttnArgs A) {
   // wave index as a wave-uniform (scalar) value: unit indices and record
   // addresses then stay in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), L = tid & 63;
-  u32x4 (&Wbk)[4][8 * GRP] = lds_bk[wave];
-  u32x4 (&Wbv)[4][8 * GRP] = lds_bv[wave];
-  float (&Wsc)[2 * GRP][kRowPad] = lds_sc[wave];
-  float (&Wpr)[GRP][kRowPad] = lds_pr[wave];
+  typedef u32x4 BTiles[4][8 * GRP];
+  typedef float Rows[GRP][kRowPad];
+  BTiles& Wbk = *reinterpret_cast<BTiles*>(lds_tile[wave]);
+  BTiles& Wbv = *reinterpret_cast<BTiles*>(lds_tile[wave]);
+  Rows& Wsc = *reinterpret_cast<Rows*>(lds_tile[wave]);
+  Rows& Wpr = *reinterpret_cast<Rows*>(lds_tile[wave] + GRP * kRowPad * 4);
   float (&Wfac)[GRP] = lds_fac[wave];
   float (&Wzs)[4][GRP] = lds_zs[wave];
   // set-up (loads, query rotation, the window chunk) runs at the highest
@@ -624,27 +629,6 @@ void attn_mfma_kernel(AttnArgs A) {
   };
   auto unit_nrm = [&](int p) { return rsrc(A.pool_norm + static_cast<size_t>(p) * 32, 64); };
 
-  // the window chunk and the first INT2 block load while the query is rotated
-  u32x4 rk[2][4], rv[8];
-  float rnt[TPL];
-  int ring_valid = 0, slot0 = 0;
-  if (has_ring) {
-    const int tb = Q + kG * (first + 4 * cnt - nb);
-    ring_valid = n - tb < 32 ? n - tb : 32;
-    slot0 = tb % kR;  // a multiple of 32: the chunk is 32 consecutive slots
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        rk[tau][kk] = *reinterpret_cast<const u32x4*>(
-            A.res_k + (bh * kR + slot0 + 16 * tau + col) * kD + 32 * g4 + 8 * kk);
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-      rv[ct] = *reinterpret_cast<const u32x4*>(A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
-#pragma unroll
-    for (int j = 0; j < TPL; ++j)
-      rnt[j] = f16_to_f32(A.res_norm[static_cast<size_t>(b) * kR + slot0 + ((sm_t0 + j) & 31)]);
-  }
   // Block j of the wave goes through stage j % 2.  Its DMA is issued two
   // blocks ahead (unconditionally: past the end it re-reads the last block)
   // so that two records are in flight while one is processed.
@@ -723,15 +707,14 @@ void attn_mfma_kernel(AttnArgs A) {
     lds_order();
   };
 
-  // combine the hi and lo columns of the q.K^T tiles into Wsc (rows
-  // GRP..NCOL-1 receive sums with unused columns)
+  // combine the hi and lo columns of the q.K^T tiles into Wsc
   auto store_scores = [&](const f32x4* cs) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       f32x4 v;
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = cs[tau][j] + dpp<dpp_row_shl(GRP)>(cs[tau][j]);
-      if (col < NCOL) *reinterpret_cast<f32x4*>(&Wsc[col][16 * tau + 4 * g4]) = v;
+      if (col < GRP) *reinterpret_cast<f32x4*>(&Wsc[col][16 * tau + 4 * g4]) = v;
     }
     lds_order();
   };
@@ -739,13 +722,25 @@ void attn_mfma_kernel(AttnArgs A) {
   // P.V operands of one block from Wpr: W unit c -> group c / (4 GRP),
   // head (c >> 2) % GRP, token octet c & 3
   auto pv_tiles = [&](const UnitRegs<NR, CPL>* cur) {
+    // every unit's probabilities are read before any B tile is written: the
+    // tiles share their LDS region with Wpr
+    f32x4 pq[NR][2];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int c = L + 64 * r;
+      if (c < NCOMBO) {
+        const int hh = (c >> 2) % GRP, g8 = c & 3;
+        pq[r][0] = *reinterpret_cast<const f32x4*>(&Wpr[hh][8 * g8]);
+        pq[r][1] = *reinterpret_cast<const f32x4*>(&Wpr[hh][8 * g8 + 4]);
+      }
+    }
+    lds_order();
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const int c = L + 64 * r;
       if (c < NCOMBO) {
         const int gv = c / (4 * GRP), hh = (c >> 2) % GRP, g8 = c & 3;
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(&Wpr[hh][8 * g8]);
-        const f32x4 p1 = *reinterpret_cast<const f32x4*>(&Wpr[hh][8 * g8 + 4]);
+        const f32x4 p0 = pq[r][0], p1 = pq[r][1];
         const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
         u32x4 hi, lo;
         if (cur) {
@@ -769,38 +764,8 @@ void attn_mfma_kernel(AttnArgs A) {
     lds_order();
   };
 
-  // ---------------- the fp16 window chunk (its data is already loaded)
-  if (has_ring) {
-    // q' hi/lo B tiles, channels 32 g4 + 8 kk + 0..7 in natural order
-    u32x4 bq[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      float x[8];
-      const float* q = qs + (col % GRP) * kD + 32 * g4 + 8 * kk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = q[i];
-      u32x4 hi, lo;
-      split8(x, hi, lo);
-      bq[kk] = col < GRP ? hi : lo;  // columns >= 2 GRP are unused
-    }
-    f32x4 cs[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = mfma_f16(rk[tau][kk], bq[kk], acc);
-      cs[tau] = acc;
-    }
-    store_scores(cs);
-    softmax_block(rnt, 0.0f, ring_valid, true);
-    pv_tiles(nullptr);
-    const u32x4 b0 = Wbv[0][vrow];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) o[ct] = mfma_f16(rv[ct], b0, f32x4{0.f, 0.f, 0.f, 0.f});
-  } else {
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Alpha unit c: head c % GRP, channels c0 .. c0+7 with
   // c0 = 32 ((c / GRP) & 3) + 8 (c / (4 GRP)); slot i holds channel c0 + s(i).
   float qa[NR][8];
@@ -912,6 +877,55 @@ void attn_mfma_kernel(AttnArgs A) {
     step(k + 1, st1, st0);
   }
   __builtin_amdgcn_s_setprio(0);
+
+  // ---------------- the fp16 window chunk, last (its loads are issued here,
+  // when the INT2 registers are free; splits weigh a chunk as kRingWeight
+  // blocks to make up for the exposed latency)
+  if (has_ring) {
+    const int tb = Q + kG * (first + 4 * cnt - nb);
+    const int ring_valid = n - tb < 32 ? n - tb : 32;
+    const int slot0 = tb % kR;  // a multiple of 32: the chunk is 32 consecutive slots
+    u32x4 rk[2][4], rv[8];
+    float rnt[TPL];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        rk[tau][kk] = *reinterpret_cast<const u32x4*>(
+            A.res_k + (bh * kR + slot0 + 16 * tau + col) * kD + 32 * g4 + 8 * kk);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      rv[ct] = *reinterpret_cast<const u32x4*>(A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
+#pragma unroll
+    for (int j = 0; j < TPL; ++j)
+      rnt[j] = f16_to_f32(A.res_norm[static_cast<size_t>(b) * kR + slot0 + ((sm_t0 + j) & 31)]);
+    // q' hi/lo B tiles, channels 32 g4 + 8 kk + 0..7 in natural order
+    u32x4 bq[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      float x[8];
+      const float* q = qs + (col % GRP) * kD + 32 * g4 + 8 * kk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = q[i];
+      u32x4 hi, lo;
+      split8(x, hi, lo);
+      bq[kk] = col < GRP ? hi : lo;  // columns >= 2 GRP are unused
+    }
+    f32x4 cs[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mfma_f16(rk[tau][kk], bq[kk], acc);
+      cs[tau] = acc;
+    }
+    store_scores(cs);
+    softmax_block(rnt, 0.0f, ring_valid, cnt == 0);
+    pv_tiles(nullptr);
+    const u32x4 b0 = Wbv[0][vrow];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) o[ct] = mfma_f16(rv[ct], b0, o[ct]);
+  }
 
   // ---------------- this wave's partial: l, Z, o for each head
   const float lsum = group_sum<LPH>(l_part);
