@@ -180,8 +180,9 @@ OSCAR_API oscar_status oscar_append_kv(const oscar_cache_geom *geom, const oscar
  * End-to-End Flow: prefill Keys pass FHT, per-token scaling and INT2
  * per-channel quantization before entering the cache).  The resulting cache
  * state is byte-identical, on its valid region, to n_tokens appends.
- *   k, v  device, [n_tokens][Hkv][128] fp16 or bf16.
- * Errors: EINVAL (also when the blocks needed exceed max_blocks_per_seq);
+ *   k, v  device, [n_tokens][Hkv][128] fp16 or bf16, 16-byte aligned.
+ * Errors: EINVAL (also when the blocks needed exceed max_blocks_per_seq, or
+ * k / v are not 16-byte aligned);
  * device: OSCAR_FLAG_NONEMPTY if the sequence already holds tokens. */
 OSCAR_API oscar_status oscar_prefill_quantize(const oscar_cache_geom *geom, const oscar_cache *cache,
                                     int32_t seq, const void *k, const void *v,

@@ -182,38 +182,93 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
 // Lane-parallel INT2 quantizer: the 32 values of a group sit one per lane in
 // a 32-lane half-wave.  Same arithmetic as quant32 (min and max do not depend
 // on the order once a zero is canonicalised to +0).
-__device__ __forceinline__ int quant_lane32(float x, float& d, float& z) {
+
+// ---------------------------------------------------------------- prefill
+// Range of 32 values: zero = min, delta = (max - min) / 3, both from the
+// canonicalised (+0) extremes; 1/delta (0 when delta == 0).
+struct Range {
+  float zero, delta, rdelta;
+  uint32_t zm;  // fp16 bits of min | max << 16 (both fp16 values)
+};
+__device__ __forceinline__ Range range32(const float* x) {
 #pragma clang fp contract(off)
-  float mn = x, mx = x;
+  float mn = x[0], mx = x[0];
 #pragma unroll
-  for (int s = 1; s < 32; s <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, s, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, s, 64));
+  for (int i = 1; i < 32; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
   }
   mn = mn + 0.0f;
   mx = mx + 0.0f;
-  d = __fdiv_rn(mx - mn, 3.0f);
-  z = mn;
-  int q = 0;
-  if (d > 0.0f) {
-    const float r = rintf(__fdiv_rn(x - mn, d));
-    q = r < 0.0f ? 0 : (r > 3.0f ? 3 : static_cast<int>(r));
-  }
-  return q;
+  Range r;
+  r.zero = mn;
+  r.delta = __fdiv_rn(mx - mn, 3.0f);
+  r.rdelta = r.delta > 0.0f ? __fdiv_rn(1.0f, r.delta) : 0.0f;
+  r.zm = static_cast<uint32_t>(f32_to_f16(mn)) | (static_cast<uint32_t>(f32_to_f16(mx)) << 16);
+  return r;
+}
+// The code of x under a stored range (zero and max as fp16 bits, 1/delta),
+// without a per-element division: q1 = (x - zero) * (1/delta), with 1/delta
+// correctly rounded, is within 2^-20 of the correctly rounded quotient
+// (which is <= 3), so both round to the same integer unless q1 lies within
+// 2^-18 of a half integer; there the exact quotient decides.
+__device__ __forceinline__ uint32_t code_zm(float x, uint32_t zm, float rdelta) {
+#pragma clang fp contract(off)
+  if (!(rdelta > 0.0f)) return 0u;
+  const float zero = f16_to_f32(static_cast<uint16_t>(zm));
+  const float mx = f16_to_f32(static_cast<uint16_t>(zm >> 16));
+  const float a = x - zero;
+  const float q1 = a * rdelta;
+  float q = q1;
+  if (fabsf((q1 - floorf(q1)) - 0.5f) <= 0x1p-18f) q = __fdiv_rn(a, __fdiv_rn(mx - zero, 3.0f));
+  const float r = rintf(q);
+  return r < 0.0f ? 0u : (r > 3.0f ? 3u : static_cast<uint32_t>(r));
 }
 
-// grid nb + nr: block j < nb quantizes tokens 32j..32j+31 (all KV heads);
-// block nb + c writes ring chunk c (tokens Q + 32c ..) without quantizing.
-// 256 threads.  Dynamic LDS: k_hat [32][Hkv][128] fp16 + images [Hkv][512].
-__global__ __launch_bounds__(256) void prefill_kernel(CacheArgs ca, int seq,
-                                                      const uint16_t* __restrict__ k,
-                                                      const uint16_t* __restrict__ v,
-                                                      int n_tokens, int Qn, int is_bf16) {
-  extern __shared__ uint32_t dyn[];
+// Quad cross-lane read (lanes 4m..4m+3 exchange): xor 1 or xor 2.
+template <int X>
+__device__ __forceinline__ float quad_xor(float x) {
+  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xF, 0xF, true));
+}
+
+// grid nb + nr, 1024 threads: workgroup j < nb turns tokens 32j..32j+31 (all
+// KV heads) into block j; workgroup nb + c writes window chunk c (tokens
+// Q + 32c ..) without quantizing.
+//
+// Rotation: four lanes per (token, head) vector, lane tq holding elements
+// 32 tq .. 32 tq + 31; butterflies with strides 1..16 are in registers,
+// strides 32 and 64 exchange within the lane quad -- the oracle's stages in
+// the oracle's order.  The sum of squares follows the same tree (strides
+// 1..16 in registers, 32 and 64 across the quad, then over the heads).
+// Quantization without atomics: every Key range (head, channel) and Value
+// range (token, head, group) is computed once and kept in LDS, then each
+// thread assembles whole code words (Key: 4 words of one token row; Value:
+// 4 words of one token octet) and stores them.
+// Dynamic LDS: k_hat [32][Hkv][128] fp16, then the ranges region (Key
+// [Hkv][128] and Value [32][Hkv][4] x (1/delta, zero|max)); the rotation
+// phase borrows the ranges region for the per-head sums and per-token
+// factors.
+constexpr int kPrefillThreads = 1024;
+size_t prefill_lds_bytes(int hkv) {
+  return static_cast<size_t>(hkv) * (32 * kD * 2 + 2 * 1024);
+}
+
+__global__ __launch_bounds__(1024) void prefill_kernel(CacheArgs ca, int seq,
+                                                       const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v,
+                                                       int n_tokens, int Qn, int is_bf16) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int hkv = ca.hkv;
-  uint16_t* khs = reinterpret_cast<uint16_t*>(dyn);         // [32][hkv][128]
-  uint32_t* imgs = dyn + 32 * hkv * kD / 2;                   // [hkv][512]
-  __shared__ float nrm_s[32];
+  uint16_t* khs = reinterpret_cast<uint16_t*>(dyn);                      // [32][hkv][128]
+  uint8_t* prm = dyn + static_cast<size_t>(32) * hkv * kD * 2;           // ranges region
+  float* k_rd = reinterpret_cast<float*>(prm);                          // [hkv*128]
+  uint32_t* k_zm = reinterpret_cast<uint32_t*>(k_rd + hkv * kD);         // [hkv*128]
+  float* v_rd = reinterpret_cast<float*>(k_zm + hkv * kD);               // [32*hkv*4]
+  uint32_t* v_zm = reinterpret_cast<uint32_t*>(v_rd + 32 * hkv * 4);     // [32*hkv*4]
+  float* part = reinterpret_cast<float*>(prm);                          // rotation phase: [32][hkv]
+  float* tok_r = part + 32 * hkv;                                        // [32]
+
   if (ca.seq_state[2 * seq] != 0) {
     if (blockIdx.x == 0 && threadIdx.x == 0)
       atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_NONEMPTY));
@@ -222,113 +277,200 @@ __global__ __launch_bounds__(256) void prefill_kernel(CacheArgs ca, int seq,
   const int nb = Qn / kG;
   const bool ring = static_cast<int>(blockIdx.x) >= nb;
   const int t0 = ring ? Qn + 32 * (blockIdx.x - nb) : 32 * blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
   const size_t row = static_cast<size_t>(hkv) * kD;
   const int p = ring ? 0 : ca.block_table[static_cast<size_t>(seq) * ca.max_blocks + blockIdx.x];
   if (p < 0 || p >= ca.nphys) {
     if (threadIdx.x == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
     return;
   }
+  auto rec_of = [&](int h) { return ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec; };
 
-  if (!ring) {
-    for (int i = tid; i < hkv * 512; i += 256) imgs[i] = 0;
-    __syncthreads();
-  }
-  // Token phase: wave w takes tokens w, w+4, ...: rotate + scale every head
-  // of the token, then (quantized blocks) Value quantization per token.
-  for (int tt = wave; tt < 32; tt += 4) {
-    const int t = t0 + tt;
-    if (t >= n_tokens) break;  // ring chunk tail; uniform per wave
-    float ya[16], yb[16];
-    float part[16];
+  // ---- rotation and sums of squares (1 round for Hkv <= 8, 2 for Hkv <= 16)
+  const int nvec = 32 * hkv;
+  float y[2][32];
 #pragma unroll
-    for (int h = 0; h < 16; ++h) {
-      part[h] = 0.0f;
-      if (h < hkv) {
-        const size_t base = static_cast<size_t>(t) * row + h * kD;
-        float a = in_to_f32(k[base + lane], is_bf16);
-        float b = in_to_f32(k[base + lane + 64], is_bf16);
-        fht128_wave(a, b);
-        part[h] = wave_tree_sumsq(a, b);
-        ya[h] = a;
-        yb[h] = b;
-      }
-    }
-    float nrm, r;
-    scale_from_ss(tree16(part, hkv), nrm, r);
-    const int slot = t % kR;
+  for (int rr = 0; rr < 2; ++rr) {
+    const int task = rr * kPrefillThreads + tid;
+    const int vtx = task >> 2, tq = task & 3;
+    if (rr * kPrefillThreads >= nvec * 4) break;  // uniform
+    const int t = vtx / hkv, h = vtx % hkv;
+    const bool valid = vtx < nvec && t0 + t < n_tokens;
+    float* x = y[rr];
+    if (valid) {
+      const uint16_t* src = k + static_cast<size_t>(t0 + t) * row + h * kD + 32 * tq;
 #pragma unroll
-    for (int h = 0; h < 16; ++h) {
-      if (h < hkv) {
-        const uint16_t ka = f32_to_f16(mul_rn(ya[h], r)), kb = f32_to_f16(mul_rn(yb[h], r));
-        const size_t base = static_cast<size_t>(t) * row + h * kD;
-        const uint16_t va = f32_to_f16(in_to_f32(v[base + lane], is_bf16));
-        const uint16_t vb = f32_to_f16(in_to_f32(v[base + lane + 64], is_bf16));
-        if (ring) {
-          const size_t bh = static_cast<size_t>(seq) * hkv + h;
-          uint16_t* rk = ca.res_k + (bh * kR + slot) * kD;
-          rk[lane] = ka;
-          rk[lane + 64] = kb;
-          uint16_t* rv = ca.res_v + bh * kD * kR + slot;
-          rv[static_cast<size_t>(lane) * kR] = va;
-          rv[static_cast<size_t>(lane + 64) * kR] = vb;
-        } else {
-          khs[(tt * hkv + h) * kD + lane] = ka;
-          khs[(tt * hkv + h) * kD + lane + 64] = kb;
-          // Value groups: lanes 0..31 / 32..63 of register a are groups 0 / 1,
-          // of register b groups 2 / 3.
-          float da, za, db, zb;
-          const int qa = quant_lane32(f16_to_f32(va), da, za);
-          const int qb = quant_lane32(f16_to_f32(vb), db, zb);
-          uint32_t* img = imgs + h * 512 + 256;
-          const int bita = vcode_bitpos(tt, lane), bitb = vcode_bitpos(tt, lane + 64);
-          atomicOr(&img[bita >> 5], static_cast<uint32_t>(qa) << (bita & 31));
-          atomicOr(&img[bitb >> 5], static_cast<uint32_t>(qb) << (bitb & 31));
-          uint8_t* rec = ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec;
-          uint32_t* vp = reinterpret_cast<uint32_t*>(rec + kRecVParam);
-          if ((lane & 31) == 0) {
-            const int g = lane >> 5;
-            vp[32 * g + tt] = static_cast<uint32_t>(f32_to_f16(da)) |
-                             (static_cast<uint32_t>(f32_to_f16(za)) << 16);
-            vp[32 * (2 + g) + tt] = static_cast<uint32_t>(f32_to_f16(db)) |
-                                 (static_cast<uint32_t>(f32_to_f16(zb)) << 16);
-          }
+      for (int q = 0; q < 4; ++q) {
+        const uint4 w = reinterpret_cast<const uint4*>(src)[q];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * q + 2 * e] = in_to_f32(static_cast<uint16_t>(ww[e]), is_bf16);
+          x[8 * q + 2 * e + 1] = in_to_f32(static_cast<uint16_t>(ww[e] >> 16), is_bf16);
         }
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) x[j] = 0.0f;
     }
-    if (lane == 0) {
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int hs = 1; hs < 32; hs <<= 1)
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+          if ((j & hs) == 0) {
+            const float a = x[j], b = x[j + hs];
+            x[j] = a + b;
+            x[j + hs] = a - b;
+          }
+      // strides 32 and 64: the partner is lane tq ^ 1, then tq ^ 2
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float pj = quad_xor<1>(x[j]);
+        x[j] = (tq & 1) ? (pj - x[j]) : (x[j] + pj);
+      }
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float pj = quad_xor<2>(x[j]);
+        x[j] = (tq & 2) ? (pj - x[j]) : (x[j] + pj);
+      }
+#pragma unroll
+      for (int j = 0; j < 32; ++j) x[j] = x[j] * kFhtScale;
+      float sq[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) sq[j] = x[j] * x[j];
+#pragma unroll
+      for (int hs = 1; hs < 32; hs <<= 1)
+#pragma unroll
+        for (int j = 0; j < 32; j += 2 * hs) sq[j] = sq[j] + sq[j + hs];
+      float ssum = sq[0];
+      ssum = ssum + quad_xor<1>(ssum);
+      ssum = ssum + quad_xor<2>(ssum);
+      if (tq == 0 && vtx < nvec) part[t * hkv + h] = ssum;
+    }
+  }
+  __syncthreads();
+  if (tid < 32) {
+    float nrm, r;
+    scale_from_ss(tree16(part + tid * hkv, hkv), nrm, r);
+    tok_r[tid] = r;
+    const int t = t0 + tid;
+    if (t < n_tokens) {
       if (ring)
-        ca.res_norm[seq * kR + slot] = f32_to_f16(nrm);
+        ca.res_norm[seq * kR + t % kR] = f32_to_f16(nrm);
       else
-        nrm_s[tt] = nrm;
+        ca.pool_norm[static_cast<size_t>(p) * 32 + tid] = f32_to_f16(nrm);
+    }
+  }
+  __syncthreads();
+  // ---- scaled Keys (and, for a window chunk, fp16 Values) to LDS or the ring
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int task = rr * kPrefillThreads + tid;
+    const int vtx = task >> 2, tq = task & 3;
+    if (rr * kPrefillThreads >= nvec * 4) break;
+    const int t = vtx / hkv, h = vtx % hkv;
+    if (vtx < nvec && t0 + t < n_tokens) {
+      const float r = tok_r[t];
+      uint32_t kw[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        kw[e] = static_cast<uint32_t>(f32_to_f16(mul_rn(y[rr][2 * e], r))) |
+                (static_cast<uint32_t>(f32_to_f16(mul_rn(y[rr][2 * e + 1], r))) << 16);
+      uint4* dst;
+      if (ring) {
+        const int slot = (t0 + t) % kR;
+        const size_t bh = static_cast<size_t>(seq) * hkv + h;
+        dst = reinterpret_cast<uint4*>(ca.res_k + (bh * kR + slot) * kD + 32 * tq);
+        const uint16_t* vs = v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * tq;
+        uint16_t* rv = ca.res_v + bh * kD * kR + slot;
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+          rv[static_cast<size_t>(32 * tq + j) * kR] = f32_to_f16(in_to_f32(vs[j], is_bf16));
+      } else {
+        dst = reinterpret_cast<uint4*>(khs + (t * hkv + h) * kD + 32 * tq);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = uint4{kw[4 * q], kw[4 * q + 1], kw[4 * q + 2], kw[4 * q + 3]};
     }
   }
   if (ring) return;
   __syncthreads();
-  if (tid < 32) ca.pool_norm[static_cast<size_t>(p) * 32 + tid] = f32_to_f16(nrm_s[tid]);
-  // Key quantization: per (head, channel) over the block's 32 tokens.
-  for (int u = tid; u < hkv * kD; u += 256) {
-    const int h = u >> 7, c = u & 127;
+
+  // ---- ranges: Key (head, channel) over 32 tokens; Value (token, head, group)
+  const int nku = hkv * kD, nvu = 32 * hkv * 4;
+  for (int u = tid; u < nku + nvu; u += kPrefillThreads) {
     float x[32];
+    if (u < nku) {
+      const int h = u >> 7, c = u & 127;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(khs[(t * hkv + h) * kD + c]);
-    float d, z;
-    const uint64_t codes = quant32(x, d, z);
-    uint32_t* img = imgs + h * 512;
+      for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(khs[(t * hkv + h) * kD + c]);
+      const Range r = range32(x);
+      k_rd[u] = r.rdelta;
+      k_zm[u] = r.zm;
+      uint8_t* rec = rec_of(h);
+      reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(r.delta);
+      reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = static_cast<uint16_t>(r.zm);
+    } else {
+      const int w = u - nku, t = w / (hkv * 4), h = (w >> 2) % hkv, g = w & 3;
+      const uint16_t* src = v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * g;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const int bit = kcode_bitpos(t, c);
-      atomicOr(&img[bit >> 5], static_cast<uint32_t>((codes >> (2 * t)) & 3u) << (bit & 31));
+      for (int i = 0; i < 32; ++i) x[i] = f16_to_f32(f32_to_f16(in_to_f32(src[i], is_bf16)));
+      const Range r = range32(x);
+      v_rd[w] = r.rdelta;
+      v_zm[w] = r.zm;
+      reinterpret_cast<uint32_t*>(rec_of(h) + kRecVParam)[32 * g + t] =
+          static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
     }
-    uint8_t* rec = ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec;
-    reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(d);
-    reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = f32_to_f16(z);
   }
   __syncthreads();
-  for (int i = tid; i < hkv * 128; i += 256) {
-    const int h = i >> 7, q = i & 127;
-    uint8_t* rec = ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec;
-    reinterpret_cast<uint4*>(rec)[q] = reinterpret_cast<const uint4*>(imgs + h * 512)[q];
+
+  // ---- code words.  Key unit (head, token, half): channels 64 half .. +63,
+  // words 4 half .. 4 half + 3 of the token row.  Value unit (head, octet,
+  // group, quarter): slices 16 octet + 4 quarter .. +3, word `group`.
+  const int nkw = hkv * 32 * 2, nvw = hkv * 4 * 4 * 4;
+  for (int u = tid; u < nkw + nvw; u += kPrefillThreads) {
+    if (u < nkw) {
+      const int h = u / 64, t = (u >> 1) & 31, half = u & 1;
+      const uint16_t* kr = khs + (t * hkv + h) * kD + 64 * half;
+      uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        const int c = 64 * half + i;
+        const uint32_t code = code_zm(f16_to_f32(kr[i]), k_zm[h * kD + c], k_rd[h * kD + c]);
+        words[i >> 4] |= code << (2 * (i & 3) + 8 * ((i >> 2) & 3));
+      }
+      *reinterpret_cast<uint4*>(rec_of(h) + kRecKCodes + 32 * t + 16 * half) =
+          uint4{words[0], words[1], words[2], words[3]};
+    } else {
+      const int w = u - nkw, h = w / 64, oct = (w >> 4) & 3, d = (w >> 2) & 3, qt = w & 3;
+      uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int t = 8 * oct + kk;
+        const int pi = (t * hkv + h) * 4 + d;
+        const uint32_t zm = v_zm[pi];
+        const float rd = v_rd[pi];
+        const int sk = (kk & 4) | ((kk & 1) << 1) | ((kk >> 1) & 1);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint16_t* src = v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * d + 16 * e + 4 * qt;
+          const uint2 raw = *reinterpret_cast<const uint2*>(src);
+          const uint16_t vv[4] = {static_cast<uint16_t>(raw.x), static_cast<uint16_t>(raw.x >> 16),
+                                  static_cast<uint16_t>(raw.y), static_cast<uint16_t>(raw.y >> 16)};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = f16_to_f32(f32_to_f16(in_to_f32(vv[i], is_bf16)));
+            words[i] |= code_zm(x, zm, rd) << (2 * (8 * e + sk));
+          }
+        }
+      }
+      uint8_t* rec = rec_of(h) + kRecVCodes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint32_t*>(rec + 16 * (16 * oct + 4 * qt + i) + 4 * d) = words[i];
+    }
   }
 }
 
@@ -402,6 +544,7 @@ extern "C" oscar_status oscar_prefill_quantize(const oscar_cache_geom* geom,
   oscar_status st = check_cache(geom, cache);
   if (st != OSCAR_OK) return st;
   if (!k || !v || n_tokens < 0 || seq < 0 || seq >= geom->batch) return OSCAR_EINVAL;
+  if (!aligned(k, 16) || !aligned(v, 16)) return OSCAR_EINVAL;
   if (dtype != OSCAR_FP16 && dtype != OSCAR_BF16) return OSCAR_EINVAL;
   // Q(n) = 32 * ceil(max(0, n - 128) / 32): the state n appends would leave.
   const int Qb = ((n_tokens > kR ? n_tokens - kR : 0) + 31) / 32;
@@ -411,12 +554,11 @@ extern "C" oscar_status oscar_prefill_quantize(const oscar_cache_geom* geom,
   if (n_tokens == 0) return OSCAR_OK;
   const int Q = 32 * Qb;
   const int nr = (n_tokens - Q + 31) / 32;
-  const size_t lds = static_cast<size_t>(32) * geom->num_kv_heads * kD * sizeof(uint16_t) +
-                     static_cast<size_t>(geom->num_kv_heads) * 512 * sizeof(uint32_t);
+  const size_t lds = prefill_lds_bytes(geom->num_kv_heads);
   if (lds > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  hipLaunchKernelGGL(prefill_kernel, dim3(Qb + nr), dim3(256), lds, as_stream(stream),
+  hipLaunchKernelGGL(prefill_kernel, dim3(Qb + nr), dim3(kPrefillThreads), lds, as_stream(stream),
                      make_args(geom, cache), static_cast<int>(seq),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<int>(n_tokens), Q, dtype == OSCAR_BF16 ? 1 : 0);

@@ -99,6 +99,20 @@ def test_prefill_equals_appends(n):
     pr.compare_state()
 
 
+@pytest.mark.parametrize("hkv", [1, 3, 5, 16])
+def test_prefill_kv_head_counts(hkv):
+    """Bulk prefill with KV-head counts that are not the workloads' 8 (the
+    rotation tree pads the heads to 16; 16 heads take two lane rounds)."""
+    base = synth.workload(2, ctx=300)
+    cfg = synth.Config("hkv", 1, hkv, hkv, 300, synth.BF16, 0.4, (4, 8), 1)
+    outl = (base.outlier_idx * 4)[:hkv]
+    wl = synth.Workload(cfg, 55, [300], outl)
+    pr = Pair(wl)
+    k, v = wl.prefill(0, 299)
+    pr.prefill(0, k, v)
+    pr.compare_state()
+
+
 def test_prefill_then_appends_and_ragged_batch():
     wl = synth.workload(2, ctx=None, batch=3)
     wl.ctx_lens = [300, 1000, 161]
