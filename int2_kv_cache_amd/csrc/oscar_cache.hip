@@ -75,115 +75,6 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restr
   if (h == 0 && tg < 32) norm_out[static_cast<size_t>(j) * 32 + tg] = knorm[32 * j + tg];
 }
 
-// ---------------------------------------------------------------- append
-struct CacheArgs {
-  uint8_t* pool;
-  uint16_t* pool_norm;
-  uint16_t* res_k;
-  uint16_t* res_v;
-  uint16_t* res_norm;
-  const int32_t* block_table;
-  int32_t* seq_state;
-  int32_t* error_flag;
-  int hkv;
-  int max_blocks;
-  int nphys;
-};
-
-// {n, Q} as the kernels leave it: 0 <= Q, Q % 32 == 0, 0 <= n - Q <= 128,
-// Q / 32 <= max_blocks.
-__device__ __forceinline__ bool state_ok(int n, int Q, int max_blocks) {
-  return Q >= 0 && (Q & 31) == 0 && n >= Q && n - Q <= kR && Q / kG <= max_blocks;
-}
-
-// grid B, block max(256, 64*Hkv) rounded up to a multiple of 256.
-__global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16_t* __restrict__ k_new,
-                                                      const uint16_t* __restrict__ v_new,
-                                                      int is_bf16) {
-  __shared__ uint32_t img[4][512];
-  __shared__ float part[16];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int grp = tid >> 8, tg = tid & 255, ngrp = blockDim.x >> 8;
-  const int hkv = ca.hkv;
-  int32_t* st = ca.seq_state + 2 * b;
-  const int n = st[0];
-  int Q = st[1];
-  if (!state_ok(n, Q, ca.max_blocks)) {
-    if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
-    return;
-  }
-
-  if (n - Q == kR) {
-    // The window is full: its 32 oldest tokens become block Q/32.
-    const int j = Q / kG;
-    if (j >= ca.max_blocks) {
-      if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_CAPACITY));
-      return;
-    }
-    const int p = ca.block_table[static_cast<size_t>(b) * ca.max_blocks + j];
-    if (p < 0 || p >= ca.nphys) {
-      if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
-      return;
-    }
-    const int s0 = Q % kR;
-    if (tid < 32) ca.pool_norm[static_cast<size_t>(p) * 32 + tid] = ca.res_norm[b * kR + s0 + tid];
-    for (int h0 = 0; h0 < hkv; h0 += ngrp) {
-      const int h = h0 + grp;
-      for (int i = tg; i < 512; i += 256) img[grp][i] = 0;
-      __syncthreads();
-      uint8_t* rec = ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec;
-      if (h < hkv) {
-        const uint16_t* rk = ca.res_k + ((static_cast<size_t>(b) * hkv + h) * kR + s0) * kD;
-        const uint16_t* rv = ca.res_v + (static_cast<size_t>(b) * hkv + h) * kD * kR + s0;
-        quant_record_units(
-            tg, [&](int t, int c) { return rk[t * kD + c]; },
-            [&](int t, int c) { return rv[c * kR + t]; }, img[grp], rec);
-      }
-      __syncthreads();
-      if (h < hkv) copy_codes_out(tg, img[grp], rec);
-      __syncthreads();
-    }
-    Q += kG;
-  }
-
-  // Rotate + scale the new token; store it in slot n % 128.
-  const int slot = n % kR;
-  const int h = tid >> 6, lane = tid & 63;
-  float a = 0.0f, bb = 0.0f;
-  if (h < hkv) {
-    const size_t base = (static_cast<size_t>(b) * hkv + h) * kD;
-    a = in_to_f32(k_new[base + lane], is_bf16);
-    bb = in_to_f32(k_new[base + lane + 64], is_bf16);
-    fht128_wave(a, bb);
-    const float hs = wave_tree_sumsq(a, bb);
-    if (lane == 0) part[h] = hs;
-  }
-  __syncthreads();
-  if (h < hkv) {
-    float nrm, r;
-    scale_from_ss(tree16(part, hkv), nrm, r);
-    const size_t bh = static_cast<size_t>(b) * hkv + h;
-    uint16_t* rk = ca.res_k + (bh * kR + slot) * kD;
-    rk[lane] = f32_to_f16(mul_rn(a, r));
-    rk[lane + 64] = f32_to_f16(mul_rn(bb, r));
-    const size_t base = bh * kD;
-    uint16_t* rv = ca.res_v + bh * kD * kR + slot;
-    rv[static_cast<size_t>(lane) * kR] = f32_to_f16(in_to_f32(v_new[base + lane], is_bf16));
-    rv[static_cast<size_t>(lane + 64) * kR] = f32_to_f16(in_to_f32(v_new[base + lane + 64], is_bf16));
-    if (h == 0 && lane == 0) ca.res_norm[b * kR + slot] = f32_to_f16(nrm);
-  }
-  if (tid == 0) {
-    st[0] = n + 1;
-    st[1] = Q;
-  }
-}
-
-// ---------------------------------------------------------------- prefill
-// Lane-parallel INT2 quantizer: the 32 values of a group sit one per lane in
-// a 32-lane half-wave.  Same arithmetic as quant32 (min and max do not depend
-// on the order once a zero is canonicalised to +0).
-
-// ---------------------------------------------------------------- prefill
 // Range of 32 values: zero = min, delta = (max - min) / 3, both from the
 // canonicalised (+0) extremes; 1/delta (0 when delta == 0).
 struct Range {
@@ -232,6 +123,189 @@ __device__ __forceinline__ float quad_xor(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xF, 0xF, true));
 }
 
+// ---------------------------------------------------------------- append
+struct CacheArgs {
+  uint8_t* pool;
+  uint16_t* pool_norm;
+  uint16_t* res_k;
+  uint16_t* res_v;
+  uint16_t* res_norm;
+  const int32_t* block_table;
+  int32_t* seq_state;
+  int32_t* error_flag;
+  int hkv;
+  int max_blocks;
+  int nphys;
+};
+
+// {n, Q} as the kernels leave it: 0 <= Q, Q % 32 == 0, 0 <= n - Q <= 128,
+// Q / 32 <= max_blocks.
+__device__ __forceinline__ bool state_ok(int n, int Q, int max_blocks) {
+  return Q >= 0 && (Q & 31) == 0 && n >= Q && n - Q <= kR && Q / kG <= max_blocks;
+}
+
+// grid B, 1024 threads (wave h < Hkv rotates head h; all of them share a flush).
+__global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16_t* __restrict__ k_new,
+                                                      const uint16_t* __restrict__ v_new,
+                                                      int is_bf16) {
+  // block flush: Key and Value ranges ((1/delta), zero|max) of the block
+  __shared__ float fl_krd[16 * kD];
+  __shared__ uint32_t fl_kzm[16 * kD];
+  __shared__ float fl_vrd[32 * 16 * 4];
+  __shared__ uint32_t fl_vzm[32 * 16 * 4];
+  __shared__ float part[16];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int hkv = ca.hkv;
+  // the new token's inputs do not depend on the state: load them first
+  const int h = tid >> 6, lane = tid & 63;
+  uint16_t kin[2] = {0, 0}, vin[2] = {0, 0};
+  if (h < hkv) {
+    const size_t base = (static_cast<size_t>(b) * hkv + h) * kD;
+    kin[0] = k_new[base + lane];
+    kin[1] = k_new[base + lane + 64];
+    vin[0] = v_new[base + lane];
+    vin[1] = v_new[base + lane + 64];
+  }
+  int32_t* st = ca.seq_state + 2 * b;
+  const int n = st[0];
+  int Q = st[1];
+  if (!state_ok(n, Q, ca.max_blocks)) {
+    if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
+    return;
+  }
+
+  if (n - Q == kR) {
+    // The window is full: its 32 oldest tokens become block Q/32.
+    const int j = Q / kG;
+    if (j >= ca.max_blocks) {
+      if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_CAPACITY));
+      return;
+    }
+    const int p = ca.block_table[static_cast<size_t>(b) * ca.max_blocks + j];
+    if (p < 0 || p >= ca.nphys) {
+      if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
+      return;
+    }
+    const int s0 = Q % kR;
+    if (tid < 32) ca.pool_norm[static_cast<size_t>(p) * 32 + tid] = ca.res_norm[b * kR + s0 + tid];
+    const size_t bh0 = static_cast<size_t>(b) * hkv;
+    auto rec_of = [&](int h) { return ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec; };
+    // ranges: Key (head, channel) over the 32 ring tokens, Value (token,
+    // head, group) over 32 channels
+    const int nku = hkv * kD, nvu = 32 * hkv * 4;
+    for (int u = tid; u < nku + nvu; u += blockDim.x) {
+      float x[32];
+      if (u < nku) {
+        const int h = u >> 7, c = u & 127;
+        const uint16_t* rk = ca.res_k + ((bh0 + h) * kR + s0) * kD + c;
+#pragma unroll
+        for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(rk[t * kD]);
+        const Range r = range32(x);
+        fl_krd[u] = r.rdelta;
+        fl_kzm[u] = r.zm;
+        uint8_t* rec = rec_of(h);
+        reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(r.delta);
+        reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = static_cast<uint16_t>(r.zm);
+      } else {
+        // slot fastest across lanes: the window's Values are channel-major
+        const int w = u - nku, t = w & 31, h = (w >> 5) / 4, g = (w >> 5) & 3;
+        const uint16_t* rv = ca.res_v + ((bh0 + h) * kD + 32 * g) * kR + s0 + t;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = f16_to_f32(rv[static_cast<size_t>(i) * kR]);
+        const Range r = range32(x);
+        const int pi = (t * hkv + h) * 4 + g;
+        fl_vrd[pi] = r.rdelta;
+        fl_vzm[pi] = r.zm;
+        reinterpret_cast<uint32_t*>(rec_of(h) + kRecVParam)[32 * g + t] =
+            static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
+      }
+    }
+    __syncthreads();
+    // code words: Key unit (head, token, half), Value unit (head, octet,
+    // group, quarter), as in the bulk prefill
+    const int nkw = hkv * 64, nvw = hkv * 64;
+    for (int u = tid; u < nkw + nvw; u += blockDim.x) {
+      if (u < nkw) {
+        const int h = u / 64, t = (u >> 1) & 31, half = u & 1;
+        const uint4* kr = reinterpret_cast<const uint4*>(ca.res_k + ((bh0 + h) * kR + s0 + t) * kD + 64 * half);
+        uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint4 w8 = kr[q];
+          const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = 8 * q + e, c = 64 * half + i;
+            const uint16_t xh = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
+            const uint32_t code = code_zm(f16_to_f32(xh), fl_kzm[h * kD + c], fl_krd[h * kD + c]);
+            words[i >> 4] |= code << (2 * (i & 3) + 8 * ((i >> 2) & 3));
+          }
+        }
+        *reinterpret_cast<uint4*>(rec_of(h) + kRecKCodes + 32 * t + 16 * half) =
+            uint4{words[0], words[1], words[2], words[3]};
+      } else {
+        const int w = u - nkw, h = w / 64, oct = (w >> 4) & 3, d = (w >> 2) & 3, qt = w & 3;
+        uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = 32 * d + 16 * e + 4 * qt + i;
+            const uint4 w8 = *reinterpret_cast<const uint4*>(ca.res_v + ((bh0 + h) * kD + c) * kR + s0 + 8 * oct);
+            const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+              const int t = 8 * oct + kk, pi = (t * hkv + h) * 4 + d;
+              const int sk = (kk & 4) | ((kk & 1) << 1) | ((kk >> 1) & 1);
+              const uint16_t xh = static_cast<uint16_t>(ww[kk >> 1] >> (16 * (kk & 1)));
+              words[i] |= code_zm(f16_to_f32(xh), fl_vzm[pi], fl_vrd[pi]) << (2 * (8 * e + sk));
+            }
+          }
+        }
+        uint8_t* rec = rec_of(h) + kRecVCodes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<uint32_t*>(rec + 16 * (16 * oct + 4 * qt + i) + 4 * d) = words[i];
+      }
+    }
+    Q += kG;
+  }
+
+  // Rotate + scale the new token; store it in slot n % 128.
+  const int slot = n % kR;
+  float a = 0.0f, bb = 0.0f;
+  if (h < hkv) {
+    a = in_to_f32(kin[0], is_bf16);
+    bb = in_to_f32(kin[1], is_bf16);
+    fht128_wave(a, bb);
+    const float hs = wave_tree_sumsq(a, bb);
+    if (lane == 0) part[h] = hs;
+  }
+  __syncthreads();
+  if (h < hkv) {
+    float nrm, r;
+    scale_from_ss(tree16(part, hkv), nrm, r);
+    const size_t bh = static_cast<size_t>(b) * hkv + h;
+    uint16_t* rk = ca.res_k + (bh * kR + slot) * kD;
+    rk[lane] = f32_to_f16(mul_rn(a, r));
+    rk[lane + 64] = f32_to_f16(mul_rn(bb, r));
+    uint16_t* rv = ca.res_v + bh * kD * kR + slot;
+    rv[static_cast<size_t>(lane) * kR] = f32_to_f16(in_to_f32(vin[0], is_bf16));
+    rv[static_cast<size_t>(lane + 64) * kR] = f32_to_f16(in_to_f32(vin[1], is_bf16));
+    if (h == 0 && lane == 0) ca.res_norm[b * kR + slot] = f32_to_f16(nrm);
+  }
+  if (tid == 0) {
+    st[0] = n + 1;
+    st[1] = Q;
+  }
+}
+
+// ---------------------------------------------------------------- prefill
+// Lane-parallel INT2 quantizer: the 32 values of a group sit one per lane in
+// a 32-lane half-wave.  Same arithmetic as quant32 (min and max do not depend
+// on the order once a zero is canonicalised to +0).
+
+// ---------------------------------------------------------------- prefill
 // grid nb + nr, 1024 threads: workgroup j < nb turns tokens 32j..32j+31 (all
 // KV heads) into block j; workgroup nb + c writes window chunk c (tokens
 // Q + 32c ..) without quantizing.
@@ -414,9 +488,18 @@ __global__ __launch_bounds__(1024) void prefill_kernel(CacheArgs ca, int seq,
       reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = static_cast<uint16_t>(r.zm);
     } else {
       const int w = u - nku, t = w / (hkv * 4), h = (w >> 2) % hkv, g = w & 3;
-      const uint16_t* src = v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * g;
+      // 64 contiguous bytes per unit: four 16-byte loads
+      const uint4* src = reinterpret_cast<const uint4*>(v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * g);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) x[i] = f16_to_f32(f32_to_f16(in_to_f32(src[i], is_bf16)));
+      for (int q = 0; q < 4; ++q) {
+        const uint4 w8 = src[q];
+        const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t xh = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
+          x[8 * q + e] = f16_to_f32(f32_to_f16(in_to_f32(xh, is_bf16)));
+        }
+      }
       const Range r = range32(x);
       v_rd[w] = r.rdelta;
       v_zm[w] = r.zm;
@@ -530,8 +613,7 @@ extern "C" oscar_status oscar_append_kv(const oscar_cache_geom* geom, const osca
   if (dtype != OSCAR_FP16 && dtype != OSCAR_BF16) return OSCAR_EINVAL;
   st = check_device();
   if (st != OSCAR_OK) return st;
-  const int threads = ((64 * geom->num_kv_heads + 255) / 256) * 256;
-  hipLaunchKernelGGL(append_kernel, dim3(geom->batch), dim3(threads), 0, as_stream(stream),
+  hipLaunchKernelGGL(append_kernel, dim3(geom->batch), dim3(1024), 0, as_stream(stream),
                      make_args(geom, cache), static_cast<const uint16_t*>(k_new),
                      static_cast<const uint16_t*>(v_new), dtype == OSCAR_BF16 ? 1 : 0);
   return launch_status();
