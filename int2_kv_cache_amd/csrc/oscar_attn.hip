@@ -440,6 +440,7 @@ __device__ __forceinline__ void dma_unit(__amdgpu_buffer_rsrc_t rec, __amdgpu_bu
 // copy of the next block (4 instructions) may still run, every older one
 // (the block about to be read) has landed in LDS.
 __device__ __forceinline__ void vmcnt_le4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+__device__ __forceinline__ void vmcnt_0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // The lane's operands of one block, from a stage.
 template <class T>
@@ -635,15 +636,12 @@ void attn_mfma_kernel(AttnArgs A) {
   uint8_t* st0 = stage0[wave];
   uint8_t* st1 = stage1[wave];
   auto dma_block = [&](int j, uint8_t* st) {
-    const int jc = j < cnt ? j : cnt - 1;
-    if (j < cnt && j > 0 && (j & 63) == 0) idv = load_ids(j);
-    const int p = __builtin_amdgcn_readlane(idv, jc & 63);
+    if (j > 0 && (j & 63) == 0) idv = load_ids(j);
+    const int p = __builtin_amdgcn_readlane(idv, j & 63);
     dma_unit(unit_rec(p), unit_nrm(p), st, L);
   };
-  if (cnt > 0) {
-    dma_block(0, st0);
-    dma_block(1, st1);
-  }
+  if (cnt > 0) dma_block(0, st0);
+  if (cnt > 1) dma_block(1, st1);
 
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
@@ -862,11 +860,18 @@ void attn_mfma_kernel(AttnArgs A) {
     process_int2(
         ru,
         [&]() {
-          lds_wait();  // block k's stage has been read completely
-          dma_block(k + 2, stc);
+          if (k + 2 < cnt) {
+            lds_wait();  // block k's stage has been read completely
+            dma_block(k + 2, stc);
+          }
         },
         [&]() {
-          vmcnt_le4();  // block k + 1's copy has landed (k + 2's may still run)
+          // block k + 1's copy has landed (k + 2's may still run); past the
+          // last block nothing is read that is used
+          if (k + 2 < cnt)
+            vmcnt_le4();
+          else
+            vmcnt_0();
           read_kpart<GRP, NR, TPL, CPL>(ru, off, stn, L);
         });
     read_vpart<GRP, NR, TPL, CPL>(ru, off, stn, L);
@@ -964,21 +969,31 @@ void attn_mfma_kernel(AttnArgs A) {
 
   // ---------------- merge the 4 waves into this split's partial
   const size_t pbase = (static_cast<size_t>(b) * A.hq + h * GRP) * A.splits;
-  for (int idx = tid; idx < GRP * kD; idx += 256) {
-    const int hh = idx >> 7, c = idx & 127;
-    float M = -INFINITY;
+  // every operand is read before any is combined (no branch between the
+  // LDS reads); a wave with no tokens has m = -inf and weight 0
+  constexpr int NI = (GRP * kD + 255) / 256;
+  float mw[NI][4], lw[NI][4], ow[NI][4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, lds_ml[0][w][hh]);
+  for (int i = 0; i < NI; ++i) {
+    const int idx = tid + 256 * i, hh = (idx >> 7) % GRP, c = idx & 127;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[i][w] = lds_ml[0][w][hh];
+      lw[i][w] = lds_ml[1][w][hh];
+      ow[i][w] = wo_at(w, hh)[c];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = tid + 256 * i, hh = idx >> 7, c = idx & 127;
+    if (idx >= GRP * kD) break;
+    const float M = fmaxf(fmaxf(mw[i][0], mw[i][1]), fmaxf(mw[i][2], mw[i][3]));
     float Lw = 0.0f, Ow = 0.0f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = lds_ml[0][w][hh];
-        if (mw == -INFINITY) continue;
-        const float sc = exp2f(mw - M);
-        Lw += sc * lds_ml[1][w][hh];
-        Ow += sc * wo_at(w, hh)[c];
-      }
+    for (int w = 0; w < 4; ++w) {
+      const float sc = mw[i][w] == -INFINITY ? 0.0f : exp2f(mw[i][w] - M);
+      Lw += sc * lw[i][w];
+      Ow += sc * ow[i][w];
     }
     const size_t part = pbase + static_cast<size_t>(hh) * A.splits + s;
     A.ws_o[part * kD + c] = Ow;

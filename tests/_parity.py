@@ -99,12 +99,15 @@ class Pair:
                 assert_same_bits(rn[b][slots], o.res_norm[b][slots], "res_norm seq %d" % b)
 
     def attend(self, q: np.ndarray, variant=ok.ATTN_AUTO, splits=0, max_ctx=None,
-               q_dtype=None):
-        """GPU decode attention -> (out, lse) numpy."""
+               q_dtype=None, ws=None):
+        """GPU decode attention -> (out, lse) numpy.  `ws`: a workspace to
+        reuse, else a fresh one."""
         cfg = self.wl.cfg
         mctx = max_ctx or (max(o for o in [self.orc.n(b) for b in range(cfg.batch)]) + 1)
         S, nbytes = ok.decode_workspace_bytes(self.geom, mctx, splits)
-        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        if ws is None:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        assert ws.numel() >= nbytes
         out = torch.empty(cfg.batch, cfg.hq, 128, dtype=torch.float32, device="cuda")
         lse = torch.empty(cfg.batch, cfg.hq, dtype=torch.float32, device="cuda")
         if q_dtype == ok.FP32:

@@ -213,6 +213,25 @@ def test_attention_prerotated_query():
     assert np.abs(got - want).max() <= ATOL
 
 
+def test_attention_workspace_reuse():
+    """One workspace serves calls with different split counts and kernels:
+    no call depends on what an earlier one left in it."""
+    wl = synth.workload(3, batch=3, ctx=None)
+    wl.ctx_lens = [3000, 700, 129]
+    pr = Pair(wl)
+    for b in range(3):
+        k, v = wl.prefill(b)
+        pr.prefill(b, k, v)
+    kn, vn, q = next(wl.steps(1))
+    pr.append(kn, vn)
+    want, _ = pr.orc.decode_attn(oracle.rotate_query(q, wl.cfg.dtype))
+    _, nbytes = ok.decode_workspace_bytes(pr.geom, 3001, 64)
+    ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device="cuda")
+    for S, var in [(64, 2), (5, 2), (1, 1), (0, 2), (64, 1), (3, 2)]:
+        got, _ = pr.attend(q, variant=var, splits=S, max_ctx=3001, ws=ws)
+        assert np.abs(got - want).max() <= ATOL, (S, var)
+
+
 def test_abi_rejects_bad_arguments():
     g = ok.make_geom(1, 4, 1, 4, 4, head_dim=64)
     with pytest.raises(ok.OscarError) as e:
