@@ -116,6 +116,37 @@ __device__ __forceinline__ uint32_t code_zm(float x, uint32_t zm, float rdelta) 
   return r < 0.0f ? 0u : (r > 3.0f ? 3u : static_cast<uint32_t>(r));
 }
 
+// The 32 codes of a range's own values, packed two bits each: channel or
+// token i at bits 2 (i & 15) of w[i >> 4].  q1 = (x - zero) * (1/delta) is
+// within 2^-20 of the correctly rounded quotient (which lies in [0, 3]), so
+// rint(q1) is the code unless q1 lies within 2^-18 of a half integer; if any
+// of the 32 does, all 32 are recomputed with the exact quotient.  Codes
+// accumulate eight at a time as sum c * 4^k in fp32 (exact: below 2^16).
+__device__ __forceinline__ void codes32(const float* x, const Range& r, uint32_t w[2]) {
+#pragma clang fp contract(off)
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float far = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float q1 = (x[i] - r.zero) * r.rdelta;
+    const float c = rintf(q1);
+    far = fmaxf(far, fabsf(q1 - c));
+    acc[i >> 3] = __builtin_fmaf(c, static_cast<float>(1u << (2 * (i & 7))), acc[i >> 3]);
+  }
+  if (far >= 0.5f - 0x1p-18f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float q = rintf(__fdiv_rn(x[i] - r.zero, r.delta));
+      const float c = r.delta > 0.0f ? fminf(fmaxf(q, 0.0f), 3.0f) : 0.0f;
+      acc[i >> 3] = __builtin_fmaf(c, static_cast<float>(1u << (2 * (i & 7))), acc[i >> 3]);
+    }
+  }
+  w[0] = static_cast<uint32_t>(acc[0]) | (static_cast<uint32_t>(acc[1]) << 16);
+  w[1] = static_cast<uint32_t>(acc[2]) | (static_cast<uint32_t>(acc[3]) << 16);
+}
+
 // Quad cross-lane read (lanes 4m..4m+3 exchange): xor 1 or xor 2.
 template <int X>
 __device__ __forceinline__ float quad_xor(float x) {
@@ -315,31 +346,37 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
 // strides 32 and 64 exchange within the lane quad -- the oracle's stages in
 // the oracle's order.  The sum of squares follows the same tree (strides
 // 1..16 in registers, 32 and 64 across the quad, then over the heads).
-// Quantization without atomics: every Key range (head, channel) and Value
-// range (token, head, group) is computed once and kept in LDS, then each
-// thread assembles whole code words (Key: 4 words of one token row; Value:
-// 4 words of one token octet) and stores them.
-// Dynamic LDS: k_hat [32][Hkv][128] fp16, then the ranges region (Key
-// [Hkv][128] and Value [32][Hkv][4] x (1/delta, zero|max)); the rotation
-// phase borrows the ranges region for the per-head sums and per-token
-// factors.
-constexpr int kPrefillThreads = 1024;
+// Quantization without atomics: the thread that takes a range (Key: head,
+// channel over the 32 tokens; Value: token, head, 32-channel group) holds its
+// 32 values and computes their codes at once, into an LDS image of 32-bit
+// words of 16 codes; whole code words of the record are then assembled from
+// that image (Key: one word = 16 channels of one token; Value: one word = 8
+// tokens x 2 channels).
+// Dynamic LDS: k_hat [32][Hkv][128] fp16 (the Value image reuses it once the
+// Key ranges are done), then the Key image [Hkv][2][128] words (the rotation
+// phase borrows it for the per-head sums and per-token factors).
 size_t prefill_lds_bytes(int hkv) {
-  return static_cast<size_t>(hkv) * (32 * kD * 2 + 2 * 1024);
+  return static_cast<size_t>(hkv) * (32 * kD * 2 + 2 * kD * 4);
 }
+// Value image: [Hkv][4 groups] rows of 32 tokens x 2 words, padded to 80
+// words so that the four groups a wave reads fall in different banks.
+constexpr int kVImgRow = 80;
 
-__global__ __launch_bounds__(1024) void prefill_kernel(CacheArgs ca, int seq,
+// NT threads: 512 for Hkv <= 8 (two workgroups share a CU, so that one's
+// loads overlap the other's arithmetic), 1024 above.  Four waves per SIMD
+// either way (at most 128 registers).
+template <int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void prefill_kernel(CacheArgs ca, int seq,
                                                        const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v,
                                                        int n_tokens, int Qn, int is_bf16) {
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int hkv = ca.hkv;
   uint16_t* khs = reinterpret_cast<uint16_t*>(dyn);                      // [32][hkv][128]
-  uint8_t* prm = dyn + static_cast<size_t>(32) * hkv * kD * 2;           // ranges region
-  float* k_rd = reinterpret_cast<float*>(prm);                          // [hkv*128]
-  uint32_t* k_zm = reinterpret_cast<uint32_t*>(k_rd + hkv * kD);         // [hkv*128]
-  float* v_rd = reinterpret_cast<float*>(k_zm + hkv * kD);               // [32*hkv*4]
-  uint32_t* v_zm = reinterpret_cast<uint32_t*>(v_rd + 32 * hkv * 4);     // [32*hkv*4]
+  uint32_t* img_v = reinterpret_cast<uint32_t*>(dyn);                    // [hkv][4][kVImgRow]
+  uint8_t* prm = dyn + static_cast<size_t>(32) * hkv * kD * 2;
+  uint32_t* img_k = reinterpret_cast<uint32_t*>(prm);                    // [hkv][2][128]
   float* part = reinterpret_cast<float*>(prm);                          // rotation phase: [32][hkv]
   float* tok_r = part + 32 * hkv;                                        // [32]
 
@@ -365,9 +402,9 @@ __global__ __launch_bounds__(1024) void prefill_kernel(CacheArgs ca, int seq,
   float y[2][32];
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
-    const int task = rr * kPrefillThreads + tid;
+    const int task = rr * NT + tid;
     const int vtx = task >> 2, tq = task & 3;
-    if (rr * kPrefillThreads >= nvec * 4) break;  // uniform
+    if (rr * NT >= nvec * 4) break;  // uniform
     const int t = vtx / hkv, h = vtx % hkv;
     const bool valid = vtx < nvec && t0 + t < n_tokens;
     float* x = y[rr];
@@ -398,17 +435,14 @@ __global__ __launch_bounds__(1024) void prefill_kernel(CacheArgs ca, int seq,
             x[j] = a + b;
             x[j + hs] = a - b;
           }
-      // strides 32 and 64: the partner is lane tq ^ 1, then tq ^ 2
+      // strides 32 and 64: the partner is lane tq ^ 1, then tq ^ 2; the
+      // upper lane of a pair takes partner - own, as one exactly rounded
+      // fma with -1
+      const float sg1 = (tq & 1) ? -1.0f : 1.0f, sg2 = (tq & 2) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const float pj = quad_xor<1>(x[j]);
-        x[j] = (tq & 1) ? (pj - x[j]) : (x[j] + pj);
-      }
+      for (int j = 0; j < 32; ++j) x[j] = __builtin_fmaf(sg1, x[j], quad_xor<1>(x[j]));
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const float pj = quad_xor<2>(x[j]);
-        x[j] = (tq & 2) ? (pj - x[j]) : (x[j] + pj);
-      }
+      for (int j = 0; j < 32; ++j) x[j] = __builtin_fmaf(sg2, x[j], quad_xor<2>(x[j]));
 #pragma unroll
       for (int j = 0; j < 32; ++j) x[j] = x[j] * kFhtScale;
       float sq[32];
@@ -441,9 +475,9 @@ __global__ __launch_bounds__(1024) void prefill_kernel(CacheArgs ca, int seq,
   // ---- scaled Keys (and, for a window chunk, fp16 Values) to LDS or the ring
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
-    const int task = rr * kPrefillThreads + tid;
+    const int task = rr * NT + tid;
     const int vtx = task >> 2, tq = task & 3;
-    if (rr * kPrefillThreads >= nvec * 4) break;
+    if (rr * NT >= nvec * 4) break;
     const int t = vtx / hkv, h = vtx % hkv;
     if (vtx < nvec && t0 + t < n_tokens) {
       const float r = tok_r[t];
@@ -472,87 +506,100 @@ __global__ __launch_bounds__(1024) void prefill_kernel(CacheArgs ca, int seq,
   if (ring) return;
   __syncthreads();
 
-  // ---- ranges: Key (head, channel) over 32 tokens; Value (token, head, group)
-  const int nku = hkv * kD, nvu = 32 * hkv * 4;
-  for (int u = tid; u < nku + nvu; u += kPrefillThreads) {
-    float x[32];
-    if (u < nku) {
-      const int h = u >> 7, c = u & 127;
+  // The Value inputs of this thread's Value units (at most two: 32 Hkv 4
+  // units over NT threads) are requested now and land during the Key phase.
+  uint4 vraw[2][4];
 #pragma unroll
-      for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(khs[(t * hkv + h) * kD + c]);
-      const Range r = range32(x);
-      k_rd[u] = r.rdelta;
-      k_zm[u] = r.zm;
-      uint8_t* rec = rec_of(h);
-      reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(r.delta);
-      reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = static_cast<uint16_t>(r.zm);
-    } else {
-      const int w = u - nku, t = w / (hkv * 4), h = (w >> 2) % hkv, g = w & 3;
-      // 64 contiguous bytes per unit: four 16-byte loads
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + NT * i;
+    if (u < 32 * hkv * 4) {
+      const int t = u / (hkv * 4), h = (u >> 2) % hkv, g = u & 3;
       const uint4* src = reinterpret_cast<const uint4*>(v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * g);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 w8 = src[q];
-        const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint16_t xh = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
-          x[8 * q + e] = f16_to_f32(f32_to_f16(in_to_f32(xh, is_bf16)));
-        }
-      }
-      const Range r = range32(x);
-      v_rd[w] = r.rdelta;
-      v_zm[w] = r.zm;
-      reinterpret_cast<uint32_t*>(rec_of(h) + kRecVParam)[32 * g + t] =
-          static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
+      for (int q = 0; q < 4; ++q) vraw[i][q] = src[q];
     }
+  }
+
+  // ---- Key ranges and codes: unit (head, channel) over the 32 tokens
+  for (int u = tid; u < hkv * kD; u += NT) {
+    const int h = u >> 7, c = u & 127;
+    float x[32];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(khs[(t * hkv + h) * kD + c]);
+    const Range r = range32(x);
+    uint8_t* rec = rec_of(h);
+    reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(r.delta);
+    reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = static_cast<uint16_t>(r.zm);
+    uint32_t w[2];
+    codes32(x, r, w);
+    img_k[(2 * h) * kD + c] = w[0];      // tokens 0..15
+    img_k[(2 * h + 1) * kD + c] = w[1];  // tokens 16..31
+  }
+  __syncthreads();  // k_hat is dead: its space takes the Value image
+
+  // ---- Value ranges and codes: unit (token, head, group) over 32 channels
+  static_assert(32 * 16 * 4 <= 2 * 1024 && 32 * 8 * 4 <= 2 * 512, "two Value units per thread");
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + NT * i;
+    if (u >= 32 * hkv * 4) break;
+    const int t = u / (hkv * 4), h = (u >> 2) % hkv, g = u & 3;
+    float x[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w8 = vraw[i][q];
+      const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t xh = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
+        x[8 * q + e] = f16_to_f32(f32_to_f16(in_to_f32(xh, is_bf16)));
+      }
+    }
+    const Range r = range32(x);
+    reinterpret_cast<uint32_t*>(rec_of(h) + kRecVParam)[32 * g + t] =
+        static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
+    uint32_t w[2];
+    codes32(x, r, w);
+    *reinterpret_cast<uint2*>(img_v + (h * 4 + g) * kVImgRow + 2 * t) = uint2{w[0], w[1]};
   }
   __syncthreads();
 
-  // ---- code words.  Key unit (head, token, half): channels 64 half .. +63,
-  // words 4 half .. 4 half + 3 of the token row.  Value unit (head, octet,
-  // group, quarter): slices 16 octet + 4 quarter .. +3, word `group`.
-  const int nkw = hkv * 32 * 2, nvw = hkv * 4 * 4 * 4;
-  for (int u = tid; u < nkw + nvw; u += kPrefillThreads) {
+  // ---- code words.  Key word (head, token, j): channels 16 j .. 16 j + 15
+  // of the token row.  Value word (head, octet, group d, quarter, i): tokens
+  // 8 octet .. + 7 at channels 32 d + 16 e + 4 quarter + i, e = 0, 1.
+  const int nkw = hkv * 32 * 8;
+  for (int u = tid; u < 2 * nkw; u += NT) {
     if (u < nkw) {
-      const int h = u / 64, t = (u >> 1) & 31, half = u & 1;
-      const uint16_t* kr = khs + (t * hkv + h) * kD + 64 * half;
-      uint32_t words[4] = {0u, 0u, 0u, 0u};
+      const int h = u >> 8, t = (u >> 3) & 31, j = u & 7;
+      const uint4* src = reinterpret_cast<const uint4*>(img_k + (2 * h + (t >> 4)) * kD + 16 * j);
+      const int sh = 2 * (t & 15);
+      uint32_t word = 0u;
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const int c = 64 * half + i;
-        const uint32_t code = code_zm(f16_to_f32(kr[i]), k_zm[h * kD + c], k_rd[h * kD + c]);
-        words[i >> 4] |= code << (2 * (i & 3) + 8 * ((i >> 2) & 3));
+      for (int q = 0; q < 4; ++q) {
+        const uint4 w4 = src[q];
+        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) word |= ((ww[e] >> sh) & 3u) << (2 * e + 8 * q);
       }
-      *reinterpret_cast<uint4*>(rec_of(h) + kRecKCodes + 32 * t + 16 * half) =
-          uint4{words[0], words[1], words[2], words[3]};
+      *reinterpret_cast<uint32_t*>(rec_of(h) + kRecKCodes + 32 * t + 4 * j) = word;
     } else {
-      const int w = u - nkw, h = w / 64, oct = (w >> 4) & 3, d = (w >> 2) & 3, qt = w & 3;
-      uint32_t words[4] = {0u, 0u, 0u, 0u};
+      const int w = u - nkw, h = w >> 8, oct = (w >> 6) & 3, qt = (w >> 4) & 3, i = (w >> 2) & 3,
+                d = w & 3;
+      const uint4* src = reinterpret_cast<const uint4*>(img_v + (h * 4 + d) * kVImgRow + 16 * oct);
+      const int m = 4 * qt + i;
+      uint32_t word = 0u;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int t = 8 * oct + kk;
-        const int pi = (t * hkv + h) * 4 + d;
-        const uint32_t zm = v_zm[pi];
-        const float rd = v_rd[pi];
-        const int sk = (kk & 4) | ((kk & 1) << 1) | ((kk >> 1) & 1);
+      for (int q = 0; q < 4; ++q) {
+        const uint4 w4 = src[q];  // tokens 8 oct + 2q, + 2q + 1; words e = 0, 1
+        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint16_t* src = v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * d + 16 * e + 4 * qt;
-          const uint2 raw = *reinterpret_cast<const uint2*>(src);
-          const uint16_t vv[4] = {static_cast<uint16_t>(raw.x), static_cast<uint16_t>(raw.x >> 16),
-                                  static_cast<uint16_t>(raw.y), static_cast<uint16_t>(raw.y >> 16)};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = f16_to_f32(f32_to_f16(in_to_f32(vv[i], is_bf16)));
-            words[i] |= code_zm(x, zm, rd) << (2 * (8 * e + sk));
-          }
+        for (int f = 0; f < 4; ++f) {
+          const int kk = 2 * q + (f >> 1), e = f & 1;
+          const int sk = (kk & 4) | ((kk & 1) << 1) | ((kk >> 1) & 1);
+          word |= ((ww[f] >> (2 * m)) & 3u) << (2 * (8 * e + sk));
         }
       }
-      uint8_t* rec = rec_of(h) + kRecVCodes;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint32_t*>(rec + 16 * (16 * oct + 4 * qt + i) + 4 * d) = words[i];
+      *reinterpret_cast<uint32_t*>(rec_of(h) + kRecVCodes + 16 * (16 * oct + m) + 4 * d) = word;
     }
   }
 }
@@ -637,13 +684,19 @@ extern "C" oscar_status oscar_prefill_quantize(const oscar_cache_geom* geom,
   const int Q = 32 * Qb;
   const int nr = (n_tokens - Q + 31) / 32;
   const size_t lds = prefill_lds_bytes(geom->num_kv_heads);
-  if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  hipLaunchKernelGGL(prefill_kernel, dim3(Qb + nr), dim3(kPrefillThreads), lds, as_stream(stream),
-                     make_args(geom, cache), static_cast<int>(seq),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                     static_cast<int>(n_tokens), Q, dtype == OSCAR_BF16 ? 1 : 0);
+  auto launch = [&](auto kernel, int nt) {
+    if (lds > 64 * 1024)
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    hipLaunchKernelGGL(kernel, dim3(Qb + nr), dim3(nt), lds, as_stream(stream),
+                       make_args(geom, cache), static_cast<int>(seq),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                       static_cast<int>(n_tokens), Q, dtype == OSCAR_BF16 ? 1 : 0);
+  };
+  if (geom->num_kv_heads <= 8)
+    launch(&prefill_kernel<512>, 512);
+  else
+    launch(&prefill_kernel<1024>, 1024);
   st = launch_status();
   if (st != OSCAR_OK) return st;
   hipLaunchKernelGGL(prefill_finish_kernel, dim3(1), dim3(64), 0, as_stream(stream),
