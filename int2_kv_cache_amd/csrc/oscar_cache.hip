@@ -365,12 +365,12 @@ constexpr int kVImgRow = 80;
 // NT threads: 512 for Hkv <= 8 (two workgroups share a CU, so that one's
 // loads overlap the other's arithmetic), 1024 above.  Four waves per SIMD
 // either way (at most 128 registers).
-template <int NT>
+// BF16: the input type (bf16 or fp16) as a compile-time choice.
+template <int NT, int BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void prefill_kernel(CacheArgs ca, int seq,
-                                                       const uint16_t* __restrict__ k,
-                                                       const uint16_t* __restrict__ v,
-                                                       int n_tokens, int Qn, int is_bf16) {
+void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
+                    const uint16_t* __restrict__ v, int n_tokens, int Qn) {
+  constexpr int is_bf16 = BF16;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int hkv = ca.hkv;
   uint16_t* khs = reinterpret_cast<uint16_t*>(dyn);                      // [32][hkv][128]
@@ -691,12 +691,13 @@ extern "C" oscar_status oscar_prefill_quantize(const oscar_cache_geom* geom,
     hipLaunchKernelGGL(kernel, dim3(Qb + nr), dim3(nt), lds, as_stream(stream),
                        make_args(geom, cache), static_cast<int>(seq),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<int>(n_tokens), Q, dtype == OSCAR_BF16 ? 1 : 0);
+                       static_cast<int>(n_tokens), Q);
   };
+  const bool bf16 = dtype == OSCAR_BF16;
   if (geom->num_kv_heads <= 8)
-    launch(&prefill_kernel<512>, 512);
+    bf16 ? launch(&prefill_kernel<512, 1>, 512) : launch(&prefill_kernel<512, 0>, 512);
   else
-    launch(&prefill_kernel<1024>, 1024);
+    bf16 ? launch(&prefill_kernel<1024, 1>, 1024) : launch(&prefill_kernel<1024, 0>, 1024);
   st = launch_status();
   if (st != OSCAR_OK) return st;
   hipLaunchKernelGGL(prefill_finish_kernel, dim3(1), dim3(64), 0, as_stream(stream),
