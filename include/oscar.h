@@ -149,14 +149,16 @@ OSCAR_API oscar_status oscar_rotate_scale(const void *x, oscar_dtype dtype, int3
 
 /* Stateless INT2 quantize + pack of whole 32-token blocks (summary "OScaR：…",
  * 方法步骤详情 ②, the quantization kernel handling Keys and Values together).
- *   khat16, v16  device, [32*n_blocks][n_kv_heads][128] fp16.
+ *   khat16, v16  device, [32*n_blocks][n_kv_heads][128] fp16; v16 16-byte
+ *                aligned.
  *   knorm16      device, [32*n_blocks] fp16 token norms (TOKEN scope).
  *   rec_out      device, [n_blocks][n_kv_heads][3072] records (layout above).
  *   norm_out     device, [n_blocks][32] fp16.
  * Keys: per channel over the block's 32 tokens; Values: per token over each
  * 32-channel group; delta = (max-min)/3, zero = min, code =
  * clamp(rint((x-zero)/delta), 0, 3) in IEEE fp32, delta == 0 -> code 0.
- * Errors: EINVAL. */
+ * Errors: EINVAL (null, counts out of range, rec_out or v16 not 16-byte
+ * aligned). */
 OSCAR_API oscar_status oscar_quant_pack(const void *khat16, const void *knorm16, const void *v16,
                               int32_t n_blocks, int32_t n_kv_heads,
                               oscar_norm_scope norm_scope, void *rec_out,

@@ -11,70 +11,10 @@
 
 namespace oscar {
 
-// Record quantization by one group of 256 threads.  Thread tg < 128 takes
-// Key channel tg (32 tokens); thread tg >= 128 takes Value (token, group)
-// unit tg - 128.  Codes are OR-ed into the LDS image `img` (512 words: Key
-// codes then Value codes), steps and zero points go straight to `rec`.
-template <class KGet, class VGet>
-__device__ __forceinline__ void quant_record_units(int tg, KGet kget, VGet vget, uint32_t* img,
-                                                   uint8_t* rec) {
-  float x[32];
-  float d, z;
-  if (tg < 128) {
-    const int c = tg;
-#pragma unroll
-    for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(kget(t, c));
-    const uint64_t codes = quant32(x, d, z);
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const int bit = kcode_bitpos(t, c);
-      atomicOr(&img[bit >> 5], static_cast<uint32_t>((codes >> (2 * t)) & 3u) << (bit & 31));
-    }
-    reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(d);
-    reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = f32_to_f16(z);
-  } else {
-    const int u = tg - 128, t = u >> 2, g = u & 3;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = f16_to_f32(vget(t, 32 * g + i));
-    const uint64_t codes = quant32(x, d, z);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int bit = vcode_bitpos(t, 32 * g + i);
-      atomicOr(&img[256 + (bit >> 5)], static_cast<uint32_t>((codes >> (2 * i)) & 3u) << (bit & 31));
-    }
-    reinterpret_cast<uint32_t*>(rec + kRecVParam)[32 * g + t] =
-        static_cast<uint32_t>(f32_to_f16(d)) | (static_cast<uint32_t>(f32_to_f16(z)) << 16);
-  }
-}
-
-__device__ __forceinline__ void copy_codes_out(int tg, const uint32_t* img, uint8_t* rec) {
-  if (tg < 128)
-    reinterpret_cast<uint4*>(rec)[tg] = reinterpret_cast<const uint4*>(img)[tg];
-}
-
-// ---------------------------------------------------------------- quant_pack
-// grid (n_blocks, Hkv), 256 threads.
-__global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restrict__ khat,
-                                                         const uint16_t* __restrict__ knorm,
-                                                         const uint16_t* __restrict__ v16,
-                                                         int hkv, uint8_t* __restrict__ rec_out,
-                                                         uint16_t* __restrict__ norm_out) {
-  __shared__ uint32_t img[512];
-  const int j = blockIdx.x, h = blockIdx.y, tg = threadIdx.x;
-  for (int i = tg; i < 512; i += 256) img[i] = 0;
-  __syncthreads();
-  const size_t row = static_cast<size_t>(hkv) * kD;
-  const uint16_t* kb = khat + static_cast<size_t>(32 * j) * row + static_cast<size_t>(h) * kD;
-  const uint16_t* vb = v16 + static_cast<size_t>(32 * j) * row + static_cast<size_t>(h) * kD;
-  uint8_t* rec = rec_out + (static_cast<size_t>(j) * hkv + h) * kRec;
-  quant_record_units(
-      tg, [&](int t, int c) { return kb[t * row + c]; },
-      [&](int t, int c) { return vb[t * row + c]; }, img, rec);
-  __syncthreads();
-  copy_codes_out(tg, img, rec);
-  if (h == 0 && tg < 32) norm_out[static_cast<size_t>(j) * 32 + tg] = knorm[32 * j + tg];
-}
-
+// INT2 min-max quantizer over 32 fp16-valued numbers: delta = (max - min)/3,
+// zero = min, code = clamp(rint((x - zero)/delta), 0, 3) with ties to even,
+// delta == 0 -> code 0 ([SUM] 前置知识 on per-channel quantization and
+// 方法步骤详情 ②; [RN] §I).
 // Range of 32 values: zero = min, delta = (max - min) / 3, both from the
 // canonicalised (+0) extremes; 1/delta (0 when delta == 0).
 struct Range {
@@ -145,6 +85,100 @@ __device__ __forceinline__ void codes32(const float* x, const Range& r, uint32_t
   }
   w[0] = static_cast<uint32_t>(acc[0]) | (static_cast<uint32_t>(acc[1]) << 16);
   w[1] = static_cast<uint32_t>(acc[2]) | (static_cast<uint32_t>(acc[3]) << 16);
+}
+
+// Value image: per (head, group) a row of 32 tokens x 2 words (channels
+// 0..15 and 16..31 of the group), padded to 80 words so that the four groups
+// a wave reads fall in different banks.
+constexpr int kVImgRow = 80;
+
+// Key code word j of token t (channels 16 j .. 16 j + 15) from a head's Key
+// image [2][128] (word s of channel c holds tokens 16 s .. 16 s + 15).
+__device__ __forceinline__ uint32_t key_word(const uint32_t* img, int t, int j) {
+  const uint4* src = reinterpret_cast<const uint4*>(img + (t >> 4) * kD + 16 * j);
+  const int sh = 2 * (t & 15);
+  uint32_t word = 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 w4 = src[q];
+    const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) word |= ((ww[e] >> sh) & 3u) << (2 * e + 8 * q);
+  }
+  return word;
+}
+// Value code word (octet, m, group d): tokens 8 octet .. + 7 at channels
+// 32 d + 16 e + m, e = 0, 1, from a head's Value image [4][kVImgRow].
+__device__ __forceinline__ uint32_t value_word(const uint32_t* img, int oct, int m, int d) {
+  const uint4* src = reinterpret_cast<const uint4*>(img + d * kVImgRow + 16 * oct);
+  uint32_t word = 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 w4 = src[q];  // tokens 8 oct + 2q, + 2q + 1; words e = 0, 1
+    const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int kk = 2 * q + (f >> 1), e = f & 1;
+      const int sk = (kk & 4) | ((kk & 1) << 1) | ((kk >> 1) & 1);
+      word |= ((ww[f] >> (2 * m)) & 3u) << (2 * (8 * e + sk));
+    }
+  }
+  return word;
+}
+
+// ---------------------------------------------------------------- quant_pack
+// grid (n_blocks, Hkv), 256 threads: one (block, KV head) record.  Thread
+// tg < 128 takes Key channel tg over the 32 tokens, thread tg >= 128 the
+// Value (token, group) unit tg - 128; each computes its range and its 32
+// codes into the LDS images, then every thread assembles two code words.
+__global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restrict__ khat,
+                                                         const uint16_t* __restrict__ knorm,
+                                                         const uint16_t* __restrict__ v16,
+                                                         int hkv, uint8_t* __restrict__ rec_out,
+                                                         uint16_t* __restrict__ norm_out) {
+  __shared__ __attribute__((aligned(16))) uint32_t img_k[2 * kD];
+  __shared__ __attribute__((aligned(16))) uint32_t img_v[4 * kVImgRow];
+  const int j = blockIdx.x, h = blockIdx.y, tg = threadIdx.x;
+  const size_t row = static_cast<size_t>(hkv) * kD;
+  uint8_t* rec = rec_out + (static_cast<size_t>(j) * hkv + h) * kRec;
+  float x[32];
+  uint32_t w[2];
+  if (tg < 128) {
+    const uint16_t* kb = khat + static_cast<size_t>(32 * j) * row + static_cast<size_t>(h) * kD + tg;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(kb[t * row]);
+    const Range r = range32(x);
+    reinterpret_cast<uint16_t*>(rec + kRecKDelta)[tg] = f32_to_f16(r.delta);
+    reinterpret_cast<uint16_t*>(rec + kRecKZero)[tg] = static_cast<uint16_t>(r.zm);
+    codes32(x, r, w);
+    img_k[tg] = w[0];
+    img_k[kD + tg] = w[1];
+  } else {
+    const int u = tg - 128, t = u >> 2, g = u & 3;
+    const uint4* src = reinterpret_cast<const uint4*>(v16 + static_cast<size_t>(32 * j + t) * row +
+                                                      static_cast<size_t>(h) * kD + 32 * g);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w8 = src[q];
+      const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * q + e] = f16_to_f32(static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1))));
+    }
+    const Range r = range32(x);
+    reinterpret_cast<uint32_t*>(rec + kRecVParam)[32 * g + t] =
+        static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
+    codes32(x, r, w);
+    *reinterpret_cast<uint2*>(img_v + g * kVImgRow + 2 * t) = uint2{w[0], w[1]};
+  }
+  __syncthreads();
+  {
+    const int t = tg >> 3, jw = tg & 7;  // Key word jw of token t
+    *reinterpret_cast<uint32_t*>(rec + kRecKCodes + 32 * t + 4 * jw) = key_word(img_k, t, jw);
+    const int oct = (tg >> 6) & 3, m = (tg >> 2) & 15, d = tg & 3;
+    *reinterpret_cast<uint32_t*>(rec + kRecVCodes + 16 * (16 * oct + m) + 4 * d) =
+        value_word(img_v, oct, m, d);
+  }
+  if (h == 0 && tg < 32) norm_out[static_cast<size_t>(j) * 32 + tg] = knorm[32 * j + tg];
 }
 
 // Quad cross-lane read (lanes 4m..4m+3 exchange): xor 1 or xor 2.
@@ -332,12 +366,7 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
 }
 
 // ---------------------------------------------------------------- prefill
-// Lane-parallel INT2 quantizer: the 32 values of a group sit one per lane in
-// a 32-lane half-wave.  Same arithmetic as quant32 (min and max do not depend
-// on the order once a zero is canonicalised to +0).
-
-// ---------------------------------------------------------------- prefill
-// grid nb + nr, 1024 threads: workgroup j < nb turns tokens 32j..32j+31 (all
+// grid nb + nr, NT threads: workgroup j < nb turns tokens 32j..32j+31 (all
 // KV heads) into block j; workgroup nb + c writes window chunk c (tokens
 // Q + 32c ..) without quantizing.
 //
@@ -358,9 +387,7 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
 size_t prefill_lds_bytes(int hkv) {
   return static_cast<size_t>(hkv) * (32 * kD * 2 + 2 * kD * 4);
 }
-// Value image: [Hkv][4 groups] rows of 32 tokens x 2 words, padded to 80
-// words so that the four groups a wave reads fall in different banks.
-constexpr int kVImgRow = 80;
+
 
 // NT threads: 512 for Hkv <= 8 (two workgroups share a CU, so that one's
 // loads overlap the other's arithmetic), 1024 above.  Four waves per SIMD
@@ -571,35 +598,12 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
   for (int u = tid; u < 2 * nkw; u += NT) {
     if (u < nkw) {
       const int h = u >> 8, t = (u >> 3) & 31, j = u & 7;
-      const uint4* src = reinterpret_cast<const uint4*>(img_k + (2 * h + (t >> 4)) * kD + 16 * j);
-      const int sh = 2 * (t & 15);
-      uint32_t word = 0u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 w4 = src[q];
-        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) word |= ((ww[e] >> sh) & 3u) << (2 * e + 8 * q);
-      }
-      *reinterpret_cast<uint32_t*>(rec_of(h) + kRecKCodes + 32 * t + 4 * j) = word;
+      *reinterpret_cast<uint32_t*>(rec_of(h) + kRecKCodes + 32 * t + 4 * j) =
+          key_word(img_k + 2 * h * kD, t, j);
     } else {
-      const int w = u - nkw, h = w >> 8, oct = (w >> 6) & 3, qt = (w >> 4) & 3, i = (w >> 2) & 3,
-                d = w & 3;
-      const uint4* src = reinterpret_cast<const uint4*>(img_v + (h * 4 + d) * kVImgRow + 16 * oct);
-      const int m = 4 * qt + i;
-      uint32_t word = 0u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 w4 = src[q];  // tokens 8 oct + 2q, + 2q + 1; words e = 0, 1
-        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const int kk = 2 * q + (f >> 1), e = f & 1;
-          const int sk = (kk & 4) | ((kk & 1) << 1) | ((kk >> 1) & 1);
-          word |= ((ww[f] >> (2 * m)) & 3u) << (2 * (8 * e + sk));
-        }
-      }
-      *reinterpret_cast<uint32_t*>(rec_of(h) + kRecVCodes + 16 * (16 * oct + m) + 4 * d) = word;
+      const int w = u - nkw, h = w >> 8, oct = (w >> 6) & 3, m = (w >> 2) & 15, d = w & 3;
+      *reinterpret_cast<uint32_t*>(rec_of(h) + kRecVCodes + 16 * (16 * oct + m) + 4 * d) =
+          value_word(img_v + 4 * h * kVImgRow, oct, m, d);
     }
   }
 }
@@ -639,7 +643,7 @@ extern "C" oscar_status oscar_quant_pack(const void* khat16, const void* knorm16
   if (n_blocks < 0 || n_kv_heads < 1 || n_kv_heads > 16) return OSCAR_EINVAL;
   if (norm_scope == OSCAR_NORM_HEAD) return OSCAR_EUNSUPPORTED;
   if (norm_scope != OSCAR_NORM_TOKEN) return OSCAR_EINVAL;
-  if (!aligned(rec_out, 16)) return OSCAR_EINVAL;
+  if (!aligned(rec_out, 16) || !aligned(v16, 16)) return OSCAR_EINVAL;
   oscar_status st = check_device();
   if (st != OSCAR_OK) return st;
   if (n_blocks == 0) return OSCAR_OK;

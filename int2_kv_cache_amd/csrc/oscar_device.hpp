@@ -134,36 +134,6 @@ __device__ __forceinline__ void scale_from_ss(float ss, float& norm, float& r) {
   r = ss > 0.0f ? __fdiv_rn(1.0f, norm) : 0.0f;
 }
 
-// INT2 min-max quantizer over 32 values (fp16-valued fp32): delta =
-// (max - min)/3, zero = min, code = clamp(rint((x - zero)/delta), 0, 3),
-// round half to even, delta == 0 -> code 0 ([SUM] 前置知识 on per-channel
-// quantization and 方法步骤详情; [RN] §I).  A zero minimum or maximum is
-// canonicalised to +0.  Codes are returned 2 bits each, value i at bits 2i.
-__device__ __forceinline__ uint64_t quant32(const float* x, float& delta, float& zero) {
-#pragma clang fp contract(off)
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int i = 1; i < 32; ++i) {
-    mn = fminf(mn, x[i]);
-    mx = fmaxf(mx, x[i]);
-  }
-  mn = mn + 0.0f;
-  mx = mx + 0.0f;
-  const float d = __fdiv_rn(mx - mn, 3.0f);
-  uint64_t codes = 0;
-  if (d > 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float r = rintf(__fdiv_rn(x[i] - mn, d));
-      const int q = r < 0.0f ? 0 : (r > 3.0f ? 3 : static_cast<int>(r));
-      codes |= static_cast<uint64_t>(q) << (2 * i);
-    }
-  }
-  delta = d;
-  zero = mn;
-  return codes;
-}
-
 // Packed record layout (see include/oscar.h).
 __device__ __forceinline__ int kcode_bitpos(int t, int c) {   // bit index in K codes
   return 8 * (32 * t + (c >> 2)) + 2 * (c & 3);

@@ -78,6 +78,61 @@ def test_quant_pack_bit_exact(nb, hkv):
     assert_same_bits(host_u16(nrm), wn, "norms")
 
 
+def _tie_groups(rng, shape):
+    """Values whose quantization quotients (x - min) / delta are exact half
+    integers under a delta that is not a power of two: per 32-value group
+    min = -r d/2, max = min + 3 d, the rest min + q d/2 (q = 0..6), with
+    d = m 2^e, m odd <= 15, so every value is exact in bf16 and fp16 and the
+    correctly rounded 1/delta is inexact.  shape[-1] is a multiple of 32."""
+    *lead, c = shape
+    g = int(np.prod(lead)) * (c // 32)
+    m = rng.choice(np.arange(3, 16, 2), g)
+    e = rng.integers(-9, -2, g)
+    d = (m * np.exp2(e)).astype(np.float64)
+    r = rng.integers(0, 7, g)
+    q = rng.integers(0, 7, (g, 32))
+    q[:, 0], q[:, 1] = 0, 6
+    x = (q - r[:, None]) * (d[:, None] / 2)
+    return x.reshape(*lead, c).astype(np.float32)
+
+
+def test_quant_pack_exact_ties():
+    """Keys and Values whose every second quotient is a tie: the reciprocal
+    fast path must hand each of them to the exact division."""
+    rng = np.random.default_rng(7)
+    nb, hkv = 4, 2
+    wl = synth.workload(2, ctx=32 * nb + 10)
+    k, v = wl.prefill(0, 32 * nb)
+    khat, knorm = oracle.rotate_scale_key(np.ascontiguousarray(k[:, :hkv]), synth.BF16)
+    # Key ties run along the tokens of a channel: groups of 32 tokens
+    kt = _tie_groups(rng, (nb, hkv, 128, 32)).transpose(0, 3, 1, 2).reshape(32 * nb, hkv, 128)
+    khat[:, :, 64:] = synth.to_fp16_bits(kt[:, :, 64:])
+    v16 = synth.to_fp16_bits(_tie_groups(rng, (32 * nb, hkv, 128)))
+    rec = torch.zeros(nb, hkv, 3072, dtype=torch.uint8, device="cuda")
+    nrm = torch.zeros(nb, 32, dtype=torch.int16, device="cuda")
+    ok.quant_pack(dev_u16(khat), dev_u16(knorm), dev_u16(v16), rec, nrm)
+    torch.cuda.synchronize()
+    wr, wn = oracle.quant_pack(khat, knorm, v16)
+    assert_same_bits(rec.cpu().numpy(), wr, "records")
+
+
+def test_prefill_and_flush_value_ties():
+    """bf16 Values with exact-tie quotients through bulk prefill and through
+    appends that flush blocks."""
+    rng = np.random.default_rng(11)
+    wl = synth.workload(1, ctx=32 * 6 + 150 + 40)
+    pr = Pair(wl)
+    n0 = 32 * 6 + 150
+    k, _ = wl.prefill(0, n0)
+    v = synth.to_bf16_bits(_tie_groups(rng, (n0, wl.cfg.hkv, 128)))
+    pr.prefill(0, k, v)
+    pr.compare_state()
+    for kn, _, _ in wl.steps(40):
+        vn = synth.to_bf16_bits(_tie_groups(rng, (1, wl.cfg.hkv, 128)))
+        pr.append(kn, vn)
+    pr.compare_state()
+
+
 @pytest.mark.parametrize("cfg,batch,steps", [(0, 1, 300), (1, 2, 200)])
 def test_append_sequence_bit_exact(cfg, batch, steps):
     """Appends from an empty cache cross several window flushes."""
