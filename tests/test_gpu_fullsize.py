@@ -62,3 +62,11 @@ def test_ragged_batch_8k_32k():
     wl = synth.workload(3, batch=6)
     wl.ctx_lens = wl.ctx_lens[:6]
     _run(wl, [(b, (7 * b) % 32) for b in range(6)])
+
+
+def test_ragged_batch_48_full():
+    """The whole 48-sequence ragged batch (contexts 8K..32K) in one launch,
+    sampled (sequence, head) outputs against the oracle."""
+    wl = synth.workload(3)
+    assert wl.cfg.batch == 48
+    _run(wl, [(b, (5 * b + 3) % 32) for b in range(0, 48, 6)], variants=(2,))
