@@ -76,6 +76,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="query heads of the oracle sample (scaled to all heads)")
+    ap.add_argument("--batch48", action="store_true",
+                    help="instead of the headline run: the batched workload (48 ragged "
+                         "sequences of 8K..32K tokens, every one of 36 layer caches resident), "
+                         "one JSON line of its own")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times) and "
                          "exit: the reference for scaling HBM byte counters")
@@ -123,10 +127,134 @@ def cpu_baseline(wl, k, v, steps, hq, args):
             "cpu": platform.processor() or platform.machine()}
 
 
+def batch48(args):
+    """The batched decode workload: 48 sequences with contexts drawn from
+    8K..32K (block-table indexed, blocks packed per sequence), 32/8 heads,
+    bf16; one layer's cache is prefilled and copied to all 36 layers, which
+    stay resident.  A step appends one token to every sequence and runs
+    decode attention, layer by layer.  Reports decode tokens/s (48 per step)
+    and the attention's algorithmic bandwidth."""
+    import torch
+
+    import int2_kv_cache_amd as ok
+    from int2_kv_cache_amd import synth
+
+    torch.cuda.set_device(0)
+    wl = synth.workload(3)
+    cfg = wl.cfg
+    L = 36
+    B = cfg.batch
+    steps = args.steps if args.steps != 100 else 10
+    warm = args.warmup if args.warmup != 5 else 2
+    n_total = steps + warm
+    cap = [(n + n_total + 64 + 31) // 32 for n in wl.ctx_lens]
+    mb = max(cap)
+    nphys = sum(cap)
+    table = np.full((B, mb), -1, np.int32)
+    off = 0
+    for b, c in enumerate(cap):
+        table[b, :c] = np.arange(off, off + c)
+        off += c
+    geom = ok.make_geom(B, cfg.hq, cfg.hkv, mb, nphys)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    t0 = time.perf_counter()
+    c0 = ok.DeviceCache(geom, block_table=table)
+    for b in range(B):
+        k, v = wl.prefill(b)
+        ok.prefill_quantize(c0, b, dev(k), dev(v), cfg.dtype)
+    torch.cuda.synchronize()
+    print("batch48: prefilled %d sequences (%.1f s)" % (B, time.perf_counter() - t0),
+          file=sys.stderr, flush=True)
+    caches = [c0]
+    for _ in range(L - 1):
+        c = ok.DeviceCache(geom, block_table=table)
+        for name in ("pool", "pool_norm", "res_k", "res_v", "res_norm", "seq_state"):
+            getattr(c, name).copy_(getattr(c0, name))
+        caches.append(c)
+    torch.cuda.synchronize()
+    print("batch48: %d layer caches resident (%.1f s)" % (L, time.perf_counter() - t0),
+          file=sys.stderr, flush=True)
+    stp = list(wl.steps(n_total))
+    kn_d = [dev(x[0]) for x in stp]
+    vn_d = [dev(x[1]) for x in stp]
+    q_d = [dev(x[2]) for x in stp]
+    max_ctx = max(wl.ctx_lens) + n_total + 64
+    S, nbytes = ok.decode_workspace_bytes(geom, max_ctx, args.splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, cfg.hq, 128, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, cfg.hq, dtype=torch.float32, device="cuda")
+    setup_s = time.perf_counter() - t0
+
+    def step(i, ev=None, ev_layer=-1):
+        for li, c in enumerate(caches):
+            ok.append_kv(c, kn_d[i], vn_d[i], cfg.dtype)
+            if li == ev_layer:
+                ev[0].record()
+            ok.decode_attn(c, q_d[i], cfg.dtype, out, lse, ws, max_ctx, S, args.variant)
+            if li == ev_layer:
+                ev[1].record()
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    n0 = caches[0].seq_state.cpu().numpy()[:, 0].astype(np.int64)
+    attn_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t_beg, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_beg.record()
+    for s_i in range(steps):
+        step(warm + s_i, attn_ev[s_i], (7 * s_i) % L)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_beg.elapsed_time(t_end)
+    attn_us = float(np.mean([e[0].elapsed_time(e[1]) for e in attn_ev])) * 1000.0
+    assert int(caches[0].error_flag.item()) == 0
+    n_mid = n0 + 1 + steps // 2
+    q_mid = 32 * ((np.maximum(0, n_mid - 128) + 31) // 32)
+    bytes_attn = sum(algorithmic_bytes(int(n), int(q), cfg.hq, cfg.hkv) for n, q in zip(n_mid, q_mid))
+    achieved = bytes_attn / (attn_us * 1e-6) / 1e9
+    int2_bytes = sum(int(n) // 32 * (cfg.hkv * 3072 + 64) + 128 * (cfg.hkv * 512 + 2)
+                     for n in n0) * L
+    bf16_bytes = int(np.sum(n0)) * cfg.hkv * 128 * 2 * 2 * L
+    res = {
+        "metric": "decode tokens/s, batch 48 ragged 8K..32K, 36 layers resident",
+        "value": B * steps / (total_ms / 1000.0),
+        "unit": "decode tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": total_ms / steps,
+        "higher_is_better": True,
+        "dtype": "int2 cache; fp16 MFMA operands, fp32 accumulate",
+        "data": "synthetic (seeded; K outliers/sinks/log-normal norms, V and q N(0,1))",
+        "config": {"workload": "qwen3-8b-shape decode, batch 48, contexts 8K..32K, 36 layers",
+                   "batch": B, "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv,
+                   "head_dim": 128, "mean_ctx": float(np.mean(n0)), "layers": L, "splits": S},
+        "ctx_tokens_per_s": float(np.sum(n0 + 1 + (steps - 1) / 2.0)) * L / (total_ms / 1000.0),
+        "us_per_layer_step": total_ms * 1000.0 / (steps * L),
+        "attn_us_per_layer": attn_us,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_attn (split-K attention + LSE reduce, timed together)",
+                     "algorithmic_bytes": bytes_attn},
+        "cache_bytes_int2_36_layers": int2_bytes,
+        "cache_bytes_bf16_36_layers": bf16_bytes,
+        "setup_s": setup_s,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.batch48:
+        if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        batch48(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "
