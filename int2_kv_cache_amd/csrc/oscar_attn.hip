@@ -276,6 +276,18 @@ __device__ __forceinline__ float dpp(float x) {
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 constexpr int dpp_row_shl(int n) { return 0x100 + n; }
 
+// x + (x of lane l + N in the same row of 16, 0 past the row's end): one
+// v_add_f32_dpp (the compiler keeps the DPP move and the add apart here).
+// The s_nop covers the DPP read-after-VALU-write hazard of the source.
+template <int N>
+__device__ __forceinline__ float add_row_shl(float x) {
+  float r;
+  asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_shl:%2 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+               : "=v"(r)
+               : "v"(x), "i"(N));
+  return r;
+}
+
 // max / sum over aligned groups of N lanes; every lane of a group gets the result
 template <int N>
 __device__ __forceinline__ float group_max(float v) {
@@ -648,8 +660,10 @@ void attn_mfma_kernel(AttnArgs A) {
     const int i = wave + 4 * j;
     if (i < GRP) {
       if (A.q_mode != 2) fht128_wave(qx[j], qy[j]);
-      qs[i * kD + L] = qx[j];
-      qs[i * kD + L + 64] = qy[j];
+      // q' carries the score scale 1/sqrt(128) * log2(e): every score
+      // comes out in the log2 domain of the softmax
+      qs[i * kD + L] = qx[j] * kScale;
+      qs[i * kD + L + 64] = qy[j] * kScale;
     }
   }
   __syncthreads();
@@ -670,27 +684,27 @@ void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         const int t = sm_t0 + j;
-        sv[j] = t < t_valid ? (Wsc[sm_head][t] + kp) * nt[j] * kScale : -INFINITY;
+        sv[j] = t < t_valid ? (Wsc[sm_head][t] + kp) * nt[j] : -INFINITY;
         bm = fmaxf(bm, sv[j]);
       }
     }
     bm = group_max<LPH>(bm);
     const float m_new = fmaxf(m_run, bm);
     const bool grow = sm_on && m_new > m_run;
-    const float f = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // -inf gives 0
+    float ps = 0.0f;
     if (sm_on) {
-      float ps = 0.0f;
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         const float pj = __builtin_amdgcn_exp2f(sv[j] - m_new);  // -inf gives 0
         Wpr[sm_head][sm_t0 + j] = pj;
         ps += pj;
       }
-      l_part = l_part * f + ps;
     }
-    m_run = m_new;
     if (!first && __any(grow)) {
       // rare after the first blocks: rescale the heads whose maximum grew
+      // (a wave's first block has m_run = -inf: factor 0 on zero sums)
+      const float f = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // -inf gives 0
+      l_part *= f;
       if (sm_on && (L % LPH) == 0) Wfac[sm_head] = f;
       lds_order();
       const float fo = col < NCOL ? Wfac[col % GRP] : 1.0f;
@@ -702,6 +716,8 @@ void attn_mfma_kernel(AttnArgs A) {
         if (c < NCOMBO) zacc[r] *= Wfac[(c >> 2) % GRP];
       }
     }
+    l_part += ps;
+    m_run = m_new;
     lds_order();
   };
 
@@ -711,7 +727,7 @@ void attn_mfma_kernel(AttnArgs A) {
     for (int tau = 0; tau < 2; ++tau) {
       f32x4 v;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = cs[tau][j] + dpp<dpp_row_shl(GRP)>(cs[tau][j]);
+      for (int j = 0; j < 4; ++j) v[j] = add_row_shl<GRP>(cs[tau][j]);
       if (col < GRP) *reinterpret_cast<f32x4*>(&Wsc[col][16 * tau + 4 * g4]) = v;
     }
     lds_order();
@@ -946,7 +962,7 @@ void attn_mfma_kernel(AttnArgs A) {
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      ov[ct][j] = o[ct][j] + dpp<dpp_row_shl(GRP)>(o[ct][j]) + (col < GRP ? Wzs[ct >> 1][col] : 0.0f);
+      ov[ct][j] = add_row_shl<GRP>(o[ct][j]) + (col < GRP ? Wzs[ct >> 1][col] : 0.0f);
   // the stages take the waves' partial outputs: head hh of wave w at
   // (hh < 4 ? stage0 : stage1)[w] + 512 (hh % 4) bytes, once every copy into
   // them has landed
