@@ -276,18 +276,6 @@ __device__ __forceinline__ float dpp(float x) {
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 constexpr int dpp_row_shl(int n) { return 0x100 + n; }
 
-// x + (x of lane l + N in the same row of 16, 0 past the row's end): one
-// v_add_f32_dpp (the compiler keeps the DPP move and the add apart here).
-// The s_nop covers the DPP read-after-VALU-write hazard of the source.
-template <int N>
-__device__ __forceinline__ float add_row_shl(float x) {
-  float r;
-  asm volatile("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_shl:%2 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-               : "=v"(r)
-               : "v"(x), "i"(N));
-  return r;
-}
-
 // max / sum over aligned groups of N lanes; every lane of a group gets the result
 template <int N>
 __device__ __forceinline__ float group_max(float v) {
@@ -727,7 +715,7 @@ void attn_mfma_kernel(AttnArgs A) {
     for (int tau = 0; tau < 2; ++tau) {
       f32x4 v;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = add_row_shl<GRP>(cs[tau][j]);
+      for (int j = 0; j < 4; ++j) v[j] = cs[tau][j] + dpp<dpp_row_shl(GRP)>(cs[tau][j]);
       if (col < GRP) *reinterpret_cast<f32x4*>(&Wsc[col][16 * tau + 4 * g4]) = v;
     }
     lds_order();
@@ -962,7 +950,7 @@ void attn_mfma_kernel(AttnArgs A) {
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      ov[ct][j] = add_row_shl<GRP>(o[ct][j]) + (col < GRP ? Wzs[ct >> 1][col] : 0.0f);
+      ov[ct][j] = o[ct][j] + dpp<dpp_row_shl(GRP)>(o[ct][j]) + (col < GRP ? Wzs[ct >> 1][col] : 0.0f);
   // the stages take the waves' partial outputs: head hh of wave w at
   // (hh < 4 ? stage0 : stage1)[w] + 512 (hh % 4) bytes, once every copy into
   // them has landed
