@@ -82,7 +82,8 @@ typedef struct {
     int32_t num_q_heads;         /* Hq */
     int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0, Hq/Hkv in {1,2,4,8} */
     int32_t head_dim;            /* must be 128 */
-    int32_t norm_scope;          /* oscar_norm_scope; only TOKEN is built */
+    int32_t norm_scope;          /* oscar_norm_scope: TOKEN (default) or HEAD,
+                                    which sizes the two norm buffers below */
     int32_t max_blocks_per_seq;  /* block-table row length */
     int32_t num_physical_blocks; /* pool capacity */
 } oscar_cache_geom;
@@ -100,10 +101,11 @@ typedef struct {
  *                 [2048,2304) K step (delta) fp16 [128]
  *                 [2304,2560) K zero point fp16 [128]
  *                 [2560,3072) V (step, zero) fp16 pairs, [4 groups][32 tokens]
- *   pool_norm   [num_physical_blocks][32] fp16 token norms
+ *   pool_norm   [num_physical_blocks][32] fp16 token norms (TOKEN scope), or
+ *               [num_physical_blocks][Hkv][32] norms per (token, KV head) (HEAD)
  *   res_k       [B][Hkv][128 slots][128] fp16 rotated+scaled keys (k_hat)
  *   res_v       [B][Hkv][128 channels][128 slots] fp16 values
- *   res_norm    [B][128 slots] fp16 token norms
+ *   res_norm    [B][128 slots] fp16 token norms (TOKEN), or [B][Hkv][128] (HEAD)
  *   block_table [B][max_blocks_per_seq] int32 physical block ids (caller fills)
  *   seq_state   [B][2] int32 = {n tokens, Q quantized tokens}; zero = empty
  *   error_flag  [1] int32 sticky bits (OSCAR_FLAG_*); caller zeroes it
@@ -151,9 +153,12 @@ OSCAR_API oscar_status oscar_rotate_scale(const void *x, oscar_dtype dtype, int3
  * 方法步骤详情 ②, the quantization kernel handling Keys and Values together).
  *   khat16, v16  device, [32*n_blocks][n_kv_heads][128] fp16; v16 16-byte
  *                aligned.
- *   knorm16      device, [32*n_blocks] fp16 token norms (TOKEN scope).
+ *   knorm16      device, fp16 norms: [32*n_blocks] (TOKEN scope) or
+ *                [32*n_blocks][n_kv_heads] (HEAD scope), as oscar_rotate_scale
+ *                returns them.
  *   rec_out      device, [n_blocks][n_kv_heads][3072] records (layout above).
- *   norm_out     device, [n_blocks][32] fp16.
+ *   norm_out     device, fp16 [n_blocks][32] (TOKEN) or [n_blocks][n_kv_heads][32]
+ *                (HEAD).
  * Keys: per channel over the block's 32 tokens; Values: per token over each
  * 32-channel group; delta = (max-min)/3, zero = min, code =
  * clamp(rint((x-zero)/delta), 0, 3) in IEEE fp32, delta == 0 -> code 0.

@@ -134,10 +134,13 @@ class DeviceCache:
             return torch.zeros(n, dtype=torch.uint8, device=device)
 
         self.pool = u8(sz.pool).view(geom.num_physical_blocks, H, RECORD_BYTES)
-        self.pool_norm = torch.zeros(geom.num_physical_blocks, 32, dtype=torch.int16, device=device)
+        nh = (H,) if geom.norm_scope == NORM_HEAD else ()   # norms per (token, KV head)
+        self.pool_norm = torch.zeros(geom.num_physical_blocks, *nh, 32, dtype=torch.int16,
+                                     device=device)
         self.res_k = torch.zeros(B, H, 128, 128, dtype=torch.int16, device=device)
         self.res_v = torch.zeros(B, H, 128, 128, dtype=torch.int16, device=device)
-        self.res_norm = torch.zeros(B, 128, dtype=torch.int16, device=device)
+        self.res_norm = torch.zeros(B, *nh, 128, dtype=torch.int16, device=device)
+        assert self.pool_norm.numel() * 2 == sz.pool_norm and self.res_norm.numel() * 2 == sz.res_norm
         if block_table is None:
             block_table = torch.arange(B * geom.max_blocks_per_seq, dtype=torch.int32)
             block_table = block_table.view(B, geom.max_blocks_per_seq) % geom.num_physical_blocks

@@ -32,8 +32,7 @@ oscar_status check_geom(const oscar_cache_geom* g) {
   const int grp = g->num_q_heads / g->num_kv_heads;
   if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return OSCAR_EINVAL;
   if (g->max_blocks_per_seq < 1 || g->num_physical_blocks < 1) return OSCAR_EINVAL;
-  if (g->norm_scope == OSCAR_NORM_HEAD) return OSCAR_EUNSUPPORTED;
-  if (g->norm_scope != OSCAR_NORM_TOKEN) return OSCAR_EINVAL;
+  if (g->norm_scope != OSCAR_NORM_TOKEN && g->norm_scope != OSCAR_NORM_HEAD) return OSCAR_EINVAL;
   return OSCAR_OK;
 }
 
@@ -60,10 +59,11 @@ extern "C" oscar_status oscar_cache_layout(const oscar_cache_geom* g, oscar_cach
   if (st != OSCAR_OK) return st;
   const size_t B = g->batch, H = g->num_kv_heads, P = g->num_physical_blocks;
   out->pool = P * H * OSCAR_RECORD_BYTES;
-  out->pool_norm = P * 32 * sizeof(uint16_t);
+  const size_t NH = g->norm_scope == OSCAR_NORM_HEAD ? H : 1;  // norms per token
+  out->pool_norm = P * NH * 32 * sizeof(uint16_t);
   out->res_k = B * H * 128 * 128 * sizeof(uint16_t);
   out->res_v = B * H * 128 * 128 * sizeof(uint16_t);
-  out->res_norm = B * 128 * sizeof(uint16_t);
+  out->res_norm = B * NH * 128 * sizeof(uint16_t);
   out->block_table = B * static_cast<size_t>(g->max_blocks_per_seq) * sizeof(int32_t);
   out->seq_state = B * 2 * sizeof(int32_t);
   out->error_flag = sizeof(int32_t);

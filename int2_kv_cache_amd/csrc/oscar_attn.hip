@@ -33,10 +33,19 @@ struct AttnArgs {
   const void* q;
   int q_mode;  // 0 fp16, 1 bf16, 2 fp32 pre-rotated
   int hkv, hq, max_blocks, nphys, splits;
+  int head_norm;  // 1: token norms per (token, KV head): [P][Hkv][32], [B][Hkv][128]
   int32_t* error_flag;
   float2* ws_ml;  // [B][Hq][S] (m, l)
   float* ws_o;    // [B][Hq][S][128]
 };
+
+// The 32 token norms of block p for KV head h, and window slot 0 of (b, h).
+__device__ __forceinline__ const uint16_t* block_norms(const AttnArgs& A, int p, int h) {
+  return A.pool_norm + (A.head_norm ? (static_cast<size_t>(p) * A.hkv + h) * 32 : static_cast<size_t>(p) * 32);
+}
+__device__ __forceinline__ const uint16_t* window_norms(const AttnArgs& A, int b, int h) {
+  return A.res_norm + (A.head_norm ? (static_cast<size_t>(b) * A.hkv + h) * kR : static_cast<size_t>(b) * kR);
+}
 
 // Rotated query heads of KV head h into qs[GRP][128] (fp32).
 template <int GRP>
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs A) {
       }
       const uint4* rec = reinterpret_cast<const uint4*>(A.pool + (static_cast<size_t>(p) * A.hkv + h) * kRec);
       if (tid < 192) stage[tid] = rec[tid];
-      else if (tid < 196) stage[tid] = reinterpret_cast<const uint4*>(A.pool_norm + static_cast<size_t>(p) * 32)[tid - 192];
+      else if (tid < 196) stage[tid] = reinterpret_cast<const uint4*>(block_norms(A, p, h))[tid - 192];
       __syncthreads();
       const uint16_t* dl = st16 + kRecKDelta / 2;
       const uint16_t* zr = st16 + kRecKZero / 2;
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs A) {
         const int t = tid / GRP, i = tid % GRP;
         float acc = 0.0f;
         for (int c = 0; c < kD; ++c) acc += qs[i * kD + c] * f16_to_f32(st16[t * kD + c]);
-        const float nt = f16_to_f32(A.res_norm[static_cast<size_t>(b) * kR + s0 + (t < t_valid ? t : 0)]);
+        const float nt = f16_to_f32(window_norms(A, b, h)[s0 + (t < t_valid ? t : 0)]);
         sc[i][t] = t < t_valid ? nt * acc * (kInvSqrtD * kLog2e) : -INFINITY;
       }
     }
@@ -628,7 +637,7 @@ void attn_mfma_kernel(AttnArgs A) {
   auto unit_rec = [&](int p) {
     return rsrc(A.pool + (static_cast<size_t>(p) * A.hkv + h) * kRec, kRec);
   };
-  auto unit_nrm = [&](int p) { return rsrc(A.pool_norm + static_cast<size_t>(p) * 32, 64); };
+  auto unit_nrm = [&](int p) { return rsrc(block_norms(A, p, h), 64); };
 
   // Block j of the wave goes through stage j % 2.  Its DMA is issued two
   // blocks ahead (unconditionally: past the end it re-reads the last block)
@@ -907,7 +916,7 @@ void attn_mfma_kernel(AttnArgs A) {
       rv[ct] = *reinterpret_cast<const u32x4*>(A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
 #pragma unroll
     for (int j = 0; j < TPL; ++j)
-      rnt[j] = f16_to_f32(A.res_norm[static_cast<size_t>(b) * kR + slot0 + ((sm_t0 + j) & 31)]);
+      rnt[j] = f16_to_f32(window_norms(A, b, h)[slot0 + ((sm_t0 + j) & 31)]);
     // q' hi/lo B tiles, channels 32 g4 + 8 kk + 0..7 in natural order
     u32x4 bq[4];
 #pragma unroll
@@ -1156,6 +1165,7 @@ extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const os
   A.res_k = static_cast<const uint16_t*>(cache->res_k);
   A.res_v = static_cast<const uint16_t*>(cache->res_v);
   A.res_norm = static_cast<const uint16_t*>(cache->res_norm);
+  A.head_norm = geom->norm_scope == OSCAR_NORM_HEAD ? 1 : 0;
   A.block_table = cache->block_table;
   A.seq_state = cache->seq_state;
   A.q = q;

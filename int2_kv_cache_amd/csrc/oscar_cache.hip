@@ -134,7 +134,8 @@ __device__ __forceinline__ uint32_t value_word(const uint32_t* img, int oct, int
 __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restrict__ khat,
                                                          const uint16_t* __restrict__ knorm,
                                                          const uint16_t* __restrict__ v16,
-                                                         int hkv, uint8_t* __restrict__ rec_out,
+                                                         int hkv, int head_norm,
+                                                         uint8_t* __restrict__ rec_out,
                                                          uint16_t* __restrict__ norm_out) {
   __shared__ __attribute__((aligned(16))) uint32_t img_k[2 * kD];
   __shared__ __attribute__((aligned(16))) uint32_t img_v[4 * kVImgRow];
@@ -178,7 +179,13 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(const uint16_t* __restr
     *reinterpret_cast<uint32_t*>(rec + kRecVCodes + 16 * (16 * oct + m) + 4 * d) =
         value_word(img_v, oct, m, d);
   }
-  if (h == 0 && tg < 32) norm_out[static_cast<size_t>(j) * 32 + tg] = knorm[32 * j + tg];
+  // norms: TOKEN knorm [T] -> [n_blocks][32]; HEAD knorm [T][Hkv] -> [n_blocks][Hkv][32]
+  if (tg < 32) {
+    if (head_norm)
+      norm_out[(static_cast<size_t>(j) * hkv + h) * 32 + tg] = knorm[static_cast<size_t>(32 * j + tg) * hkv + h];
+    else if (h == 0)
+      norm_out[static_cast<size_t>(j) * 32 + tg] = knorm[32 * j + tg];
+  }
 }
 
 // Quad cross-lane read (lanes 4m..4m+3 exchange): xor 1 or xor 2.
@@ -201,7 +208,16 @@ struct CacheArgs {
   int hkv;
   int max_blocks;
   int nphys;
+  int head_norm;  // 1: a norm per (token, KV head) ([P][Hkv][32], [B][Hkv][128])
 };
+// Token norm slots: TOKEN scope [P][32] and [B][128]; HEAD scope [P][Hkv][32]
+// and [B][Hkv][128].
+__device__ __forceinline__ size_t pool_norm_at(const CacheArgs& ca, int p, int h, int t) {
+  return ca.head_norm ? (static_cast<size_t>(p) * ca.hkv + h) * 32 + t : static_cast<size_t>(p) * 32 + t;
+}
+__device__ __forceinline__ size_t res_norm_at(const CacheArgs& ca, int b, int h, int slot) {
+  return ca.head_norm ? (static_cast<size_t>(b) * ca.hkv + h) * kR + slot : static_cast<size_t>(b) * kR + slot;
+}
 
 // {n, Q} as the kernels leave it: 0 <= Q, Q % 32 == 0, 0 <= n - Q <= 128,
 // Q / 32 <= max_blocks.
@@ -252,7 +268,8 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
       return;
     }
     const int s0 = Q % kR;
-    if (tid < 32) ca.pool_norm[static_cast<size_t>(p) * 32 + tid] = ca.res_norm[b * kR + s0 + tid];
+    for (int i = tid; i < (ca.head_norm ? hkv : 1) * 32; i += blockDim.x)
+      ca.pool_norm[pool_norm_at(ca, p, i >> 5, i & 31)] = ca.res_norm[res_norm_at(ca, b, i >> 5, s0 + (i & 31))];
     const size_t bh0 = static_cast<size_t>(b) * hkv;
     auto rec_of = [&](int h) { return ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec; };
     // ranges: Key (head, channel) over the 32 ring tokens, Value (token,
@@ -349,7 +366,8 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
   __syncthreads();
   if (h < hkv) {
     float nrm, r;
-    scale_from_ss(tree16(part, hkv), nrm, r);
+    // TOKEN: the tree over all heads; HEAD: the head's own (within-head) tree
+    scale_from_ss(ca.head_norm ? part[h] : tree16(part, hkv), nrm, r);
     const size_t bh = static_cast<size_t>(b) * hkv + h;
     uint16_t* rk = ca.res_k + (bh * kR + slot) * kD;
     rk[lane] = f32_to_f16(mul_rn(a, r));
@@ -357,7 +375,7 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
     uint16_t* rv = ca.res_v + bh * kD * kR + slot;
     rv[static_cast<size_t>(lane) * kR] = f32_to_f16(in_to_f32(vin[0], is_bf16));
     rv[static_cast<size_t>(lane + 64) * kR] = f32_to_f16(in_to_f32(vin[1], is_bf16));
-    if (h == 0 && lane == 0) ca.res_norm[b * kR + slot] = f32_to_f16(nrm);
+    if (lane == 0 && (ca.head_norm || h == 0)) ca.res_norm[res_norm_at(ca, b, h, slot)] = f32_to_f16(nrm);
   }
   if (tid == 0) {
     st[0] = n + 1;
@@ -405,7 +423,7 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
   uint8_t* prm = dyn + static_cast<size_t>(32) * hkv * kD * 2;
   uint32_t* img_k = reinterpret_cast<uint32_t*>(prm);                    // [hkv][2][128]
   float* part = reinterpret_cast<float*>(prm);                          // rotation phase: [32][hkv]
-  float* tok_r = part + 32 * hkv;                                        // [32]
+  float* tok_r = part + 32 * hkv;                          // [32] or [32][hkv] (HEAD)
 
   if (ca.seq_state[2 * seq] != 0) {
     if (blockIdx.x == 0 && threadIdx.x == 0)
@@ -486,16 +504,19 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
     }
   }
   __syncthreads();
-  if (tid < 32) {
+  // one factor per token (TOKEN: tree over the heads) or per (token, head)
+  // (HEAD: the head's own tree); NT >= 32 * 16
+  if (tid < 32 * (ca.head_norm ? hkv : 1)) {
+    const int tl = ca.head_norm ? tid / hkv : tid, h = ca.head_norm ? tid % hkv : 0;
     float nrm, r;
-    scale_from_ss(tree16(part + tid * hkv, hkv), nrm, r);
+    scale_from_ss(ca.head_norm ? part[tid] : tree16(part + tid * hkv, hkv), nrm, r);
     tok_r[tid] = r;
-    const int t = t0 + tid;
+    const int t = t0 + tl;
     if (t < n_tokens) {
       if (ring)
-        ca.res_norm[seq * kR + t % kR] = f32_to_f16(nrm);
+        ca.res_norm[res_norm_at(ca, seq, h, t % kR)] = f32_to_f16(nrm);
       else
-        ca.pool_norm[static_cast<size_t>(p) * 32 + tid] = f32_to_f16(nrm);
+        ca.pool_norm[pool_norm_at(ca, p, h, tl)] = f32_to_f16(nrm);
     }
   }
   __syncthreads();
@@ -507,7 +528,7 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
     if (rr * NT >= nvec * 4) break;
     const int t = vtx / hkv, h = vtx % hkv;
     if (vtx < nvec && t0 + t < n_tokens) {
-      const float r = tok_r[t];
+      const float r = tok_r[ca.head_norm ? t * hkv + h : t];
       uint32_t kw[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e)
@@ -628,6 +649,7 @@ CacheArgs make_args(const oscar_cache_geom* g, const oscar_cache* c) {
   a.hkv = g->num_kv_heads;
   a.max_blocks = g->max_blocks_per_seq;
   a.nphys = g->num_physical_blocks;
+  a.head_norm = g->norm_scope == OSCAR_NORM_HEAD ? 1 : 0;
   return a;
 }
 
@@ -641,8 +663,7 @@ extern "C" oscar_status oscar_quant_pack(const void* khat16, const void* knorm16
                                          void* norm_out, void* stream) {
   if (!khat16 || !knorm16 || !v16 || !rec_out || !norm_out) return OSCAR_EINVAL;
   if (n_blocks < 0 || n_kv_heads < 1 || n_kv_heads > 16) return OSCAR_EINVAL;
-  if (norm_scope == OSCAR_NORM_HEAD) return OSCAR_EUNSUPPORTED;
-  if (norm_scope != OSCAR_NORM_TOKEN) return OSCAR_EINVAL;
+  if (norm_scope != OSCAR_NORM_TOKEN && norm_scope != OSCAR_NORM_HEAD) return OSCAR_EINVAL;
   if (!aligned(rec_out, 16) || !aligned(v16, 16)) return OSCAR_EINVAL;
   oscar_status st = check_device();
   if (st != OSCAR_OK) return st;
@@ -650,8 +671,8 @@ extern "C" oscar_status oscar_quant_pack(const void* khat16, const void* knorm16
   hipLaunchKernelGGL(quant_pack_kernel, dim3(n_blocks, n_kv_heads), dim3(256), 0,
                      as_stream(stream), static_cast<const uint16_t*>(khat16),
                      static_cast<const uint16_t*>(knorm16), static_cast<const uint16_t*>(v16),
-                     static_cast<int>(n_kv_heads), static_cast<uint8_t*>(rec_out),
-                     static_cast<uint16_t*>(norm_out));
+                     static_cast<int>(n_kv_heads), norm_scope == OSCAR_NORM_HEAD ? 1 : 0,
+                     static_cast<uint8_t*>(rec_out), static_cast<uint16_t*>(norm_out));
   return launch_status();
 }
 

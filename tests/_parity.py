@@ -49,17 +49,19 @@ def shuffled_table(batch: int, max_blocks: int, seed: int = 99) -> np.ndarray:
 class Pair:
     """The same cache on the GPU and in the oracle."""
 
-    def __init__(self, wl: synth.Workload, max_ctx: int | None = None, table=None):
+    def __init__(self, wl: synth.Workload, max_ctx: int | None = None, table=None,
+                 norm_scope: int = ok.NORM_TOKEN):
         cfg = wl.cfg
         self.wl = wl
         mctx = max_ctx or (max(wl.ctx_lens) + 8)
         self.max_blocks = blocks_needed(mctx)
         self.table = table if table is not None else shuffled_table(cfg.batch, self.max_blocks)
         nphys = cfg.batch * self.max_blocks
-        self.geom = ok.make_geom(cfg.batch, cfg.hq, cfg.hkv, self.max_blocks, nphys)
+        self.geom = ok.make_geom(cfg.batch, cfg.hq, cfg.hkv, self.max_blocks, nphys,
+                                 norm_scope=norm_scope)
         self.gpu = ok.DeviceCache(self.geom, block_table=torch.from_numpy(self.table))
         self.orc = oracle.OracleCache(cfg.batch, cfg.hq, cfg.hkv, self.max_blocks, nphys,
-                                      block_table=self.table)
+                                      block_table=self.table, norm_scope=norm_scope)
         self.dtype = cfg.dtype
 
     def prefill(self, b: int, k: np.ndarray, v: np.ndarray, gpu_bulk: bool = True):
@@ -96,7 +98,7 @@ class Pair:
             if len(slots):
                 assert_same_bits(rk[b][:, slots, :], o.res_k[b][:, slots, :], "res_k seq %d" % b)
                 assert_same_bits(rv[b][:, :, slots], o.res_v[b][:, :, slots], "res_v seq %d" % b)
-                assert_same_bits(rn[b][slots], o.res_norm[b][slots], "res_norm seq %d" % b)
+                assert_same_bits(rn[b][..., slots], o.res_norm[b][..., slots], "res_norm seq %d" % b)
 
     def attend(self, q: np.ndarray, variant=ok.ATTN_AUTO, splits=0, max_ctx=None,
                q_dtype=None, ws=None):

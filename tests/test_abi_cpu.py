@@ -49,11 +49,17 @@ def test_cache_layout_rejects(bad):
     assert e.value.status == ok.EINVAL
 
 
-def test_head_norm_scope_not_built():
-    g = ok.make_geom(1, 4, 1, 4, 4, norm_scope=ok.NORM_HEAD)
+def test_cache_layout_norm_scopes():
+    """TOKEN scope keeps one norm per token, HEAD one per (token, KV head);
+    any other scope value is rejected."""
+    t = ok.cache_layout(ok.make_geom(3, 16, 4, 10, 25))
+    h = ok.cache_layout(ok.make_geom(3, 16, 4, 10, 25, norm_scope=ok.NORM_HEAD))
+    assert (t.pool_norm, t.res_norm) == (25 * 32 * 2, 3 * 128 * 2)
+    assert (h.pool_norm, h.res_norm) == (25 * 4 * 32 * 2, 3 * 4 * 128 * 2)
+    assert (t.pool, t.res_k, t.res_v) == (h.pool, h.res_k, h.res_v)
     with pytest.raises(ok.OscarError) as e:
-        ok.cache_layout(g)
-    assert e.value.status == ok.EUNSUPPORTED
+        ok.cache_layout(ok.make_geom(1, 4, 1, 4, 4, norm_scope=7))
+    assert e.value.status == ok.EINVAL
 
 
 def test_status_strings():

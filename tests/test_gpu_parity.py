@@ -304,3 +304,60 @@ def test_abi_rejects_bad_arguments():
     with pytest.raises(ok.OscarError) as e:
         ok.decode_attn(pr.gpu, q, 0, out, None, small, 100, 0)
     assert e.value.status == ok.EWORKSPACE
+
+
+# ---------------------------------------------------------------- HEAD scope
+# One norm per (token, KV head) instead of one per token.
+
+@pytest.mark.parametrize("hkv", [3, 8])
+def test_head_scope_rotate_scale_key(hkv):
+    wl = synth.workload(2, ctx=300)
+    k, _ = wl.prefill(0, 150)
+    k = np.ascontiguousarray(k[:, :hkv])
+    khat = torch.empty(k.shape, dtype=torch.int16, device="cuda")
+    norm = torch.empty(k.shape[0], hkv, dtype=torch.int16, device="cuda")
+    ok.rotate_scale(dev_u16(k), wl.cfg.dtype, ok.ROT_KEY, norm_scope=ok.NORM_HEAD,
+                    khat_out=khat, norm_out=norm)
+    torch.cuda.synchronize()
+    wk, wn = oracle.rotate_scale_key(k, wl.cfg.dtype, oracle.NORM_HEAD)
+    assert_same_bits(host_u16(norm), wn, "norm")
+    assert_same_bits(host_u16(khat), wk, "k_hat")
+
+
+def test_head_scope_quant_pack():
+    nb, hkv = 3, 8
+    wl = synth.workload(2, ctx=32 * nb + 10)
+    k, v = wl.prefill(0, 32 * nb)
+    khat, knorm = oracle.rotate_scale_key(k, synth.BF16, oracle.NORM_HEAD)
+    v16 = oracle.in_to_f16(v, synth.BF16)
+    rec = torch.zeros(nb, hkv, 3072, dtype=torch.uint8, device="cuda")
+    nrm = torch.zeros(nb, hkv, 32, dtype=torch.int16, device="cuda")
+    ok.quant_pack(dev_u16(khat), dev_u16(knorm), dev_u16(v16), rec, nrm, norm_scope=ok.NORM_HEAD)
+    torch.cuda.synchronize()
+    wr, wn = oracle.quant_pack(khat, knorm, v16, norm_scope=oracle.NORM_HEAD)
+    assert_same_bits(rec.cpu().numpy(), wr, "records")
+    assert_same_bits(host_u16(nrm), wn, "norms")
+
+
+@pytest.mark.parametrize("hkv", [8, 16])
+def test_head_scope_cache_and_attention(hkv):
+    """Bulk prefill, appends across block flushes and decode attention (both
+    kernels) in HEAD scope; 16 KV heads take the 1024-thread prefill."""
+    base = synth.workload(1, ctx=700)
+    if hkv == 8:
+        wl = base
+    else:
+        cfg = synth.Config("hkv16", 1, 32, 16, 700, synth.BF16, 0.3, (4, 4), 1)
+        wl = synth.Workload(cfg, 57, [700], (base.outlier_idx * 2)[:16])
+    pr = Pair(wl, max_ctx=760, norm_scope=ok.NORM_HEAD)
+    k, v = wl.prefill(0, 640)
+    pr.prefill(0, k, v)
+    pr.compare_state()
+    for kn, vn, q in wl.steps(45):
+        pr.append(kn, vn)
+    pr.compare_state()
+    want, wlse = pr.orc.decode_attn(oracle.rotate_query(q, wl.cfg.dtype))
+    for var in VARIANTS:
+        got, glse = pr.attend(q, variant=var, splits=3)
+        assert np.abs(got - want).max() <= ATOL, var
+        assert np.abs(glse - wlse).max() <= 1e-3 * max(1.0, np.abs(wlse).max())

@@ -197,3 +197,68 @@ def test_empty_sequence(orc):
     c = orc.OracleCache(1, 4, 1, 4)
     out, lse = c.decode_attn(np.zeros((1, 4, 128), np.float32))
     assert not out.any() and np.all(np.isneginf(lse))
+
+
+# ---------------------------------------------------------------- HEAD scope
+def test_head_scope_equals_token_scope_at_one_kv_head(orc):
+    """With one KV head the two norm scopes compute the same norm: every cache
+    byte and the attention output agree."""
+    wl = synth.workload(0, ctx=400)
+    caches = []
+    for scope in (orc.NORM_TOKEN, orc.NORM_HEAD):
+        c = _cache(orc, wl, norm_scope=scope)
+        k, v = wl.prefill(0, 333)
+        c.prefill(0, k, v, wl.cfg.dtype)
+        for kn, vn, q in wl.steps(40):
+            c.append(kn, vn, wl.cfg.dtype)
+        caches.append((c, c.decode_attn(orc.rotate_query(q, wl.cfg.dtype))))
+    (a, (oa, la)), (b, (ob, lb)) = caches
+    assert np.array_equal(a.pool, b.pool) and np.array_equal(a.res_k, b.res_k)
+    assert np.array_equal(a.pool_norm.ravel(), b.pool_norm.ravel())
+    assert np.array_equal(a.res_norm.ravel(), b.res_norm.ravel())
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_head_scope_rows_use_each_heads_own_norm(orc):
+    """HEAD scope, 8 KV heads of very different scales: a window row is
+    n_{t,h} * k_hat_{t,h} with both from the per-head rotate+scale, and a
+    quantized row lies within half a step of it (x its norm)."""
+    wl = synth.workload(1, ctx=300)
+    c = _cache(orc, wl, norm_scope=orc.NORM_HEAD)
+    k, v = wl.prefill(0, 290)
+    scale = np.float32([1, 8, 0.125, 2, 0.5, 4, 1, 16])[None, :, None]
+    k = synth.to_bf16_bits(synth.bits_to_f32(k, wl.cfg.dtype) * scale)
+    dt = wl.cfg.dtype
+    c.prefill(0, k, v, dt)
+    khat, norm = orc.rotate_scale_key(k, dt, orc.NORM_HEAD)
+    assert norm.shape == (290, 8)
+    for t in list(range(0, c.q(0), 11)) + list(range(c.q(0), c.n(0), 7)):
+        for h in range(wl.cfg.hkv):
+            row = c.key_row(0, h, t)
+            nn = float(norm[t, h:h + 1].view(np.float16)[0])
+            kh = khat[t, h].view(np.float16).astype(np.float64)
+            if t >= c.q(0):
+                assert np.array_equal(row, nn * kh)
+                continue
+            p = c.block_table[0, t // 32]
+            d16 = c.pool[p, h, 2048:2304].view(np.float16).astype(np.float64)
+            assert np.all(np.abs(row - nn * kh) <= nn * (0.5 * d16 * (1 + 2e-3)) + 1e-12)
+
+
+@pytest.mark.parametrize("n", [33, 161, 700])
+def test_head_scope_attention_equals_library_sdpa(orc, n):
+    wl = synth.workload(1, ctx=n)
+    c = _cache(orc, wl, norm_scope=orc.NORM_HEAD)
+    dt = wl.cfg.dtype
+    k, v = wl.prefill(0)
+    c.prefill(0, k, v, dt)
+    kn, vn, q = next(wl.steps(1))
+    c.append(kn, vn, dt)
+    qr = orc.rotate_query(q, dt)
+    out, _ = c.decode_attn(qr)
+    hq, hkv = wl.cfg.hq, wl.cfg.hkv
+    heads = [0, 9, 31]
+    K = np.stack([np.stack([c.key_row(0, i // (hq // hkv), t) for t in range(n)]) for i in heads])
+    V = np.stack([np.stack([c.value_row(0, i // (hq // hkv), t) for t in range(n)]) for i in heads])
+    ref = _sdpa64(qr[0, heads].astype(np.float64), K, V)
+    assert np.abs(out[0, heads] - ref).max() < 1e-6
