@@ -54,14 +54,16 @@ def counter_traffic():
     return kib * 1024.0
 
 
-def algorithmic_bytes(n: int, Q: int, hq: int, hkv: int) -> int:
+def algorithmic_bytes(n: int, Q: int, hq: int, hkv: int, head_norm: bool = False) -> int:
     """Bytes one decode_attn launch must move for one sequence: each INT2
-    (block, KV head) record (3072 B) + 64 B of token norms per block, each
-    fp16 window token (256 B K + 256 B V per KV head + 2 B norm), the bf16
-    query and the fp32 output."""
+    (block, KV head) record (3072 B) + the block's token norms (64 B, or 64 B
+    per KV head in HEAD scope), each fp16 window token (256 B K + 256 B V per
+    KV head + 2 B norm, per KV head in HEAD scope), the bf16 query and the
+    fp32 output."""
     nb = Q // 32
     r = n - Q
-    return nb * (hkv * 3072 + 64) + r * (hkv * 512 + 2) + hq * 128 * 2 + hq * 128 * 4
+    nh = hkv if head_norm else 1
+    return nb * (hkv * 3072 + 64 * nh) + r * (hkv * 512 + 2 * nh) + hq * 128 * 2 + hq * 128 * 4
 
 
 def parse():
@@ -76,6 +78,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="query heads of the oracle sample (scaled to all heads)")
+    ap.add_argument("--head-norm", action="store_true",
+                    help="HEAD norm scope (a norm per token and KV head) instead of TOKEN")
     ap.add_argument("--batch48", action="store_true",
                     help="instead of the headline run: the batched workload (48 ragged "
                          "sequences of 8K..32K tokens, every one of 36 layer caches resident), "
@@ -107,7 +111,8 @@ def cpu_baseline(wl, k, v, steps, hq, args):
     import oracle
     cfg = wl.cfg
     mb = (args.ctx + 4096) // 32
-    orc = oracle.OracleCache(1, cfg.hq, cfg.hkv, mb, mb)
+    orc = oracle.OracleCache(1, cfg.hq, cfg.hkv, mb, mb,
+                             norm_scope=oracle.NORM_HEAD if args.head_norm else oracle.NORM_TOKEN)
     orc.prefill(0, k, v, cfg.dtype)
     kn, vn, q = steps[0]
     t0 = time.perf_counter()
@@ -272,7 +277,8 @@ def main():
     n_steps_total = args.warmup + args.steps
     max_ctx = args.ctx + n_steps_total + 64
     mb = (max_ctx + 31) // 32
-    geom = ok.make_geom(1, cfg.hq, cfg.hkv, mb, mb)
+    geom = ok.make_geom(1, cfg.hq, cfg.hkv, mb, mb,
+                        norm_scope=ok.NORM_HEAD if args.head_norm else ok.NORM_TOKEN)
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
@@ -344,7 +350,7 @@ def main():
     attn_us = float(np.mean(attn_ms)) * 1000.0
     n_mid = n0 + 1 + args.steps // 2
     q_mid = 32 * ((max(0, n_mid - 128) + 31) // 32)
-    bytes_attn = algorithmic_bytes(n_mid, q_mid, cfg.hq, cfg.hkv)
+    bytes_attn = algorithmic_bytes(n_mid, q_mid, cfg.hq, cfg.hkv, args.head_norm)
     achieved = bytes_attn / (attn_us * 1e-6) / 1e9
     res = {
         "metric": "INT2 decode-attn µs/step, ctx tokens/s & % HBM peak; 128K ctx bs1, 16K bs48",
@@ -363,13 +369,14 @@ def main():
         "config": {"workload": "qwen3-8b-shape decode, 128K ctx, batch 1",
                    "batch": 1, "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv,
                    "head_dim": 128, "ctx_first_step": args.ctx, "layers_cycled": L,
-                   "splits": S, "variant": args.variant},
+                   "splits": S, "variant": args.variant,
+                   "norm_scope": "head" if args.head_norm else "token"},
         "us_per_layer_step": us_per_layer,
         "attn_us": attn_us,
         "append_plus_gaps_us": us_per_layer - attn_us,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counter_traffic(),
+                     "traffic": None if args.head_norm else counter_traffic(),
                      "kernel": "decode_attn (split-K attention + LSE reduce, timed together)",
                      "algorithmic_bytes": bytes_attn},
         "prefill_ms_per_layer": float(np.median(pre_ms)),
