@@ -44,7 +44,7 @@ class Cache(ctypes.Structure):
         ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
         ("num_kv_heads", ctypes.c_int32), ("norm_scope", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32),
-        ("num_physical_blocks", ctypes.c_int32),
+        ("num_physical_blocks", ctypes.c_int32), ("flush_tokens", ctypes.c_int32),
         ("pool", ctypes.c_void_p), ("pool_norm", ctypes.c_void_p),
         ("res_k", ctypes.c_void_p), ("res_v", ctypes.c_void_p),
         ("res_norm", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
@@ -55,7 +55,8 @@ class Cache(ctypes.Structure):
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        src_time = max(os.path.getmtime(SRC), os.path.getmtime(os.path.join(HERE, "oscar_oracle.h")))
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < src_time:
             build()
         L = ctypes.CDLL(LIB)
         vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -189,7 +190,7 @@ class OracleCache:
 
     def __init__(self, batch: int, hq: int, hkv: int, max_blocks: int,
                  num_phys: int | None = None, norm_scope: int = NORM_TOKEN,
-                 block_table: np.ndarray | None = None):
+                 block_table: np.ndarray | None = None, flush_tokens: int = 32):
         self.batch, self.hq, self.hkv = batch, hq, hkv
         self.norm_scope = norm_scope
         self.max_blocks = max_blocks
@@ -208,7 +209,9 @@ class OracleCache:
         self.block_table = np.ascontiguousarray(block_table, dtype=np.int32)
         self.seq_state = np.zeros((batch, 2), np.int32)
         self.error_flag = np.zeros(1, np.int32)
-        self._s = Cache(batch, hq, hkv, norm_scope, max_blocks, self.num_phys,
+        assert flush_tokens in (32, 128)
+        self.flush_tokens = flush_tokens
+        self._s = Cache(batch, hq, hkv, norm_scope, max_blocks, self.num_phys, flush_tokens,
                         _p(self.pool), _p(self.pool_norm), _p(self.res_k),
                         _p(self.res_v), _p(self.res_norm), _p(self.block_table),
                         _p(self.seq_state), _p(self.error_flag))

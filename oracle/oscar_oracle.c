@@ -378,6 +378,10 @@ void orc_quant_pack(const uint16_t *khat, const uint16_t *knorm,
  * Reading taken: capacity 128, and an append that finds the window full
  * (n - Q == 128) first quantizes its oldest 32 tokens as block Q/32, then
  * stores the new token.  Hence Q(n) = 32*ceil(max(0, n - 128)/32).
+ * Variant flush_tokens = 128 (the popular-science article's wording, 三:
+ * the full window is quantized as one batch): the full window's 128 tokens
+ * become blocks Q/32 .. Q/32 + 3 at once, so Q(n) = 128*floor((n-1)/128)
+ * for n > 128.  Every block holds the same bytes in both variants.
  * A block index beyond the block table's capacity sets bit 1 of the error
  * flag and drops the append (state unchanged).
  */
@@ -428,12 +432,14 @@ void orc_append_one(orc_cache *c, int b, const uint16_t *k_tok,
     int n = st[0], Q = st[1];
     const int hkv = c->num_kv_heads;
     if (n - Q == ORC_R) {
-        if (Q / ORC_G >= c->max_blocks_per_seq) {
+        const int nf = c->flush_tokens == ORC_R ? ORC_R : ORC_G;   /* tokens per flush */
+        if ((Q + nf) / ORC_G > c->max_blocks_per_seq) {
             *c->error_flag |= 1;
             return;
         }
-        flush_block(c, b, Q);
-        Q += ORC_G;
+        for (int q = Q; q < Q + nf; q += ORC_G)
+            flush_block(c, b, q);
+        Q += nf;
     }
     int slot = n % ORC_R;
     uint16_t *khat = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)hkv * ORC_D);

@@ -50,6 +50,7 @@ enum {
 typedef struct {
     int32_t batch, num_q_heads, num_kv_heads, norm_scope;
     int32_t max_blocks_per_seq, num_physical_blocks;
+    int32_t flush_tokens;   /* tokens quantized per flush: 32 (one block) or 128 */
     uint8_t *pool;          /* [num_physical_blocks][Hkv][3072] */
     uint16_t *pool_norm;    /* TOKEN: [num_physical_blocks][32]; HEAD: [..][Hkv][32] */
     uint16_t *res_k;        /* [B][Hkv][128 slots][128] fp16 */

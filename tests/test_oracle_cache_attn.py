@@ -262,3 +262,64 @@ def test_head_scope_attention_equals_library_sdpa(orc, n):
     V = np.stack([np.stack([c.value_row(0, i // (hq // hkv), t) for t in range(n)]) for i in heads])
     ref = _sdpa64(qr[0, heads].astype(np.float64), K, V)
     assert np.abs(out[0, heads] - ref).max() < 1e-6
+
+
+# ---------------------------------------------------------------- 128-token flush
+def q_closed_form_128(n):
+    return 128 * ((n - 1) // 128) if n > 128 else 0
+
+
+@pytest.mark.parametrize("n", [1, 127, 128, 129, 200, 256, 257, 385, 600])
+def test_flush128_quantized_count_closed_form(orc, n):
+    wl = synth.workload(0, ctx=n + 1)
+    c = _cache(orc, wl, flush_tokens=128)
+    k, v = wl.prefill(0, n)
+    c.prefill(0, k, v, wl.cfg.dtype)
+    assert c.n(0) == n and c.q(0) == q_closed_form_128(n)
+    assert 1 <= n - c.q(0) <= 128
+
+
+def test_flush128_blocks_equal_one_block_flushes(orc):
+    """The same tokens through both flush sizes: every block quantized by
+    both holds the same record and norms; the window holds the last n - Q
+    tokens."""
+    wl = synth.workload(2, ctx=700, batch=2)
+    a = _cache(orc, wl)
+    b = _cache(orc, wl, flush_tokens=128)
+    dt = wl.cfg.dtype
+    for s_ in range(2):
+        k, v = wl.prefill(s_, 450 + 31 * s_)
+        a.prefill(s_, k, v, dt)
+        b.prefill(s_, k, v, dt)
+    for kn, vn, _ in wl.steps(70):
+        a.append(kn, vn, dt)
+        b.append(kn, vn, dt)
+    for s_ in range(2):
+        n = a.n(s_)
+        assert b.n(s_) == n and b.q(s_) == q_closed_form_128(n)
+        for j in range(min(a.q(s_), b.q(s_)) // 32):
+            p = a.block_table[s_, j]
+            assert np.array_equal(a.pool[p], b.pool[p]) and np.array_equal(a.pool_norm[p], b.pool_norm[p])
+        for t in range(b.q(s_), n):
+            for h in (0, 5):
+                assert np.array_equal(b.key_row(s_, h, t), a.key_row(s_, h, t)) or t < a.q(s_)
+                if t >= a.q(s_):
+                    assert np.array_equal(b.value_row(s_, h, t), a.value_row(s_, h, t))
+
+
+def test_flush128_attention_equals_library_sdpa(orc):
+    wl = synth.workload(0, ctx=300)
+    c = _cache(orc, wl, flush_tokens=128)
+    dt = wl.cfg.dtype
+    k, v = wl.prefill(0)
+    c.prefill(0, k, v, dt)
+    kn, vn, q = next(wl.steps(1))
+    c.append(kn, vn, dt)
+    n = c.n(0)
+    assert (n, c.q(0)) == (300, 256)
+    qr = orc.rotate_query(q, dt)
+    out, _ = c.decode_attn(qr)
+    hq, hkv = wl.cfg.hq, wl.cfg.hkv
+    K = np.stack([np.stack([c.key_row(0, i // (hq // hkv), t) for t in range(n)]) for i in range(hq)])
+    V = np.stack([np.stack([c.value_row(0, i // (hq // hkv), t) for t in range(n)]) for i in range(hq)])
+    assert np.abs(out[0] - _sdpa64(qr[0].astype(np.float64), K, V)).max() < 1e-6
