@@ -80,6 +80,9 @@ def parse():
                     help="query heads of the oracle sample (scaled to all heads)")
     ap.add_argument("--head-norm", action="store_true",
                     help="HEAD norm scope (a norm per token and KV head) instead of TOKEN")
+    ap.add_argument("--flush128", action="store_true",
+                    help="quantize the full 128-token window at once (four blocks) instead "
+                         "of one block per flush")
     ap.add_argument("--batch48", action="store_true",
                     help="instead of the headline run: the batched workload (48 ragged "
                          "sequences of 8K..32K tokens, every one of 36 layer caches resident), "
@@ -112,7 +115,8 @@ def cpu_baseline(wl, k, v, steps, hq, args):
     cfg = wl.cfg
     mb = (args.ctx + 4096) // 32
     orc = oracle.OracleCache(1, cfg.hq, cfg.hkv, mb, mb,
-                             norm_scope=oracle.NORM_HEAD if args.head_norm else oracle.NORM_TOKEN)
+                             norm_scope=oracle.NORM_HEAD if args.head_norm else oracle.NORM_TOKEN,
+                             flush_tokens=128 if args.flush128 else 32)
     orc.prefill(0, k, v, cfg.dtype)
     kn, vn, q = steps[0]
     t0 = time.perf_counter()
@@ -278,7 +282,8 @@ def main():
     max_ctx = args.ctx + n_steps_total + 64
     mb = (max_ctx + 31) // 32
     geom = ok.make_geom(1, cfg.hq, cfg.hkv, mb, mb,
-                        norm_scope=ok.NORM_HEAD if args.head_norm else ok.NORM_TOKEN)
+                        norm_scope=ok.NORM_HEAD if args.head_norm else ok.NORM_TOKEN,
+                        flush_tokens=128 if args.flush128 else 32)
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
@@ -349,7 +354,10 @@ def main():
     value = ctx_tokens / (total_ms / 1000.0)
     attn_us = float(np.mean(attn_ms)) * 1000.0
     n_mid = n0 + 1 + args.steps // 2
-    q_mid = 32 * ((max(0, n_mid - 128) + 31) // 32)
+    if args.flush128:
+        q_mid = 128 * ((n_mid - 1) // 128) if n_mid > 128 else 0
+    else:
+        q_mid = 32 * ((max(0, n_mid - 128) + 31) // 32)
     bytes_attn = algorithmic_bytes(n_mid, q_mid, cfg.hq, cfg.hkv, args.head_norm)
     achieved = bytes_attn / (attn_us * 1e-6) / 1e9
     res = {
@@ -370,13 +378,14 @@ def main():
                    "batch": 1, "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv,
                    "head_dim": 128, "ctx_first_step": args.ctx, "layers_cycled": L,
                    "splits": S, "variant": args.variant,
-                   "norm_scope": "head" if args.head_norm else "token"},
+                   "norm_scope": "head" if args.head_norm else "token",
+                   "flush_tokens": 128 if args.flush128 else 32},
         "us_per_layer_step": us_per_layer,
         "attn_us": attn_us,
         "append_plus_gaps_us": us_per_layer - attn_us,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if args.head_norm else counter_traffic(),
+                     "traffic": None if (args.head_norm or args.flush128) else counter_traffic(),
                      "kernel": "decode_attn (split-K attention + LSE reduce, timed together)",
                      "algorithmic_bytes": bytes_attn},
         "prefill_ms_per_layer": float(np.median(pre_ms)),

@@ -86,6 +86,9 @@ typedef struct {
                                     which sizes the two norm buffers below */
     int32_t max_blocks_per_seq;  /* block-table row length */
     int32_t num_physical_blocks; /* pool capacity */
+    int32_t flush_tokens;        /* tokens quantized when the window is full:
+                                    0 or 32 = one block (default), 128 = the
+                                    whole window as four blocks */
 } oscar_cache_geom;
 
 /* Cache buffers (device pointers, caller-owned).  Layout, per the record
@@ -171,10 +174,11 @@ OSCAR_API oscar_status oscar_quant_pack(const void *khat16, const void *knorm16,
 
 /* One decode-step append for every sequence (popular-science article, 三:
  * residual cache of the newest tokens in fp16, quantized a block at a time;
- * summary 论文图表 (c)).  Per sequence b with state {n, Q}:
- *   if n - Q == 128: quantize ring tokens Q..Q+31 into physical block
- *                    block_table[b][Q/32] (or set OSCAR_FLAG_CAPACITY and
- *                    drop the append if Q/32 >= max_blocks_per_seq); Q += 32;
+ * summary 论文图表 (c)).  Per sequence b with state {n, Q}, F = flush_tokens
+ * (32 by default, or 128):
+ *   if n - Q == 128: quantize ring tokens Q..Q+F-1 into physical blocks
+ *                    block_table[b][Q/32 ..] (or set OSCAR_FLAG_CAPACITY and
+ *                    drop the append if (Q+F)/32 > max_blocks_per_seq); Q += F;
  *   rotate+scale k_new[b], store k_hat, norm and fp16(v_new[b]) in slot
  *   n % 128; n += 1.
  *   k_new, v_new  device, [B][Hkv][128] fp16 or bf16.

@@ -40,7 +40,7 @@ class Geom(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("norm_scope", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
-                ("num_physical_blocks", ctypes.c_int32)]
+                ("num_physical_blocks", ctypes.c_int32), ("flush_tokens", ctypes.c_int32)]
 
 
 class CacheBufs(ctypes.Structure):
@@ -109,9 +109,9 @@ def _stream(stream=None):
 
 
 def make_geom(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, num_physical_blocks,
-              norm_scope=NORM_TOKEN, head_dim=HEAD_DIM) -> Geom:
+              norm_scope=NORM_TOKEN, head_dim=HEAD_DIM, flush_tokens=32) -> Geom:
     return Geom(batch, num_q_heads, num_kv_heads, head_dim, norm_scope, max_blocks_per_seq,
-                num_physical_blocks)
+                num_physical_blocks, flush_tokens)
 
 
 def cache_layout(geom: Geom) -> CacheSizes:

@@ -33,6 +33,7 @@ oscar_status check_geom(const oscar_cache_geom* g) {
   if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return OSCAR_EINVAL;
   if (g->max_blocks_per_seq < 1 || g->num_physical_blocks < 1) return OSCAR_EINVAL;
   if (g->norm_scope != OSCAR_NORM_TOKEN && g->norm_scope != OSCAR_NORM_HEAD) return OSCAR_EINVAL;
+  if (g->flush_tokens != 0 && g->flush_tokens != 32 && g->flush_tokens != 128) return OSCAR_EINVAL;
   return OSCAR_OK;
 }
 

@@ -208,7 +208,8 @@ struct CacheArgs {
   int hkv;
   int max_blocks;
   int nphys;
-  int head_norm;  // 1: a norm per (token, KV head) ([P][Hkv][32], [B][Hkv][128])
+  int head_norm;    // 1: a norm per (token, KV head) ([P][Hkv][32], [B][Hkv][128])
+  int flush_blocks;  // blocks quantized when the window is full: 1 or 4
 };
 // Token norm slots: TOKEN scope [P][32] and [B][128]; HEAD scope [P][Hkv][32]
 // and [B][Hkv][128].
@@ -256,101 +257,109 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
   }
 
   if (n - Q == kR) {
-    // The window is full: its 32 oldest tokens become block Q/32.
-    const int j = Q / kG;
-    if (j >= ca.max_blocks) {
+    // The window is full: its oldest 32 (one block) or 128 (four blocks)
+    // tokens become blocks Q/32 ..; every block id is checked first, so a
+    // flush happens whole or not at all.
+    const int nfb = ca.flush_blocks, j0 = Q / kG;
+    if (j0 + nfb > ca.max_blocks) {
       if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_CAPACITY));
       return;
     }
-    const int p = ca.block_table[static_cast<size_t>(b) * ca.max_blocks + j];
-    if (p < 0 || p >= ca.nphys) {
-      if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
-      return;
-    }
-    const int s0 = Q % kR;
-    for (int i = tid; i < (ca.head_norm ? hkv : 1) * 32; i += blockDim.x)
-      ca.pool_norm[pool_norm_at(ca, p, i >> 5, i & 31)] = ca.res_norm[res_norm_at(ca, b, i >> 5, s0 + (i & 31))];
-    const size_t bh0 = static_cast<size_t>(b) * hkv;
-    auto rec_of = [&](int h) { return ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec; };
-    // ranges: Key (head, channel) over the 32 ring tokens, Value (token,
-    // head, group) over 32 channels
-    const int nku = hkv * kD, nvu = 32 * hkv * 4;
-    for (int u = tid; u < nku + nvu; u += blockDim.x) {
-      float x[32];
-      if (u < nku) {
-        const int h = u >> 7, c = u & 127;
-        const uint16_t* rk = ca.res_k + ((bh0 + h) * kR + s0) * kD + c;
-#pragma unroll
-        for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(rk[t * kD]);
-        const Range r = range32(x);
-        fl_krd[u] = r.rdelta;
-        fl_kzm[u] = r.zm;
-        uint8_t* rec = rec_of(h);
-        reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(r.delta);
-        reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = static_cast<uint16_t>(r.zm);
-      } else {
-        // slot fastest across lanes: the window's Values are channel-major
-        const int w = u - nku, t = w & 31, h = (w >> 5) / 4, g = (w >> 5) & 3;
-        const uint16_t* rv = ca.res_v + ((bh0 + h) * kD + 32 * g) * kR + s0 + t;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) x[i] = f16_to_f32(rv[static_cast<size_t>(i) * kR]);
-        const Range r = range32(x);
-        const int pi = (t * hkv + h) * 4 + g;
-        fl_vrd[pi] = r.rdelta;
-        fl_vzm[pi] = r.zm;
-        reinterpret_cast<uint32_t*>(rec_of(h) + kRecVParam)[32 * g + t] =
-            static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
+    for (int i = 0; i < nfb; ++i) {
+      const int pi = ca.block_table[static_cast<size_t>(b) * ca.max_blocks + j0 + i];
+      if (pi < 0 || pi >= ca.nphys) {
+        if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
+        return;
       }
     }
-    __syncthreads();
-    // code words: Key unit (head, token, half), Value unit (head, octet,
-    // group, quarter), as in the bulk prefill
-    const int nkw = hkv * 64, nvw = hkv * 64;
-    for (int u = tid; u < nkw + nvw; u += blockDim.x) {
-      if (u < nkw) {
-        const int h = u / 64, t = (u >> 1) & 31, half = u & 1;
-        const uint4* kr = reinterpret_cast<const uint4*>(ca.res_k + ((bh0 + h) * kR + s0 + t) * kD + 64 * half);
-        uint32_t words[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint4 w8 = kr[q];
-          const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = 8 * q + e, c = 64 * half + i;
-            const uint16_t xh = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
-            const uint32_t code = code_zm(f16_to_f32(xh), fl_kzm[h * kD + c], fl_krd[h * kD + c]);
-            words[i >> 4] |= code << (2 * (i & 3) + 8 * ((i >> 2) & 3));
-          }
+    for (int fi = 0; fi < nfb; ++fi) {
+      const int p = ca.block_table[static_cast<size_t>(b) * ca.max_blocks + j0 + fi];
+      const int s0 = (Q + kG * fi) % kR;
+      for (int i = tid; i < (ca.head_norm ? hkv : 1) * 32; i += blockDim.x)
+        ca.pool_norm[pool_norm_at(ca, p, i >> 5, i & 31)] = ca.res_norm[res_norm_at(ca, b, i >> 5, s0 + (i & 31))];
+      const size_t bh0 = static_cast<size_t>(b) * hkv;
+      auto rec_of = [&](int h) { return ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec; };
+      // ranges: Key (head, channel) over the 32 ring tokens, Value (token,
+      // head, group) over 32 channels
+      const int nku = hkv * kD, nvu = 32 * hkv * 4;
+      for (int u = tid; u < nku + nvu; u += blockDim.x) {
+        float x[32];
+        if (u < nku) {
+          const int h = u >> 7, c = u & 127;
+          const uint16_t* rk = ca.res_k + ((bh0 + h) * kR + s0) * kD + c;
+  #pragma unroll
+          for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(rk[t * kD]);
+          const Range r = range32(x);
+          fl_krd[u] = r.rdelta;
+          fl_kzm[u] = r.zm;
+          uint8_t* rec = rec_of(h);
+          reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(r.delta);
+          reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = static_cast<uint16_t>(r.zm);
+        } else {
+          // slot fastest across lanes: the window's Values are channel-major
+          const int w = u - nku, t = w & 31, h = (w >> 5) / 4, g = (w >> 5) & 3;
+          const uint16_t* rv = ca.res_v + ((bh0 + h) * kD + 32 * g) * kR + s0 + t;
+  #pragma unroll
+          for (int i = 0; i < 32; ++i) x[i] = f16_to_f32(rv[static_cast<size_t>(i) * kR]);
+          const Range r = range32(x);
+          const int pi = (t * hkv + h) * 4 + g;
+          fl_vrd[pi] = r.rdelta;
+          fl_vzm[pi] = r.zm;
+          reinterpret_cast<uint32_t*>(rec_of(h) + kRecVParam)[32 * g + t] =
+              static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
         }
-        *reinterpret_cast<uint4*>(rec_of(h) + kRecKCodes + 32 * t + 16 * half) =
-            uint4{words[0], words[1], words[2], words[3]};
-      } else {
-        const int w = u - nkw, h = w / 64, oct = (w >> 4) & 3, d = (w >> 2) & 3, qt = w & 3;
-        uint32_t words[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = 32 * d + 16 * e + 4 * qt + i;
-            const uint4 w8 = *reinterpret_cast<const uint4*>(ca.res_v + ((bh0 + h) * kD + c) * kR + s0 + 8 * oct);
+      }
+      __syncthreads();
+      // code words: Key unit (head, token, half), Value unit (head, octet,
+      // group, quarter), as in the bulk prefill
+      const int nkw = hkv * 64, nvw = hkv * 64;
+      for (int u = tid; u < nkw + nvw; u += blockDim.x) {
+        if (u < nkw) {
+          const int h = u / 64, t = (u >> 1) & 31, half = u & 1;
+          const uint4* kr = reinterpret_cast<const uint4*>(ca.res_k + ((bh0 + h) * kR + s0 + t) * kD + 64 * half);
+          uint32_t words[4] = {0u, 0u, 0u, 0u};
+  #pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint4 w8 = kr[q];
             const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-              const int t = 8 * oct + kk, pi = (t * hkv + h) * 4 + d;
-              const int sk = (kk & 4) | ((kk & 1) << 1) | ((kk >> 1) & 1);
-              const uint16_t xh = static_cast<uint16_t>(ww[kk >> 1] >> (16 * (kk & 1)));
-              words[i] |= code_zm(f16_to_f32(xh), fl_vzm[pi], fl_vrd[pi]) << (2 * (8 * e + sk));
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int i = 8 * q + e, c = 64 * half + i;
+              const uint16_t xh = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
+              const uint32_t code = code_zm(f16_to_f32(xh), fl_kzm[h * kD + c], fl_krd[h * kD + c]);
+              words[i >> 4] |= code << (2 * (i & 3) + 8 * ((i >> 2) & 3));
             }
           }
+          *reinterpret_cast<uint4*>(rec_of(h) + kRecKCodes + 32 * t + 16 * half) =
+              uint4{words[0], words[1], words[2], words[3]};
+        } else {
+          const int w = u - nkw, h = w / 64, oct = (w >> 4) & 3, d = (w >> 2) & 3, qt = w & 3;
+          uint32_t words[4] = {0u, 0u, 0u, 0u};
+  #pragma unroll
+          for (int e = 0; e < 2; ++e) {
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int c = 32 * d + 16 * e + 4 * qt + i;
+              const uint4 w8 = *reinterpret_cast<const uint4*>(ca.res_v + ((bh0 + h) * kD + c) * kR + s0 + 8 * oct);
+              const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
+  #pragma unroll
+              for (int kk = 0; kk < 8; ++kk) {
+                const int t = 8 * oct + kk, pi = (t * hkv + h) * 4 + d;
+                const int sk = (kk & 4) | ((kk & 1) << 1) | ((kk >> 1) & 1);
+                const uint16_t xh = static_cast<uint16_t>(ww[kk >> 1] >> (16 * (kk & 1)));
+                words[i] |= code_zm(f16_to_f32(xh), fl_vzm[pi], fl_vrd[pi]) << (2 * (8 * e + sk));
+              }
+            }
+          }
+          uint8_t* rec = rec_of(h) + kRecVCodes;
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint32_t*>(rec + 16 * (16 * oct + 4 * qt + i) + 4 * d) = words[i];
         }
-        uint8_t* rec = rec_of(h) + kRecVCodes;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<uint32_t*>(rec + 16 * (16 * oct + 4 * qt + i) + 4 * d) = words[i];
       }
+      __syncthreads();  // the next block reuses the LDS ranges
     }
-    Q += kG;
+    Q += kG * nfb;
   }
 
   // Rotate + scale the new token; store it in slot n % 128.
@@ -650,6 +659,7 @@ CacheArgs make_args(const oscar_cache_geom* g, const oscar_cache* c) {
   a.max_blocks = g->max_blocks_per_seq;
   a.nphys = g->num_physical_blocks;
   a.head_norm = g->norm_scope == OSCAR_NORM_HEAD ? 1 : 0;
+  a.flush_blocks = g->flush_tokens == 128 ? 4 : 1;
   return a;
 }
 
@@ -700,8 +710,11 @@ extern "C" oscar_status oscar_prefill_quantize(const oscar_cache_geom* geom,
   if (!k || !v || n_tokens < 0 || seq < 0 || seq >= geom->batch) return OSCAR_EINVAL;
   if (!aligned(k, 16) || !aligned(v, 16)) return OSCAR_EINVAL;
   if (dtype != OSCAR_FP16 && dtype != OSCAR_BF16) return OSCAR_EINVAL;
-  // Q(n) = 32 * ceil(max(0, n - 128) / 32): the state n appends would leave.
-  const int Qb = ((n_tokens > kR ? n_tokens - kR : 0) + 31) / 32;
+  // The state n appends would leave: Q(n) = 32 * ceil(max(0, n - 128) / 32)
+  // with one-block flushes, 128 * floor((n - 1) / 128) (n > 128) with
+  // 128-token flushes.
+  const int Qb = geom->flush_tokens == 128 ? (n_tokens > kR ? 4 * ((n_tokens - 1) / kR) : 0)
+                                           : ((n_tokens > kR ? n_tokens - kR : 0) + 31) / 32;
   if (Qb > geom->max_blocks_per_seq) return OSCAR_EINVAL;
   st = check_device();
   if (st != OSCAR_OK) return st;

@@ -361,3 +361,47 @@ def test_head_scope_cache_and_attention(hkv):
         got, glse = pr.attend(q, variant=var, splits=3)
         assert np.abs(got - want).max() <= ATOL, var
         assert np.abs(glse - wlse).max() <= 1e-3 * max(1.0, np.abs(wlse).max())
+
+
+# ---------------------------------------------------------------- 128-token flush
+# A full window is quantized as four blocks at once.
+
+@pytest.mark.parametrize("n", [1, 128, 129, 300, 385])
+def test_flush128_prefill_equals_appends(n):
+    wl = synth.workload(1, ctx=n + 1)
+    pr = Pair(wl, max_ctx=n + 160, flush_tokens=128)   # room for whole 128-token flushes
+    k, v = wl.prefill(0, n)
+    pr.prefill(0, k, v)
+    pr.compare_state()
+
+
+def test_flush128_appends_and_attention():
+    """Prefill, then appends across a four-block flush; both attention kernels."""
+    wl = synth.workload(1, ctx=400, batch=2)
+    pr = Pair(wl, max_ctx=560, flush_tokens=128)
+    for b, n in enumerate((300, 350)):
+        k, v = wl.prefill(b, n)
+        pr.prefill(b, k, v)
+    pr.compare_state()
+    for i, (kn, vn, q) in enumerate(wl.steps(140)):
+        pr.append(kn, vn)
+        if i in (83, 84, 139):
+            pr.compare_state()
+    want, _ = pr.orc.decode_attn(oracle.rotate_query(q, wl.cfg.dtype))
+    for var in VARIANTS:
+        got, _ = pr.attend(q, variant=var, splits=4)
+        assert np.abs(got - want).max() <= ATOL, var
+
+
+def test_flush128_capacity_drops_whole_flush():
+    """A block table with room for the prefill's four blocks and no more: the
+    next four-block flush sets the capacity flag and the append is dropped,
+    as in the oracle."""
+    wl = synth.workload(0, ctx=300)
+    pr = Pair(wl, max_ctx=130 + 64, flush_tokens=128)   # 4 blocks of room
+    k, v = wl.prefill(0, 256)
+    pr.prefill(0, k, v)
+    for kn, vn, _ in wl.steps(3):
+        pr.append(kn, vn)
+    pr.compare_state()
+    assert int(pr.gpu.error_flag.cpu()[0]) == ok.FLAG_CAPACITY
