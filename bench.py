@@ -83,6 +83,9 @@ def parse():
     ap.add_argument("--flush128", action="store_true",
                     help="quantize the full 128-token window at once (four blocks) instead "
                          "of one block per flush")
+    ap.add_argument("--q-standalone", action="store_true",
+                    help="rotate the query with its own oscar_rotate_scale launch and pass "
+                         "q' as fp32, instead of the rotation inside decode attention")
     ap.add_argument("--batch48", action="store_true",
                     help="instead of the headline run: the batched workload (48 ragged "
                          "sequences of 8K..32K tokens, every one of 36 layer caches resident), "
@@ -311,14 +314,22 @@ def main():
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty(1, cfg.hq, 128, dtype=torch.float32, device="cuda")
     lse = torch.empty(1, cfg.hq, dtype=torch.float32, device="cuda")
+    qrot = torch.empty(1, cfg.hq, 128, dtype=torch.float32, device="cuda")
     setup_s = time.perf_counter() - t0
+
+    def attend(c, i):
+        if args.q_standalone:
+            ok.rotate_scale(q_d[i], cfg.dtype, ok.ROT_QUERY, q_out=qrot)
+            ok.decode_attn(c, qrot, ok.FP32, out, lse, ws, max_ctx, S, args.variant)
+        else:
+            ok.decode_attn(c, q_d[i], cfg.dtype, out, lse, ws, max_ctx, S, args.variant)
 
     def step(i, ev=None, ev_layer=-1):
         for li, c in enumerate(caches):
             ok.append_kv(c, kn_d[i], vn_d[i], cfg.dtype)
             if li == ev_layer:
                 ev[0].record()
-            ok.decode_attn(c, q_d[i], cfg.dtype, out, lse, ws, max_ctx, S, args.variant)
+            attend(c, i)
             if li == ev_layer:
                 ev[1].record()
 
@@ -379,13 +390,15 @@ def main():
                    "head_dim": 128, "ctx_first_step": args.ctx, "layers_cycled": L,
                    "splits": S, "variant": args.variant,
                    "norm_scope": "head" if args.head_norm else "token",
-                   "flush_tokens": 128 if args.flush128 else 32},
+                   "flush_tokens": 128 if args.flush128 else 32,
+                   "query_rotation": "standalone" if args.q_standalone else "fused"},
         "us_per_layer_step": us_per_layer,
         "attn_us": attn_us,
         "append_plus_gaps_us": us_per_layer - attn_us,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if (args.head_norm or args.flush128) else counter_traffic(),
+                     "traffic": None if (args.head_norm or args.flush128 or args.q_standalone)
+                     else counter_traffic(),
                      "kernel": "decode_attn (split-K attention + LSE reduce, timed together)",
                      "algorithmic_bytes": bytes_attn},
         "prefill_ms_per_layer": float(np.median(pre_ms)),
