@@ -1,0 +1,131 @@
+"""Synthetic accuracy ablation of the Key path (test infrastructure, CPU only).
+
+Four ways to store Keys in INT2 with the same quantizer (per channel over
+32-token blocks, delta = (max - min)/3, zero = min):
+  kivi       the raw Key, no rotation, no scaling
+  rotation   the Hadamard-rotated Key (FHT-128 per head), no scaling
+  scaling    the raw Key divided by its token norm (over all heads)
+  oscar      rotated and scaled (the method: Canalized Rotation + Omni-Token
+             Scaling, summary "OScaR：…" 方法步骤详情 ① and ②)
+For each: the relative reconstruction error of every token's Key (all heads)
+and the relative error of attention outputs against unquantized fp64
+attention with the same queries (scaled to a score spread of 2.5) and exact
+Values.  The pages claim that rotation flattens
+outlier channels and scaling equalises token norms, so that 2-bit codes lose
+less; this measures it on the synthetic workloads.  Run: python -m oracle.ablation
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (BF16, D, FP16, NORM_TOKEN, fht128, quant_pack, rotate_scale_key)
+
+VARIANTS = ("kivi", "rotation", "scaling", "oscar")
+
+
+def _f16_bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _dequant_keys(rec: np.ndarray) -> np.ndarray:
+    """[nb, hkv, 3072] records -> [32 nb, hkv, 128] dequantized fp64 Keys."""
+    nb, hkv, _ = rec.shape
+    kb = rec[:, :, :1024].reshape(nb, hkv, 32, 32)              # [.., token, byte]
+    shifts = (2 * np.arange(4)).astype(np.uint8)
+    codes = (kb[..., None] >> shifts) & 3                        # [.., token, byte, 4]
+    codes = codes.reshape(nb, hkv, 32, 128).astype(np.float64)   # channel = 4 byte + i
+    delta = rec[:, :, 2048:2304].copy().view(np.float16).astype(np.float64)   # [nb, hkv, 128]
+    zero = rec[:, :, 2304:2560].copy().view(np.float16).astype(np.float64)
+    k = zero[:, :, None, :] + delta[:, :, None, :] * codes       # [nb, hkv, token, 128]
+    return k.transpose(0, 2, 1, 3).reshape(nb * 32, hkv, D)
+
+
+def _quantize(x16: np.ndarray) -> np.ndarray:
+    """Per-channel INT2 of [T, hkv, 128] fp16 bits (T a multiple of 32)."""
+    T, hkv, _ = x16.shape
+    ones = np.full(T, 0x3C00, np.uint16)
+    rec, _ = quant_pack(x16, ones, np.zeros_like(x16))
+    return _dequant_keys(rec)
+
+
+def reconstruct(k_bits: np.ndarray, dtype: int, variant: str):
+    """Keys [T, hkv, 128] (raw bits) -> (reference, reconstruction), both fp64
+    in the basis the variant stores (the rotation is orthogonal, so errors
+    and attention scores are the same in either basis)."""
+    k = (k_bits.astype(np.uint32) << 16).view(np.float32) if dtype == BF16 else \
+        k_bits.view(np.float16).astype(np.float32)
+    T, hkv, _ = k.shape
+    if variant in ("rotation", "oscar"):
+        ref = fht128(k).astype(np.float64)
+    else:
+        ref = k.astype(np.float64)
+    if variant == "oscar":
+        khat, norm = rotate_scale_key(k_bits, dtype, NORM_TOKEN)
+        n = norm.view(np.float16).astype(np.float64)
+        return ref, _quantize(khat) * n[:, None, None]
+    if variant == "scaling":
+        n = np.sqrt((ref.reshape(T, -1) ** 2).sum(1))
+        n16 = n.astype(np.float16).astype(np.float64)
+        x = np.where(n[:, None, None] > 0, ref / np.maximum(n, 1e-30)[:, None, None], 0.0)
+        return ref, _quantize(_f16_bits(x)) * n16[:, None, None]
+    return ref, _quantize(_f16_bits(ref))
+
+
+def attention_error(ref: np.ndarray, rec: np.ndarray, q: np.ndarray, v: np.ndarray) -> float:
+    """Relative error |o - o~| / |o| of attention outputs o = softmax(s) V,
+    averaged over KV heads and queries.  q [hkv, nq, 128] is rescaled per
+    query so that its exact scores have a standard deviation of 2.5 over the
+    tokens (the synthetic Keys' norms would otherwise make every softmax a
+    near one-hot argmax)."""
+    errs = []
+    for h in range(ref.shape[1]):
+        for z in q[h]:
+            s0 = ref[:, h] @ z / np.sqrt(D)
+            z = z * (2.5 / max(s0.std(), 1e-30))
+            outs = []
+            for K in (ref[:, h], rec[:, h]):
+                s = K @ z / np.sqrt(D)
+                p = np.exp(s - s.max())
+                outs.append(p @ v[:, h] / p.sum())
+            errs.append(np.linalg.norm(outs[0] - outs[1]) / max(np.linalg.norm(outs[0]), 1e-30))
+    return float(np.mean(errs))
+
+
+def run(workload, n_tokens: int, seed: int = 0) -> dict:
+    k_bits, _ = workload.prefill(0, n_tokens)
+    dtype = workload.cfg.dtype
+    rng = np.random.default_rng(seed)
+    hkv = workload.cfg.hkv
+    q = rng.standard_normal((hkv, 16, D))
+    v = rng.standard_normal((n_tokens, hkv, D))
+    res = {}
+    for var in VARIANTS:
+        ref, rec = reconstruct(k_bits, dtype, var)
+        if var in ("rotation", "oscar"):
+            qv = fht128(q.astype(np.float32)).astype(np.float64)   # the same rotation on q
+        else:
+            qv = q
+        num = np.sqrt(((ref - rec) ** 2).reshape(n_tokens, -1).sum(1))
+        den = np.sqrt((ref ** 2).reshape(n_tokens, -1).sum(1))
+        rel = num / np.maximum(den, 1e-30)
+        res[var] = {"rel_mean": float(rel.mean()), "rel_p99": float(np.percentile(rel, 99)),
+                    "attn_err": attention_error(ref, rec, qv, v)}
+    return res
+
+
+def main():
+    from int2_kv_cache_amd import synth
+    cases = [("tiny (1 KV head, 4 outlier channels, sigma 0.3)", synth.workload(0), 1024),
+             ("Qwen3-8B-shaped (8 KV heads, 4-8 outlier channels, sigma 0.4)", synth.workload(2, ctx=8193), 8192),
+             ("multimodal segments (x1 / x5 / x0.3, 0.1% at x30)", synth.workload(4, ctx=12289), 12288)]
+    for name, wl, n in cases:
+        print(name)
+        r = run(wl, n)
+        for var in VARIANTS:
+            x = r[var]
+            print("  %-9s Key rel. error mean %.4f  p99 %.4f  attention rel. error %.4f"
+                  % (var, x["rel_mean"], x["rel_p99"], x["attn_err"]))
+
+
+if __name__ == "__main__":
+    main()
