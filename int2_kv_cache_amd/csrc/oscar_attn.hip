@@ -314,9 +314,6 @@ __device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
 }
 __device__ __forceinline__ float h_lo(uint32_t x) { return f16_to_f32(static_cast<uint16_t>(x)); }
 __device__ __forceinline__ float h_hi(uint32_t x) { return f16_to_f32(static_cast<uint16_t>(x >> 16)); }
-__device__ __forceinline__ float h_at(const u32x4& v, int j) {
-  return (j & 1) ? h_hi(v[j >> 1]) : h_lo(v[j >> 1]);
-}
 
 // Low parts of a hi/lo split: fp16(w0 - hi.lo) into the low half and
 // fp16(w1 - hi.hi) into the high half, each from one fused mixed-precision
@@ -404,17 +401,6 @@ struct UnitOffs {
 // an offset past num_bytes reads zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, num_bytes, 0x00020000);
-}
-template <class T>
-__device__ __forceinline__ T ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  if constexpr (sizeof(T) == 16)
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-  else if constexpr (sizeof(T) == 8)
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-  else if constexpr (sizeof(T) == 4)
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-  else
-    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
 }
 
 // One LDS stage of the record pipeline: the record's 3072 bytes, then its
@@ -694,7 +680,7 @@ void attn_mfma_kernel(AttnArgs A) {
       for (int j = 0; j < TPL; ++j) {
         const float pj = __builtin_amdgcn_exp2f(sv[j] - m_new);  // -inf gives 0
         Wpr[sm_head][sm_t0 + j] = pj;
-        ps += pj;
+        ps = j == 0 ? pj : ps + pj;
       }
     }
     if (!first && __any(grow)) {

@@ -135,9 +135,6 @@ __device__ __forceinline__ void scale_from_ss(float ss, float& norm, float& r) {
 }
 
 // Packed record layout (see include/oscar.h).
-__device__ __forceinline__ int kcode_bitpos(int t, int c) {   // bit index in K codes
-  return 8 * (32 * t + (c >> 2)) + 2 * (c & 3);
-}
 __device__ __forceinline__ int vcode_bitpos(int t, int c) {   // bit index in V codes
   const int slice = 16 * (t >> 3) + (c & 15), word = c >> 5, e = (c >> 4) & 1, k = t & 7;
   const int sk = (k & 4) | ((k & 1) << 1) | ((k >> 1) & 1);
