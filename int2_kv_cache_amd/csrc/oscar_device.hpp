@@ -13,6 +13,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 namespace oscar {
@@ -51,17 +53,44 @@ __device__ __forceinline__ float in_to_f32(uint16_t x, int is_bf16) {
 // the same: the upper element of each pair gets (lower - upper), the lower
 // gets (lower + upper) ([SUM] 前置知识 on FHT; [POP] 二; [RN] §II Step One).
 // All 64 lanes must be active.
+// x of lane l ^ H (H a power of two below 64) without an LDS round trip:
+// quad permutes for 1 and 2, the swizzle unit's xor mode for 4..16, the
+// half-wave swap for 32.
+template <int H>
+__device__ __forceinline__ float lane_xor(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  if constexpr (H == 1) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  } else if constexpr (H == 2) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  } else if constexpr (H == 4 || H == 8 || H == 16) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(xi, 0x1F | (H << 10)));
+  } else {
+    static_assert(H == 32, "lane distance");
+    // swaps the upper half of the first copy with the lower half of the
+    // second: {lo, lo} and {hi, hi}
+    const auto p = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 32) ? p[0] : p[1]);
+  }
+}
+
 __device__ __forceinline__ void fht128_wave(float& a, float& b) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const float pa = __shfl_xor(a, h, 64);
-    const float pb = __shfl_xor(b, h, 64);
+  auto stage = [&](auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const float pa = lane_xor<h>(a);
+    const float pb = lane_xor<h>(b);
     const bool upper = (lane & h) != 0;
     a = upper ? (pa - a) : (a + pa);
     b = upper ? (pb - b) : (b + pb);
-  }
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 8>{});
+  stage(std::integral_constant<int, 16>{});
+  stage(std::integral_constant<int, 32>{});
   const float lo = a + b, hi = a - b;
   a = lo * kFhtScale;
   b = hi * kFhtScale;
@@ -74,11 +103,17 @@ __device__ __forceinline__ void fht128_wave(float& a, float& b) {
 __device__ __forceinline__ float wave_tree_sumsq(float a, float b) {
 #pragma clang fp contract(off)
   float sa = a * a, sb = b * b;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    sa = sa + __shfl_xor(sa, s, 64);
-    sb = sb + __shfl_xor(sb, s, 64);
-  }
+  auto level = [&](auto sc) {
+    constexpr int st = decltype(sc)::value;
+    sa = sa + lane_xor<st>(sa);
+    sb = sb + lane_xor<st>(sb);
+  };
+  level(std::integral_constant<int, 1>{});
+  level(std::integral_constant<int, 2>{});
+  level(std::integral_constant<int, 4>{});
+  level(std::integral_constant<int, 8>{});
+  level(std::integral_constant<int, 16>{});
+  level(std::integral_constant<int, 32>{});
   return sa + sb;
 }
 
