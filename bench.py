@@ -32,17 +32,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
-ATTN_SRC = os.path.join(ROOT, "int2_kv_cache_amd", "csrc", "oscar_attn.hip")
+# the decode-attention kernels and the headers they compile from
+ATTN_SRC = [os.path.join(ROOT, "int2_kv_cache_amd", "csrc", f)
+            for f in ("oscar_attn.hip", "oscar_device.hpp", "oscar_host.hpp")]
 PROFILE = os.path.join(ROOT, "profiles", "decode_attn_qwen3-8b-128k.md")
 
 
 def counter_traffic():
     """HBM bytes of one attention launch from the committed rocprofv3 counters
     (FETCH_SIZE / WRITE_SIZE, scaled by the same counters on a plain copy),
-    or None when the attention source has changed since they were taken."""
+    or None when the attention sources (kernel file and the headers it
+    includes) have changed since they were taken."""
     import hashlib
     try:
-        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+        h = hashlib.sha256()
+        for f in ATTN_SRC:
+            h.update(open(f, "rb").read())
+        src = h.hexdigest()[:16]
         line = [l for l in open(PROFILE) if l.startswith("counters:")][0]
     except (OSError, IndexError):
         return None
