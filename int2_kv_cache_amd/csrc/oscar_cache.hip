@@ -38,23 +38,6 @@ __device__ __forceinline__ Range range32(const float* x) {
   r.zm = static_cast<uint32_t>(f32_to_f16(mn)) | (static_cast<uint32_t>(f32_to_f16(mx)) << 16);
   return r;
 }
-// The code of x under a stored range (zero and max as fp16 bits, 1/delta),
-// without a per-element division: q1 = (x - zero) * (1/delta), with 1/delta
-// correctly rounded, is within 2^-20 of the correctly rounded quotient
-// (which is <= 3), so both round to the same integer unless q1 lies within
-// 2^-18 of a half integer; there the exact quotient decides.
-__device__ __forceinline__ uint32_t code_zm(float x, uint32_t zm, float rdelta) {
-#pragma clang fp contract(off)
-  if (!(rdelta > 0.0f)) return 0u;
-  const float zero = f16_to_f32(static_cast<uint16_t>(zm));
-  const float mx = f16_to_f32(static_cast<uint16_t>(zm >> 16));
-  const float a = x - zero;
-  const float q1 = a * rdelta;
-  float q = q1;
-  if (fabsf((q1 - floorf(q1)) - 0.5f) <= 0x1p-18f) q = __fdiv_rn(a, __fdiv_rn(mx - zero, 3.0f));
-  const float r = rintf(q);
-  return r < 0.0f ? 0u : (r > 3.0f ? 3u : static_cast<uint32_t>(r));
-}
 
 // The 32 codes of a range's own values, packed two bits each: channel or
 // token i at bits 2 (i & 15) of w[i >> 4].  q1 = (x - zero) * (1/delta) is
@@ -230,11 +213,9 @@ __device__ __forceinline__ bool state_ok(int n, int Q, int max_blocks) {
 __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16_t* __restrict__ k_new,
                                                       const uint16_t* __restrict__ v_new,
                                                       int is_bf16) {
-  // block flush: Key and Value ranges ((1/delta), zero|max) of the block
-  __shared__ float fl_krd[16 * kD];
-  __shared__ uint32_t fl_kzm[16 * kD];
-  __shared__ float fl_vrd[32 * 16 * 4];
-  __shared__ uint32_t fl_vzm[32 * 16 * 4];
+  // block flush: the Key and Value code images (Hkv <= 16)
+  __shared__ __attribute__((aligned(16))) uint32_t fl_img_k[16 * 2 * kD];
+  __shared__ __attribute__((aligned(16))) uint32_t fl_img_v[16 * 4 * kVImgRow];
   __shared__ float part[16];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int hkv = ca.hkv;
@@ -278,86 +259,54 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
       for (int i = tid; i < (ca.head_norm ? hkv : 1) * 32; i += blockDim.x)
         ca.pool_norm[pool_norm_at(ca, p, i >> 5, i & 31)] = ca.res_norm[res_norm_at(ca, b, i >> 5, s0 + (i & 31))];
       const size_t bh0 = static_cast<size_t>(b) * hkv;
-      auto rec_of = [&](int h) { return ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec; };
-      // ranges: Key (head, channel) over the 32 ring tokens, Value (token,
-      // head, group) over 32 channels
+      auto rec_of = [&](int hh) { return ca.pool + (static_cast<size_t>(p) * hkv + hh) * kRec; };
+      // ranges and codes, as in the bulk prefill: Key (head, channel) over
+      // the block's 32 window tokens, Value (token, head, group) over 32
+      // channels; the codes go to the LDS images
       const int nku = hkv * kD, nvu = 32 * hkv * 4;
       for (int u = tid; u < nku + nvu; u += blockDim.x) {
         float x[32];
+        uint32_t cw[2];
         if (u < nku) {
-          const int h = u >> 7, c = u & 127;
-          const uint16_t* rk = ca.res_k + ((bh0 + h) * kR + s0) * kD + c;
-  #pragma unroll
+          const int hh = u >> 7, c = u & 127;
+          const uint16_t* rk = ca.res_k + ((bh0 + hh) * kR + s0) * kD + c;
+#pragma unroll
           for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(rk[t * kD]);
           const Range r = range32(x);
-          fl_krd[u] = r.rdelta;
-          fl_kzm[u] = r.zm;
-          uint8_t* rec = rec_of(h);
+          uint8_t* rec = rec_of(hh);
           reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(r.delta);
           reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = static_cast<uint16_t>(r.zm);
+          codes32(x, r, cw);
+          fl_img_k[(2 * hh) * kD + c] = cw[0];
+          fl_img_k[(2 * hh + 1) * kD + c] = cw[1];
         } else {
           // slot fastest across lanes: the window's Values are channel-major
-          const int w = u - nku, t = w & 31, h = (w >> 5) / 4, g = (w >> 5) & 3;
-          const uint16_t* rv = ca.res_v + ((bh0 + h) * kD + 32 * g) * kR + s0 + t;
-  #pragma unroll
+          const int w = u - nku, t = w & 31, hh = (w >> 5) / 4, g = (w >> 5) & 3;
+          const uint16_t* rv = ca.res_v + ((bh0 + hh) * kD + 32 * g) * kR + s0 + t;
+#pragma unroll
           for (int i = 0; i < 32; ++i) x[i] = f16_to_f32(rv[static_cast<size_t>(i) * kR]);
           const Range r = range32(x);
-          const int pi = (t * hkv + h) * 4 + g;
-          fl_vrd[pi] = r.rdelta;
-          fl_vzm[pi] = r.zm;
-          reinterpret_cast<uint32_t*>(rec_of(h) + kRecVParam)[32 * g + t] =
+          reinterpret_cast<uint32_t*>(rec_of(hh) + kRecVParam)[32 * g + t] =
               static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
+          codes32(x, r, cw);
+          *reinterpret_cast<uint2*>(fl_img_v + (hh * 4 + g) * kVImgRow + 2 * t) = uint2{cw[0], cw[1]};
         }
       }
       __syncthreads();
-      // code words: Key unit (head, token, half), Value unit (head, octet,
-      // group, quarter), as in the bulk prefill
-      const int nkw = hkv * 64, nvw = hkv * 64;
-      for (int u = tid; u < nkw + nvw; u += blockDim.x) {
+      // the record's code words from the images
+      const int nkw = hkv * 32 * 8;
+      for (int u = tid; u < 2 * nkw; u += blockDim.x) {
         if (u < nkw) {
-          const int h = u / 64, t = (u >> 1) & 31, half = u & 1;
-          const uint4* kr = reinterpret_cast<const uint4*>(ca.res_k + ((bh0 + h) * kR + s0 + t) * kD + 64 * half);
-          uint32_t words[4] = {0u, 0u, 0u, 0u};
-  #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const uint4 w8 = kr[q];
-            const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
-  #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int i = 8 * q + e, c = 64 * half + i;
-              const uint16_t xh = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
-              const uint32_t code = code_zm(f16_to_f32(xh), fl_kzm[h * kD + c], fl_krd[h * kD + c]);
-              words[i >> 4] |= code << (2 * (i & 3) + 8 * ((i >> 2) & 3));
-            }
-          }
-          *reinterpret_cast<uint4*>(rec_of(h) + kRecKCodes + 32 * t + 16 * half) =
-              uint4{words[0], words[1], words[2], words[3]};
+          const int hh = u >> 8, t = (u >> 3) & 31, j = u & 7;
+          *reinterpret_cast<uint32_t*>(rec_of(hh) + kRecKCodes + 32 * t + 4 * j) =
+              key_word(fl_img_k + 2 * hh * kD, t, j);
         } else {
-          const int w = u - nkw, h = w / 64, oct = (w >> 4) & 3, d = (w >> 2) & 3, qt = w & 3;
-          uint32_t words[4] = {0u, 0u, 0u, 0u};
-  #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-  #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int c = 32 * d + 16 * e + 4 * qt + i;
-              const uint4 w8 = *reinterpret_cast<const uint4*>(ca.res_v + ((bh0 + h) * kD + c) * kR + s0 + 8 * oct);
-              const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
-  #pragma unroll
-              for (int kk = 0; kk < 8; ++kk) {
-                const int t = 8 * oct + kk, pi = (t * hkv + h) * 4 + d;
-                const int sk = (kk & 4) | ((kk & 1) << 1) | ((kk >> 1) & 1);
-                const uint16_t xh = static_cast<uint16_t>(ww[kk >> 1] >> (16 * (kk & 1)));
-                words[i] |= code_zm(f16_to_f32(xh), fl_vzm[pi], fl_vrd[pi]) << (2 * (8 * e + sk));
-              }
-            }
-          }
-          uint8_t* rec = rec_of(h) + kRecVCodes;
-  #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint32_t*>(rec + 16 * (16 * oct + 4 * qt + i) + 4 * d) = words[i];
+          const int w = u - nkw, hh = w >> 8, oct = (w >> 6) & 3, m = (w >> 2) & 15, d = w & 3;
+          *reinterpret_cast<uint32_t*>(rec_of(hh) + kRecVCodes + 16 * (16 * oct + m) + 4 * d) =
+              value_word(fl_img_v + 4 * hh * kVImgRow, oct, m, d);
         }
       }
-      __syncthreads();  // the next block reuses the LDS ranges
+      __syncthreads();  // the next block reuses the images
     }
     Q += kG * nfb;
   }
