@@ -275,8 +275,9 @@ def main():
         batch48(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
-              "(see DESIGN.md for how it would shard)", file=sys.stderr)
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode (it would "
+              "shard by KV head, sequence or context, each GPU running these kernels on its "
+              "share)", file=sys.stderr)
         sys.exit(2)
     import torch
 
