@@ -102,6 +102,26 @@ def parse():
     return ap.parse_args()
 
 
+def copy_ceiling_gbs(mib: int = 2048) -> float:
+    """Bandwidth of a plain device copy (reads + writes) of `mib` MiB: a
+    measured HBM ceiling to set the attention's rate beside the 8 TB/s peak."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    ev[1].record()
+    torch.cuda.synchronize()
+    gbs = 5 * 2 * n * 4 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
 def copy_probe(mib: int):
     """A plain device-to-device copy of known size, for calibrating the
     FETCH_SIZE / WRITE_SIZE counters against the attention kernel's."""
@@ -365,6 +385,7 @@ def main():
     assert flag == 0, "cache error flag %d" % flag
     n1, Q1 = int(st[0]), int(st[1])
 
+    copy_gbs = copy_ceiling_gbs()   # after the timed region
     ms_per_step = total_ms / args.steps
     us_per_layer = ms_per_step * 1000.0 / L
     # context tokens attended in the timed region (every layer, every step)
@@ -407,7 +428,9 @@ def main():
                      "traffic": None if (args.head_norm or args.flush128 or args.q_standalone)
                      else counter_traffic(),
                      "kernel": "decode_attn (split-K attention + LSE reduce, timed together)",
-                     "algorithmic_bytes": bytes_attn},
+                     "algorithmic_bytes": bytes_attn,
+                     "measured_copy_gbs": copy_gbs,
+                     "frac_of_measured_copy": achieved / copy_gbs},
         "prefill_ms_per_layer": float(np.median(pre_ms)),
         "prefill_tokens_per_s": (args.ctx - 1) / (float(np.median(pre_ms)) / 1000.0),
         "final_state": [n1, Q1],
