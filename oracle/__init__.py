@@ -83,6 +83,7 @@ def lib():
             "orc_value_row": (None, [vp, i32, i32, i32, vp]),
             "orc_decode_attn": (None, [vp, vp, vp, vp]),
             "orc_decode_attn_one": (None, [vp, vp, i32, i32, vp, vp]),
+            "orc_dense_attn": (None, [vp, vp, vp, i32, i32, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -90,6 +91,31 @@ def lib():
             fn.argtypes = args
         _lib = L
     return _lib
+
+
+def bf16_bits_to_f32(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> the fp32 values they denote (exact)."""
+    return (np.asarray(x, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def dense_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray):
+    """Unquantized fp64 decode attention of one sequence (the BF16 baseline).
+
+    q [Hq][128], k and v [n][Hkv][128], fp32 values (bf16 inputs converted
+    exactly with ``bf16_bits_to_f32``).  Returns out [Hq][128] fp32 and
+    lse [Hq] fp32.  The arithmetic is ``orc_dense_attn`` in oscar_oracle.c.
+    """
+    q = np.ascontiguousarray(q, np.float32)
+    k = np.ascontiguousarray(k, np.float32)
+    v = np.ascontiguousarray(v, np.float32)
+    hq = q.shape[0]
+    n, hkv = k.shape[0], k.shape[1]
+    assert q.shape == (hq, D) and k.shape == (n, hkv, D) and v.shape == k.shape
+    assert hq % hkv == 0
+    out = np.zeros((hq, D), np.float32)
+    lse = np.zeros(hq, np.float32)
+    lib().orc_dense_attn(_p(q), _p(k), _p(v), n, hq, hkv, _p(out), _p(lse))
+    return out, lse
 
 
 def _p(a: np.ndarray | None):

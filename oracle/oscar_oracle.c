@@ -586,3 +586,53 @@ void orc_decode_attn(const orc_cache *c, const float *qrot, float *out,
                                 out + ((size_t)b * c->num_q_heads + i) * ORC_D,
                                 lse ? lse + (size_t)b * c->num_q_heads + i : NULL);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Unquantized decode attention (the BF16 baseline)                          */
+/* ------------------------------------------------------------------------ */
+
+/* Plain decode attention over an unquantized cache: the BF16
+ * FlashDecoding-v2 baseline against which the summary's efficiency results
+ * (实验结果; 论文图表) and the popular-science article (四) measure the INT2
+ * kernel.  No rotation, no scaling, no quantization: for query head i and
+ * KV head h = i / (Hq/Hkv),
+ *     s_t = (q_i . k_t) / sqrt(128),  out = sum_t e^(s_t - max) v_t / sum_t e^(s_t - max),
+ *     lse = max + ln(sum_t e^(s_t - max)),
+ * everything in fp64.  q [Hq][128]; k, v [n][Hkv][128] (fp32 values, e.g.
+ * bf16 inputs converted exactly); out [Hq][128]; lse [Hq] or NULL.  n = 0
+ * gives zeros and lse = -inf. */
+void orc_dense_attn(const float *q, const float *k, const float *v, int n,
+                    int hq, int hkv, float *out, float *lse)
+{
+    const int grp = hq / hkv;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    for (int i = 0; i < hq; i++) {
+        const int h = i / grp;
+        const float *qi = q + (size_t)i * ORC_D;
+        double m = -INFINITY;
+        for (int t = 0; t < n; t++) {
+            const float *kt = k + ((size_t)t * hkv + h) * ORC_D;
+            double dot = 0.0;
+            for (int ch = 0; ch < ORC_D; ch++)
+                dot += (double)qi[ch] * (double)kt[ch];
+            s[t] = dot / sqrt((double)ORC_D);
+            if (s[t] > m)
+                m = s[t];
+        }
+        double acc[ORC_D], l = 0.0;
+        for (int ch = 0; ch < ORC_D; ch++)
+            acc[ch] = 0.0;
+        for (int t = 0; t < n; t++) {
+            const float *vt = v + ((size_t)t * hkv + h) * ORC_D;
+            const double p = exp(s[t] - m);
+            l += p;
+            for (int ch = 0; ch < ORC_D; ch++)
+                acc[ch] += p * (double)vt[ch];
+        }
+        for (int ch = 0; ch < ORC_D; ch++)
+            out[(size_t)i * ORC_D + ch] = n > 0 ? (float)(acc[ch] / l) : 0.0f;
+        if (lse)
+            lse[i] = n > 0 ? (float)(m + log(l)) : -INFINITY;
+    }
+    free(s);
+}

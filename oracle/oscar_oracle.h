@@ -116,6 +116,11 @@ void orc_decode_attn(const orc_cache *c, const float *qrot, float *out,
 void orc_decode_attn_one(const orc_cache *c, const float *qrot, int b, int i,
                          float *out, float *lse);
 
+/* unquantized decode attention of one sequence (the BF16 baseline), fp64:
+ * q [Hq][128], k and v [n][Hkv][128], out [Hq][128], lse [Hq] or NULL */
+void orc_dense_attn(const float *q, const float *k, const float *v, int n,
+                    int hq, int hkv, float *out, float *lse);
+
 #ifdef __cplusplus
 }
 #endif
