@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-bf16", action="store_true",
+                    help="skip the bf16 (unquantized) decode-attention baseline")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="query heads of the oracle sample (scaled to all heads)")
     ap.add_argument("--head-norm", action="store_true",
@@ -165,6 +167,63 @@ def cpu_baseline(wl, k, v, steps, hq, args):
             "cpu": platform.processor() or platform.machine()}
 
 
+def dense_bytes(ctxs, hq: int, hkv: int) -> int:
+    """Algorithmic bytes of one bf16 baseline call: every token's bf16 Key and
+    Value rows, the bf16 queries in and the fp32 outputs."""
+    return sum(int(n) * hkv * 128 * 2 * 2 for n in ctxs) + len(ctxs) * hq * 128 * (2 + 4)
+
+
+class DenseLeg:
+    """The BF16 baseline at the same shape: n_layers distinct bf16 caches
+    (written by oscar_dense_write_kv), then timed decode attention calls,
+    one event pair per call, cycling the layers."""
+
+    def __init__(self, ok, torch, geom, table, ctxs, n_layers):
+        self.ok, self.torch, self.geom = ok, torch, geom
+        self.ctxs = [int(n) for n in ctxs]
+        self.caches = [ok.DenseCache(geom, block_table=table) for _ in range(n_layers)]
+        for c in self.caches:
+            c.ctx_lens.copy_(torch.tensor(self.ctxs, dtype=torch.int32))
+
+    def write(self, b, k_dev, v_dev):
+        self.ok.dense_write_kv(self.caches[0], b, 0, k_dev, v_dev)
+
+    def replicate(self):
+        for c in self.caches[1:]:
+            c.k_pool.copy_(self.caches[0].k_pool)
+            c.v_pool.copy_(self.caches[0].v_pool)
+        self.torch.cuda.synchronize()
+
+    def time(self, q_list, calls, warm, splits, int2_attn_us):
+        ok, torch = self.ok, self.torch
+        g = self.geom
+        max_ctx = max(self.ctxs)
+        S, nbytes = ok.dense_workspace_bytes(g, max_ctx, splits)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        out = torch.empty(g.batch, g.num_q_heads, 128, dtype=torch.float32, device="cuda")
+        lse = torch.empty(g.batch, g.num_q_heads, dtype=torch.float32, device="cuda")
+        L = len(self.caches)
+        for i in range(warm):
+            ok.dense_decode_attn(self.caches[i % L], q_list[i % len(q_list)], out, lse, ws, max_ctx, S)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(calls)]
+        torch.cuda.synchronize()
+        for i in range(calls):
+            ev[i][0].record()
+            ok.dense_decode_attn(self.caches[i % L], q_list[i % len(q_list)], out, lse, ws, max_ctx, S)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        for c in self.caches:
+            assert int(c.error_flag.item()) == 0
+        us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1000.0
+        nb = dense_bytes(self.ctxs, g.num_q_heads, g.num_kv_heads)
+        ach = nb / (us * 1e-6) / 1e9
+        return {"kernel": "dense_decode_attn (bf16 split-K attention + LSE reduce)",
+                "attn_us": us, "algorithmic_bytes": nb, "achieved_gbs": ach,
+                "frac": ach / HBM_PEAK_GBS, "splits": S, "layers_cycled": L, "calls": calls,
+                "ctx": self.ctxs[0] if len(self.ctxs) == 1 else float(np.mean(self.ctxs)),
+                "int2_speedup": us / int2_attn_us}
+
+
 def batch48(args):
     """The batched decode workload: 48 sequences with contexts drawn from
     8K..32K (block-table indexed, blocks packed per sequence), 32/8 heads,
@@ -200,9 +259,16 @@ def batch48(args):
 
     t0 = time.perf_counter()
     c0 = ok.DeviceCache(geom, block_table=table)
+    dense = None
+    if not args.no_bf16:
+        dgeom = ok.make_geom(B, cfg.hq, cfg.hkv, mb, nphys)
+        dense = DenseLeg(ok, torch, dgeom, table, [n - 1 for n in wl.ctx_lens], 4)
     for b in range(B):
         k, v = wl.prefill(b)
-        ok.prefill_quantize(c0, b, dev(k), dev(v), cfg.dtype)
+        kd, vd = dev(k), dev(v)
+        ok.prefill_quantize(c0, b, kd, vd, cfg.dtype)
+        if dense is not None:
+            dense.write(b, kd, vd)
     torch.cuda.synchronize()
     print("batch48: prefilled %d sequences (%.1f s)" % (B, time.perf_counter() - t0),
           file=sys.stderr, flush=True)
@@ -280,6 +346,10 @@ def batch48(args):
         "cache_bytes_bf16_36_layers": bf16_bytes,
         "setup_s": setup_s,
     }
+    if dense is not None:
+        del caches, c0
+        dense.replicate()
+        res["bf16_baseline"] = dense.time(q_d, 20, 4, 0, attn_us)
     print(json.dumps(res), flush=True)
 
 
@@ -321,6 +391,14 @@ def main():
     t0 = time.perf_counter()
     k, v = wl.prefill(0)
     kd, vd = dev(k), dev(v)
+    dense = None
+    if not args.no_bf16:
+        # the bf16 baseline's caches: the same 131071 prefilled tokens, two
+        # layers (1.07 GB, beyond the 256 MB Infinity Cache)
+        dgeom = ok.make_geom(1, cfg.hq, cfg.hkv, mb, mb)
+        dense = DenseLeg(ok, torch, dgeom, None, [args.ctx - 1], 2)
+        dense.write(0, kd, vd)
+        dense.replicate()
     caches = []
     pre_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     pre_ms = []
@@ -436,6 +514,8 @@ def main():
         "final_state": [n1, Q1],
         "setup_s": setup_s,
     }
+    if dense is not None:
+        res["bf16_baseline"] = dense.time(q_d, args.steps, args.warmup, 0, attn_us)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, k, v, steps, cfg.hq, args)
     print(json.dumps(res), flush=True)

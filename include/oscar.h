@@ -225,6 +225,58 @@ OSCAR_API oscar_status oscar_decode_attn(const oscar_cache_geom *geom, const osc
                                void *workspace, size_t ws_bytes, int32_t num_splits,
                                int32_t max_ctx, oscar_attn_variant variant, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * The BF16 baseline: decode attention over an unquantized bf16 cache, the
+ * comparison point of the pages' efficiency results (summary "OScaR：…",
+ * 实验结果 and 论文图表: decode speed-up over BF16 FlashDecoding-v2 at long
+ * context; popular-science article, 四: batch-48 memory and throughput).
+ * Same split-K structure and log-sum-exp reduce as oscar_decode_attn; no
+ * rotation, scaling or quantization.  The geometry's norm_scope and
+ * flush_tokens are not used (any accepted value, e.g. 0, will do).
+ *
+ * Paged bf16 layout, per (physical block p, KV head h) of 32 tokens:
+ *   k_pool  [P][Hkv][32 tokens][128 channels] bf16 (P = num_physical_blocks)
+ *   v_pool  [P][Hkv][128 channels][32 tokens] bf16 (transposed per block)
+ * Token t of sequence b lives in block block_table[b][t / 32], row t % 32.
+ * ------------------------------------------------------------------------- */
+
+/* Write tokens start .. start + n_tokens - 1 of sequence `seq` into the bf16
+ * pools (a plain layout transform; the cache a model's attention layer would
+ * write).
+ *   k, v         device, [n_tokens][Hkv][128] bf16, 16-byte aligned.
+ *   k_pool, v_pool device, 256-byte aligned; block_table device [B][max_blocks].
+ *   error_flag   device int32: OSCAR_FLAG_BADSTATE for a block id outside
+ *                [0, num_physical_blocks) (that token is skipped).
+ * Errors: EINVAL (also when start + n_tokens > 32 * max_blocks_per_seq). */
+OSCAR_API oscar_status oscar_dense_write_kv(const oscar_cache_geom *geom, void *k_pool, void *v_pool,
+                                  const int32_t *block_table, int32_t seq, int32_t start,
+                                  const void *k, const void *v, int32_t n_tokens,
+                                  int32_t *error_flag, void *stream);
+
+/* Split count the bf16 kernel would pick for max_ctx (num_splits == 0) and
+ * the workspace bytes it needs with that split count. */
+OSCAR_API oscar_status oscar_dense_workspace_bytes(const oscar_cache_geom *geom, int32_t max_ctx,
+                                         int32_t num_splits, int32_t *splits_out,
+                                         size_t *bytes);
+
+/* out[b][i] = softmax(q[b][i] K_h^T / sqrt(128)) V_h over the ctx_lens[b]
+ * tokens of sequence b, h = i / (Hq/Hkv).
+ *   q          device, [B][Hq][128] bf16, 16-byte aligned (not rotated).
+ *   ctx_lens   device, [B] int32 tokens per sequence (0 gives zeros and
+ *              lse = -inf; above 32 * max_blocks_per_seq sets
+ *              OSCAR_FLAG_BADSTATE and attends to nothing).
+ *   out, lse, workspace, num_splits, max_ctx: as for oscar_decode_attn, with
+ *              the workspace from oscar_dense_workspace_bytes.
+ *   error_flag device int32 sticky bits: OSCAR_FLAG_BADSTATE for a block id
+ *              outside the pool (block 0 is read instead).
+ * Errors: EINVAL, EWORKSPACE, ELAUNCH. */
+OSCAR_API oscar_status oscar_dense_decode_attn(const oscar_cache_geom *geom, const void *k_pool,
+                                     const void *v_pool, const int32_t *block_table,
+                                     const int32_t *ctx_lens, const void *q, float *out,
+                                     float *lse, void *workspace, size_t ws_bytes,
+                                     int32_t num_splits, int32_t max_ctx, int32_t *error_flag,
+                                     void *stream);
+
 /* Static string for a status code. */
 OSCAR_API const char *oscar_status_str(oscar_status s);
 

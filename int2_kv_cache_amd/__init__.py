@@ -27,6 +27,7 @@ HEAD_DIM, BLOCK_TOKENS, RESIDUAL_TOKENS, RECORD_BYTES = 128, 32, 128, 3072
 
 API = ("oscar_cache_layout", "oscar_rotate_scale", "oscar_quant_pack", "oscar_append_kv",
        "oscar_prefill_quantize", "oscar_decode_workspace_bytes", "oscar_decode_attn",
+       "oscar_dense_write_kv", "oscar_dense_workspace_bytes", "oscar_dense_decode_attn",
        "oscar_status_str")
 
 
@@ -81,6 +82,11 @@ def lib() -> ctypes.CDLL:
                                                    P(ctypes.c_size_t)]
         L.oscar_decode_attn.argtypes = [P(Geom), P(CacheBufs), vp, st, vp, vp, vp,
                                         ctypes.c_size_t, i32, i32, st, vp]
+        L.oscar_dense_write_kv.argtypes = [P(Geom), vp, vp, vp, i32, i32, vp, vp, i32, vp, vp]
+        L.oscar_dense_workspace_bytes.argtypes = [P(Geom), i32, i32, P(ctypes.c_int32),
+                                                  P(ctypes.c_size_t)]
+        L.oscar_dense_decode_attn.argtypes = [P(Geom), vp, vp, vp, vp, vp, vp, vp, vp,
+                                              ctypes.c_size_t, i32, i32, vp, vp]
         for name in API:
             getattr(L, name).restype = ctypes.c_int
         L.oscar_status_str.restype = ctypes.c_char_p
@@ -194,3 +200,49 @@ def decode_attn(cache: DeviceCache, q, q_dtype: int, out, lse, workspace, max_ct
     _check("oscar_decode_attn", lib().oscar_decode_attn(
         ctypes.byref(cache.geom), ctypes.byref(cache.bufs), _ptr(q), q_dtype, _ptr(out),
         _ptr(lse), _ptr(workspace), nbytes, num_splits, max_ctx, variant, _stream(stream)))
+
+
+# ---------------------------------------------------------------- bf16 baseline
+
+class DenseCache:
+    """Paged bf16 cache of the baseline kernel as torch tensors on the current
+    device: k_pool [P][Hkv][32][128], v_pool [P][Hkv][128][32] (bf16 bit
+    patterns as int16), block_table [B][max_blocks], ctx_lens [B], error_flag."""
+
+    def __init__(self, geom: Geom, block_table=None, device="cuda"):
+        import torch
+        self.geom = geom
+        P, H, B = geom.num_physical_blocks, geom.num_kv_heads, geom.batch
+        self.k_pool = torch.zeros(P, H, BLOCK_TOKENS, HEAD_DIM, dtype=torch.int16, device=device)
+        self.v_pool = torch.zeros(P, H, HEAD_DIM, BLOCK_TOKENS, dtype=torch.int16, device=device)
+        if block_table is None:
+            block_table = torch.arange(B * geom.max_blocks_per_seq, dtype=torch.int32)
+            block_table = block_table.view(B, geom.max_blocks_per_seq) % P
+        self.block_table = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
+        self.ctx_lens = torch.zeros(B, dtype=torch.int32, device=device)
+        self.error_flag = torch.zeros(1, dtype=torch.int32, device=device)
+
+
+def dense_write_kv(cache: DenseCache, seq: int, start: int, k, v, stream=None):
+    """k, v: [n_tokens, Hkv, 128] bf16 bit patterns (int16/uint16 tensor)."""
+    _check("oscar_dense_write_kv", lib().oscar_dense_write_kv(
+        ctypes.byref(cache.geom), _ptr(cache.k_pool), _ptr(cache.v_pool), _ptr(cache.block_table),
+        seq, start, _ptr(k), _ptr(v), k.shape[0], _ptr(cache.error_flag), _stream(stream)))
+
+
+def dense_workspace_bytes(geom: Geom, max_ctx: int, num_splits: int = 0):
+    s = ctypes.c_int32(0)
+    nbytes = ctypes.c_size_t(0)
+    _check("oscar_dense_workspace_bytes", lib().oscar_dense_workspace_bytes(
+        ctypes.byref(geom), max_ctx, num_splits, ctypes.byref(s), ctypes.byref(nbytes)))
+    return s.value, nbytes.value
+
+
+def dense_decode_attn(cache: DenseCache, q, out, lse, workspace, max_ctx: int,
+                      num_splits: int = 0, stream=None):
+    """q: [B, Hq, 128] bf16 bit patterns; out [B, Hq, 128] fp32; lse [B, Hq] or None."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("oscar_dense_decode_attn", lib().oscar_dense_decode_attn(
+        ctypes.byref(cache.geom), _ptr(cache.k_pool), _ptr(cache.v_pool), _ptr(cache.block_table),
+        _ptr(cache.ctx_lens), _ptr(q), _ptr(out), _ptr(lse), _ptr(workspace), nbytes, num_splits,
+        max_ctx, _ptr(cache.error_flag), _stream(stream)))

@@ -1106,6 +1106,12 @@ size_t workspace_bytes(const oscar_cache_geom* g, int splits) {
   return n * sizeof(float2) + n * kD * sizeof(float) + 256;
 }
 
+void launch_lse_reduce(const float2* ws_ml, const float* ws_o, int hq, int batch, int splits,
+                       float* out, float* lse, hipStream_t st) {
+  hipLaunchKernelGGL(lse_reduce_kernel, dim3(hq, batch), dim3(256), 0, st, ws_ml, ws_o, hq, splits,
+                     out, lse);
+}
+
 template <int GRP>
 void launch_attn(const AttnArgs& A, dim3 grid, hipStream_t st, bool mfma) {
   if (mfma)
@@ -1181,7 +1187,6 @@ extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const os
   }
   st = launch_status();
   if (st != OSCAR_OK) return st;
-  hipLaunchKernelGGL(lse_reduce_kernel, dim3(geom->num_q_heads, geom->batch), dim3(256), 0, hs,
-                     A.ws_ml, A.ws_o, geom->num_q_heads, S, out, lse);
+  launch_lse_reduce(A.ws_ml, A.ws_o, geom->num_q_heads, geom->batch, S, out, lse, hs);
   return launch_status();
 }

@@ -27,4 +27,13 @@ inline oscar_status launch_status() {
 oscar_status check_geom(const oscar_cache_geom* g);
 oscar_status check_cache(const oscar_cache_geom* g, const oscar_cache* c);
 
+// Split-K partials of decode attention, shared by the INT2 and bf16 paths:
+// ws_ml [B][Hq][S] (m, l) with m in log2 units, ws_o [B][Hq][S][128]; the
+// workspace holds both (ws_o from the first 256-B boundary after ws_ml).
+size_t workspace_bytes(const oscar_cache_geom* g, int splits);
+// Merge the S partials of every (sequence, query head) into out [B][Hq][128]
+// and, if lse is not NULL, lse [B][Hq] (natural log).
+void launch_lse_reduce(const float2* ws_ml, const float* ws_o, int hq, int batch, int splits,
+                       float* out, float* lse, hipStream_t st);
+
 }  // namespace oscar
