@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--hw-rsqrt", action="store_true",
+                    help="Key scaling factor from the hardware rsqrt (OSCAR_SCALE_HW_RSQ)")
     ap.add_argument("--no-bf16", action="store_true",
                     help="skip the bf16 (unquantized) decode-attention baseline")
     ap.add_argument("--cpu-heads", type=int, default=8,
@@ -383,7 +385,8 @@ def main():
     mb = (max_ctx + 31) // 32
     geom = ok.make_geom(1, cfg.hq, cfg.hkv, mb, mb,
                         norm_scope=ok.NORM_HEAD if args.head_norm else ok.NORM_TOKEN,
-                        flush_tokens=128 if args.flush128 else 32)
+                        flush_tokens=128 if args.flush128 else 32,
+                        key_scale=ok.SCALE_HW_RSQ if args.hw_rsqrt else ok.SCALE_IEEE)
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
@@ -497,13 +500,15 @@ def main():
                    "splits": S, "variant": args.variant,
                    "norm_scope": "head" if args.head_norm else "token",
                    "flush_tokens": 128 if args.flush128 else 32,
-                   "query_rotation": "standalone" if args.q_standalone else "fused"},
+                   "query_rotation": "standalone" if args.q_standalone else "fused",
+                   "key_scale": "hw_rsq" if args.hw_rsqrt else "ieee"},
         "us_per_layer_step": us_per_layer,
         "attn_us": attn_us,
         "append_plus_gaps_us": us_per_layer - attn_us,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if (args.head_norm or args.flush128 or args.q_standalone)
+                     "traffic": None if (args.head_norm or args.flush128 or args.q_standalone
+                                         or args.hw_rsqrt)
                      else counter_traffic(),
                      "kernel": "decode_attn (split-K attention + LSE reduce, timed together)",
                      "algorithmic_bytes": bytes_attn,

@@ -63,7 +63,22 @@ typedef enum {
 
 typedef enum { OSCAR_FP16 = 0, OSCAR_BF16 = 1, OSCAR_FP32 = 2 } oscar_dtype;
 typedef enum { OSCAR_NORM_TOKEN = 0, OSCAR_NORM_HEAD = 1 } oscar_norm_scope;
-typedef enum { OSCAR_ROT_QUERY = 0, OSCAR_ROT_KEY = 1 } oscar_rot_mode;
+typedef enum {
+    OSCAR_ROT_QUERY = 0,
+    OSCAR_ROT_KEY = 1,
+    OSCAR_ROT_KEY_HW_RSQ = 2 /* KEY with the hardware reciprocal square root
+                                (see oscar_key_scale) */
+} oscar_rot_mode;
+/* How the Omni-Token Scaling factor r = 1/||y|| is computed from the sum of
+ * squares ss.  The popular-science article (三) replaces "L2 norm, then
+ * reciprocal" by one hardware reciprocal-square-root instruction. */
+typedef enum {
+    OSCAR_SCALE_IEEE = 0,  /* r = 1 / sqrt(ss), each correctly rounded: k_hat,
+                              norms and codes bit-exact with the reference */
+    OSCAR_SCALE_HW_RSQ = 1 /* r = v_rsq_f32(ss) (about 1 ulp): k_hat within one
+                              fp16 step of the IEEE result; the stored norm is
+                              still the correctly rounded sqrt(ss) */
+} oscar_key_scale;
 typedef enum {
     OSCAR_ATTN_AUTO = 0, /* the fastest kernel built (the MFMA one) */
     OSCAR_ATTN_VALU = 1, /* scalar-FMA dot products on the vector ALUs */
@@ -89,6 +104,8 @@ typedef struct {
     int32_t flush_tokens;        /* tokens quantized when the window is full:
                                     0 or 32 = one block (default), 128 = the
                                     whole window as four blocks */
+    int32_t key_scale;           /* oscar_key_scale used by append and prefill:
+                                    0 = IEEE (default), 1 = hardware rsqrt */
 } oscar_cache_geom;
 
 /* Cache buffers (device pointers, caller-owned).  Layout, per the record
@@ -143,8 +160,10 @@ OSCAR_API oscar_status oscar_cache_layout(const oscar_cache_geom *geom, oscar_ca
  *                    then x 1/sqrt(128)); khat_out, norm_out unused.
  *             KEY:   y = FHT(x) per head; ss = pairwise-tree sum of squares
  *                    over all heads (TOKEN) or per head (HEAD); khat_out
- *                    [n_tokens][n_heads][128] fp16 = fp16(y / sqrt(ss));
+ *                    [n_tokens][n_heads][128] fp16 = fp16(y * (1/sqrt(ss)));
  *                    norm_out fp16 [n_tokens] (TOKEN) or [n_tokens][n_heads].
+ *             KEY_HW_RSQ: KEY with 1/sqrt(ss) from the hardware instruction
+ *                    (OSCAR_SCALE_HW_RSQ).
  *   n_heads   >= 1 (QUERY), 1..16 (KEY: the norm spans all heads of a token).
  * Errors: EINVAL (null, n_tokens < 0, n_heads out of range, bad dtype). */
 OSCAR_API oscar_status oscar_rotate_scale(const void *x, oscar_dtype dtype, int32_t n_tokens,

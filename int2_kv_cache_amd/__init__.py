@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(PKG, "liboscar.so")
 OK, EINVAL, EUNSUPPORTED, ELAUNCH, EWORKSPACE = 0, 1, 2, 3, 4
 FP16, BF16, FP32 = 0, 1, 2
 NORM_TOKEN, NORM_HEAD = 0, 1
-ROT_QUERY, ROT_KEY = 0, 1
+ROT_QUERY, ROT_KEY, ROT_KEY_HW_RSQ = 0, 1, 2
+SCALE_IEEE, SCALE_HW_RSQ = 0, 1
 ATTN_AUTO, ATTN_VALU, ATTN_MFMA = 0, 1, 2
 FLAG_CAPACITY, FLAG_NONEMPTY, FLAG_BADSTATE = 1, 2, 4
 HEAD_DIM, BLOCK_TOKENS, RESIDUAL_TOKENS, RECORD_BYTES = 128, 32, 128, 3072
@@ -41,7 +42,8 @@ class Geom(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("norm_scope", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
-                ("num_physical_blocks", ctypes.c_int32), ("flush_tokens", ctypes.c_int32)]
+                ("num_physical_blocks", ctypes.c_int32), ("flush_tokens", ctypes.c_int32),
+                ("key_scale", ctypes.c_int32)]
 
 
 class CacheBufs(ctypes.Structure):
@@ -115,9 +117,10 @@ def _stream(stream=None):
 
 
 def make_geom(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, num_physical_blocks,
-              norm_scope=NORM_TOKEN, head_dim=HEAD_DIM, flush_tokens=32) -> Geom:
+              norm_scope=NORM_TOKEN, head_dim=HEAD_DIM, flush_tokens=32,
+              key_scale=SCALE_IEEE) -> Geom:
     return Geom(batch, num_q_heads, num_kv_heads, head_dim, norm_scope, max_blocks_per_seq,
-                num_physical_blocks, flush_tokens)
+                num_physical_blocks, flush_tokens, key_scale)
 
 
 def cache_layout(geom: Geom) -> CacheSizes:

@@ -34,6 +34,7 @@ oscar_status check_geom(const oscar_cache_geom* g) {
   if (g->max_blocks_per_seq < 1 || g->num_physical_blocks < 1) return OSCAR_EINVAL;
   if (g->norm_scope != OSCAR_NORM_TOKEN && g->norm_scope != OSCAR_NORM_HEAD) return OSCAR_EINVAL;
   if (g->flush_tokens != 0 && g->flush_tokens != 32 && g->flush_tokens != 128) return OSCAR_EINVAL;
+  if (g->key_scale != OSCAR_SCALE_IEEE && g->key_scale != OSCAR_SCALE_HW_RSQ) return OSCAR_EINVAL;
   return OSCAR_OK;
 }
 

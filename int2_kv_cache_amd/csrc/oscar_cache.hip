@@ -193,6 +193,7 @@ struct CacheArgs {
   int nphys;
   int head_norm;    // 1: a norm per (token, KV head) ([P][Hkv][32], [B][Hkv][128])
   int flush_blocks;  // blocks quantized when the window is full: 1 or 4
+  int hw_rsq;        // 1: scaling factor from the hardware rsqrt
 };
 // Token norm slots: TOKEN scope [P][32] and [B][128]; HEAD scope [P][Hkv][32]
 // and [B][Hkv][128].
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
   if (h < hkv) {
     float nrm, r;
     // TOKEN: the tree over all heads; HEAD: the head's own (within-head) tree
-    scale_from_ss(ca.head_norm ? part[h] : tree16(part, hkv), nrm, r);
+    scale_from_ss(ca.head_norm ? part[h] : tree16(part, hkv), nrm, r, ca.hw_rsq != 0);
     const size_t bh = static_cast<size_t>(b) * hkv + h;
     uint16_t* rk = ca.res_k + (bh * kR + slot) * kD;
     rk[lane] = f32_to_f16(mul_rn(a, r));
@@ -467,7 +468,7 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
   if (tid < 32 * (ca.head_norm ? hkv : 1)) {
     const int tl = ca.head_norm ? tid / hkv : tid, h = ca.head_norm ? tid % hkv : 0;
     float nrm, r;
-    scale_from_ss(ca.head_norm ? part[tid] : tree16(part + tid * hkv, hkv), nrm, r);
+    scale_from_ss(ca.head_norm ? part[tid] : tree16(part + tid * hkv, hkv), nrm, r, ca.hw_rsq != 0);
     tok_r[tid] = r;
     const int t = t0 + tl;
     if (t < n_tokens) {
@@ -609,6 +610,7 @@ CacheArgs make_args(const oscar_cache_geom* g, const oscar_cache* c) {
   a.nphys = g->num_physical_blocks;
   a.head_norm = g->norm_scope == OSCAR_NORM_HEAD ? 1 : 0;
   a.flush_blocks = g->flush_tokens == 128 ? 4 : 1;
+  a.hw_rsq = g->key_scale == OSCAR_SCALE_HW_RSQ ? 1 : 0;
   return a;
 }
 

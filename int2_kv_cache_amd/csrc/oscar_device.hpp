@@ -164,9 +164,15 @@ __device__ __forceinline__ float sqrt_rn(float x) {
 // Omni-Token Scaling factors from a sum of squares: norm = sqrt(ss) and
 // r = 1/norm, both correctly rounded fp32; ss == 0 gives r = 0 ([RN] §II
 // Step Two; [POP] 三 on 1/sqrt(sum x^2)).
-__device__ __forceinline__ void scale_from_ss(float ss, float& norm, float& r) {
+// With hw_rsq, r comes from the hardware reciprocal square root instead
+// ([POP] 三: one rsqrt instruction rather than the norm and its reciprocal);
+// the norm is the same correctly rounded root.
+__device__ __forceinline__ void scale_from_ss(float ss, float& norm, float& r, bool hw_rsq = false) {
   norm = sqrt_rn(ss);
-  r = ss > 0.0f ? __fdiv_rn(1.0f, norm) : 0.0f;
+  if (hw_rsq)
+    r = ss > 0.0f ? __builtin_amdgcn_rsqf(ss) : 0.0f;
+  else
+    r = ss > 0.0f ? __fdiv_rn(1.0f, norm) : 0.0f;
 }
 
 // Packed record layout (see include/oscar.h).

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void rotate_query_kernel(const uint16_t* __res
 
 // One block per token, one wave per head (64 * n_heads threads).
 __global__ __launch_bounds__(1024) void rotate_scale_key_kernel(
-    const uint16_t* __restrict__ x, int is_bf16, int n_heads, int head_scope,
+    const uint16_t* __restrict__ x, int is_bf16, int n_heads, int head_scope, int hw_rsq,
     uint16_t* __restrict__ khat, uint16_t* __restrict__ norm) {
   __shared__ float part[16];
   const int t = blockIdx.x, h = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(1024) void rotate_scale_key_kernel(
     ss = tree16(part, n_heads);
   }
   float nrm, r;
-  scale_from_ss(ss, nrm, r);
+  scale_from_ss(ss, nrm, r, hw_rsq != 0);
   khat[base + lane] = f32_to_f16(mul_rn(a, r));
   khat[base + lane + 64] = f32_to_f16(mul_rn(b, r));
   if (lane == 0) {
@@ -63,13 +63,13 @@ extern "C" oscar_status oscar_rotate_scale(const void* x, oscar_dtype dtype, int
                                            oscar_norm_scope norm_scope, float* q_out,
                                            void* khat_out, void* norm_out, void* stream) {
   if (!x || n_tokens < 0 || n_heads < 1) return OSCAR_EINVAL;
-  if (mode == OSCAR_ROT_KEY && n_heads > 16) return OSCAR_EINVAL;
+  if (mode != OSCAR_ROT_QUERY && n_heads > 16) return OSCAR_EINVAL;
   if (static_cast<long long>(n_tokens) * n_heads > (1LL << 30)) return OSCAR_EINVAL;
   if (dtype != OSCAR_FP16 && dtype != OSCAR_BF16) return OSCAR_EINVAL;
   if (norm_scope != OSCAR_NORM_TOKEN && norm_scope != OSCAR_NORM_HEAD) return OSCAR_EINVAL;
   if (mode == OSCAR_ROT_QUERY) {
     if (!q_out) return OSCAR_EINVAL;
-  } else if (mode == OSCAR_ROT_KEY) {
+  } else if (mode == OSCAR_ROT_KEY || mode == OSCAR_ROT_KEY_HW_RSQ) {
     if (!khat_out || !norm_out) return OSCAR_EINVAL;
   } else {
     return OSCAR_EINVAL;
@@ -86,7 +86,7 @@ extern "C" oscar_status oscar_rotate_scale(const void* x, oscar_dtype dtype, int
   } else {
     hipLaunchKernelGGL(rotate_scale_key_kernel, dim3(n_tokens), dim3(64 * n_heads), 0,
                        as_stream(stream), static_cast<const uint16_t*>(x), is_bf16, n_heads,
-                       norm_scope == OSCAR_NORM_HEAD ? 1 : 0,
+                       norm_scope == OSCAR_NORM_HEAD ? 1 : 0, mode == OSCAR_ROT_KEY_HW_RSQ ? 1 : 0,
                        static_cast<uint16_t*>(khat_out), static_cast<uint16_t*>(norm_out));
   }
   return launch_status();

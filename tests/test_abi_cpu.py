@@ -62,6 +62,17 @@ def test_cache_layout_norm_scopes():
     assert e.value.status == ok.EINVAL
 
 
+def test_cache_layout_key_scale():
+    """The scaling factor's two forms are accepted, nothing else; the sizes do
+    not depend on it."""
+    a = ok.cache_layout(ok.make_geom(1, 8, 2, 6, 6))
+    b = ok.cache_layout(ok.make_geom(1, 8, 2, 6, 6, key_scale=ok.SCALE_HW_RSQ))
+    assert (a.pool, a.pool_norm, a.res_k) == (b.pool, b.pool_norm, b.res_k)
+    with pytest.raises(ok.OscarError) as e:
+        ok.cache_layout(ok.make_geom(1, 8, 2, 6, 6, key_scale=2))
+    assert e.value.status == ok.EINVAL
+
+
 def test_status_strings():
     assert ok.status_str(ok.OK) == "ok"
     assert "workspace" in ok.status_str(ok.EWORKSPACE)
