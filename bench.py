@@ -166,7 +166,18 @@ def cpu_baseline(wl, k, v, steps, hq, args):
             "sample": "one decode step of one layer at n=%d: append + attention for %d of "
                       "%d query heads (timed %.2f s), scaled x%.1f to all heads"
                       % (n, len(heads), hq, dt, scale),
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": cpu_model(), "host_threads": os.cpu_count()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def dense_bytes(ctxs, hq: int, hkv: int) -> int:
