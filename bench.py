@@ -11,7 +11,9 @@ for each of L distinct layer caches, the whole decode hot path:
   decode_attn -- query FHT, split-K attention over the INT2 blocks and the
                  fp16 window, cross-split LSE reduce.
 L copies (default 8, 806 MB) are cycled so the 256 MB Infinity Cache cannot
-serve a layer from a previous visit.
+serve a layer from a previous visit.  `--workload 1` (Llama-3.1-8B shape, 32K,
+32 layers) and `--workload 4` (multimodal 64K: bulk prefill throughput, then
+decode, 16 layers) run the other single-sequence workloads the same way.
 
 Output: one JSON line.  value = context tokens attended per second (whole job),
 plus the per-layer microseconds, the roofline of the attention kernels and
@@ -32,6 +34,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
+# batch-1 decode workloads: synthetic config id -> (name, layer caches cycled so
+# that they exceed 3x the 256 MB Infinity Cache)
+WORKLOADS = {
+    1: ("llama-3.1-8b-shape decode, 32K ctx, batch 1", 32),
+    2: ("qwen3-8b-shape decode, 128K ctx, batch 1", 8),
+    4: ("qwen3-vl-8b-shape multimodal prefill + decode, 64K ctx, batch 1", 16),
+}
 # the decode-attention kernels and the headers they compile from
 ATTN_SRC = [os.path.join(ROOT, "int2_kv_cache_amd", "csrc", f)
             for f in ("oscar_attn.hip", "oscar_device.hpp", "oscar_host.hpp")]
@@ -77,8 +86,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layers", type=int, default=8)
-    ap.add_argument("--ctx", type=int, default=131072)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS),
+                    help="2: Qwen3-8B 128K (default); 1: Llama-3.1-8B 32K; "
+                         "4: Qwen3-VL-8B-like multimodal 64K (prefill + decode)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer caches cycled (0: enough to exceed 3x the 256 MB Infinity Cache)")
+    ap.add_argument("--ctx", type=int, default=0, help="context at the first step (0: the workload's)")
     ap.add_argument("--variant", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -146,7 +159,7 @@ def cpu_baseline(wl, k, v, steps, hq, args):
     query heads."""
     import oracle
     cfg = wl.cfg
-    mb = (args.ctx + 4096) // 32
+    mb = (wl.ctx_lens[0] + 4096) // 32
     orc = oracle.OracleCache(1, cfg.hq, cfg.hkv, mb, mb,
                              norm_scope=oracle.NORM_HEAD if args.head_norm else oracle.NORM_TOKEN,
                              flush_tokens=128 if args.flush128 else 32)
@@ -388,11 +401,13 @@ def main():
     from int2_kv_cache_amd import synth
 
     torch.cuda.set_device(0)
-    wl = synth.workload(2, ctx=args.ctx)
+    wl = synth.workload(args.workload, ctx=args.ctx) if args.ctx else synth.workload(args.workload)
+    ctx = wl.ctx_lens[0]
+    wname, default_layers = WORKLOADS[args.workload]
     cfg = wl.cfg
-    L = args.layers
+    L = args.layers or default_layers
     n_steps_total = args.warmup + args.steps
-    max_ctx = args.ctx + n_steps_total + 64
+    max_ctx = ctx + n_steps_total + 64
     mb = (max_ctx + 31) // 32
     geom = ok.make_geom(1, cfg.hq, cfg.hkv, mb, mb,
                         norm_scope=ok.NORM_HEAD if args.head_norm else ok.NORM_TOKEN,
@@ -407,10 +422,11 @@ def main():
     kd, vd = dev(k), dev(v)
     dense = None
     if not args.no_bf16:
-        # the bf16 baseline's caches: the same 131071 prefilled tokens, two
-        # layers (1.07 GB, beyond the 256 MB Infinity Cache)
+        # the bf16 baseline's caches: the same prefilled tokens, at least two
+        # layers and enough to exceed 3x the 256 MB Infinity Cache (two at 128K)
         dgeom = ok.make_geom(1, cfg.hq, cfg.hkv, mb, mb)
-        dense = DenseLeg(ok, torch, dgeom, None, [args.ctx - 1], 2)
+        dense = DenseLeg(ok, torch, dgeom, None, [ctx - 1], max(2, -(-3 * 256 * 2**20 // (
+            (ctx - 1) * cfg.hkv * 512))))
         dense.write(0, kd, vd)
         dense.replicate()
     caches = []
@@ -505,9 +521,9 @@ def main():
         "dtype": ("int2 cache; fp32 vector math" if args.variant == 1 else
                   "int2 cache; fp16 MFMA operands, fp32 accumulate"),
         "data": "synthetic (seeded; K outliers/sinks/log-normal norms, V and q N(0,1))",
-        "config": {"workload": "qwen3-8b-shape decode, 128K ctx, batch 1",
+        "config": {"workload": wname,
                    "batch": 1, "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv,
-                   "head_dim": 128, "ctx_first_step": args.ctx, "layers_cycled": L,
+                   "head_dim": 128, "ctx_first_step": ctx, "layers_cycled": L,
                    "splits": S, "variant": args.variant,
                    "norm_scope": "head" if args.head_norm else "token",
                    "flush_tokens": 128 if args.flush128 else 32,
@@ -526,7 +542,7 @@ def main():
                      "measured_copy_gbs": copy_gbs,
                      "frac_of_measured_copy": achieved / copy_gbs},
         "prefill_ms_per_layer": float(np.median(pre_ms)),
-        "prefill_tokens_per_s": (args.ctx - 1) / (float(np.median(pre_ms)) / 1000.0),
+        "prefill_tokens_per_s": (ctx - 1) / (float(np.median(pre_ms)) / 1000.0),
         "final_state": [n1, Q1],
         "setup_s": setup_s,
     }

@@ -1087,15 +1087,19 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(const float2* __restric
 }
 
 int auto_splits(const oscar_cache_geom* g, int max_ctx) {
-  // about three 4-wave workgroups per CU on 256 CUs, and at least 8 blocks
-  // per workgroup; where a workgroup would hold 256 blocks or more, twice as
-  // many workgroups (two rounds: the dispatcher's refill evens out ragged
-  // sequences and uneven CUs; measured 5 % faster on 48 sequences of 8K..32K)
+  // about three 4-wave workgroups per CU on 256 CUs while that leaves a
+  // workgroup 32 blocks or more, else two per CU (fewer partials and waves
+  // when each wave has only a few blocks: measured 20.2 vs 21.3 us at 32K,
+  // 25.9 vs 26.6 us at 64K); at least 4 blocks per workgroup; where a
+  // workgroup would hold 256 blocks or more, twice as many workgroups (two
+  // rounds: the dispatcher's refill evens out ragged sequences and uneven
+  // CUs; measured 5 % faster on 48 sequences of 8K..32K)
   const int units = (max_ctx + kG - 1) / kG + 1;
   const int pairs = g->batch * g->num_kv_heads;
   int s = (768 + pairs - 1) / pairs;
+  if (units / s < 32) s = (512 + pairs - 1) / pairs;
   if (units / s >= 256) s *= 2;
-  const int cap = units / 8 > 1 ? units / 8 : 1;
+  const int cap = units / 4 > 1 ? units / 4 : 1;
   if (s > cap) s = cap;
   if (s > 1024) s = 1024;
   return s < 1 ? 1 : s;
