@@ -73,6 +73,44 @@ def test_cache_layout_key_scale():
     assert e.value.status == ok.EINVAL
 
 
+def _dense_call(fn, *args):
+    return getattr(ok.lib(), fn)(*args)
+
+
+def test_dense_workspace_query_and_rejects():
+    """Host-only: the bf16 baseline's workspace query sizes the same partials
+    as the INT2 path; bad arguments are rejected before anything runs."""
+    g = ok.make_geom(1, 32, 8, 4200, 4200)
+    s, nbytes = ok.dense_workspace_bytes(g, 131072)
+    assert 1 <= s <= 1024
+    assert nbytes >= 32 * s * (8 + 512)
+    for bad in [dict(max_ctx=-1), dict(num_splits=1025)]:
+        args = dict(max_ctx=100, num_splits=0)
+        args.update(bad)
+        with pytest.raises(ok.OscarError) as e:
+            ok.dense_workspace_bytes(g, **args)
+        assert e.value.status == ok.EINVAL
+
+
+def test_dense_calls_validate_before_touching_memory():
+    """Null, misaligned or undersized arguments return a status and enqueue
+    nothing (the fake addresses below are never dereferenced)."""
+    g = ok.make_geom(1, 4, 1, 4, 4)
+    vp = ctypes.c_void_p
+    A = vp(0x100000)          # 256-byte aligned stand-ins
+    odd = vp(0x100002)
+    gr = ctypes.byref(g)
+    _, need = ok.dense_workspace_bytes(g, 128, 0)
+    common = lambda k, ws, nbytes: (gr, k, A, A, A, A, A, None, ws, nbytes, 0, 128, A, None)
+    assert _dense_call("oscar_dense_decode_attn", *common(None, A, need)) == ok.EINVAL
+    assert _dense_call("oscar_dense_decode_attn", *common(A, odd, need)) == ok.EINVAL
+    assert _dense_call("oscar_dense_decode_attn", *common(A, A, need - 1)) == ok.EWORKSPACE
+    # writes: sequence out of range, past the block table's capacity, misaligned input
+    assert _dense_call("oscar_dense_write_kv", gr, A, A, A, 1, 0, A, A, 8, A, None) == ok.EINVAL
+    assert _dense_call("oscar_dense_write_kv", gr, A, A, A, 0, 120, A, A, 9, A, None) == ok.EINVAL
+    assert _dense_call("oscar_dense_write_kv", gr, A, A, A, 0, 0, odd, A, 8, A, None) == ok.EINVAL
+
+
 def test_status_strings():
     assert ok.status_str(ok.OK) == "ok"
     assert "workspace" in ok.status_str(ok.EWORKSPACE)
