@@ -11,9 +11,10 @@ for each of L distinct layer caches, the whole decode hot path:
   decode_attn -- query FHT, split-K attention over the INT2 blocks and the
                  fp16 window, cross-split LSE reduce.
 L copies (default 8, 806 MB) are cycled so the 256 MB Infinity Cache cannot
-serve a layer from a previous visit.  `--workload 1` (Llama-3.1-8B shape, 32K,
-32 layers) and `--workload 4` (multimodal 64K: bulk prefill throughput, then
-decode, 16 layers) run the other single-sequence workloads the same way.
+serve a layer from a previous visit.  `--workload llama-32k` (Llama-3.1-8B
+shape, 32K, 32 layers) and `--workload multimodal-64k` (bulk prefill
+throughput, then decode, 16 layers) run the other single-sequence workloads
+the same way.
 
 Output: one JSON line.  value = context tokens attended per second (whole job),
 plus the per-layer microseconds, the roofline of the attention kernels and
@@ -34,12 +35,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
-# batch-1 decode workloads: synthetic config id -> (name, layer caches cycled so
-# that they exceed 3x the 256 MB Infinity Cache)
+# batch-1 decode workloads: option name -> (synthetic workload id, description,
+# layer caches cycled so that they exceed 3x the 256 MB Infinity Cache)
 WORKLOADS = {
-    1: ("llama-3.1-8b-shape decode, 32K ctx, batch 1", 32),
-    2: ("qwen3-8b-shape decode, 128K ctx, batch 1", 8),
-    4: ("qwen3-vl-8b-shape multimodal prefill + decode, 64K ctx, batch 1", 16),
+    "llama-32k": (1, "llama-3.1-8b-shape decode, 32K ctx, batch 1", 32),
+    "qwen3-128k": (2, "qwen3-8b-shape decode, 128K ctx, batch 1", 8),
+    "multimodal-64k": (4, "qwen3-vl-8b-shape multimodal prefill + decode, 64K ctx, batch 1", 16),
 }
 # the decode-attention kernels and the headers they compile from
 ATTN_SRC = [os.path.join(ROOT, "int2_kv_cache_amd", "csrc", f)
@@ -86,9 +87,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOADS),
-                    help="2: Qwen3-8B 128K (default); 1: Llama-3.1-8B 32K; "
-                         "4: Qwen3-VL-8B-like multimodal 64K (prefill + decode)")
+    ap.add_argument("--workload", default="qwen3-128k", choices=sorted(WORKLOADS),
+                    help="qwen3-128k: Qwen3-8B shape at 128K (default); llama-32k: "
+                         "Llama-3.1-8B shape at 32K; multimodal-64k: Qwen3-VL-8B-like "
+                         "multimodal 64K (prefill + decode)")
     ap.add_argument("--layers", type=int, default=0,
                     help="layer caches cycled (0: enough to exceed 3x the 256 MB Infinity Cache)")
     ap.add_argument("--ctx", type=int, default=0, help="context at the first step (0: the workload's)")
@@ -401,9 +403,9 @@ def main():
     from int2_kv_cache_amd import synth
 
     torch.cuda.set_device(0)
-    wl = synth.workload(args.workload, ctx=args.ctx) if args.ctx else synth.workload(args.workload)
+    wid, wname, default_layers = WORKLOADS[args.workload]
+    wl = synth.workload(wid, ctx=args.ctx) if args.ctx else synth.workload(wid)
     ctx = wl.ctx_lens[0]
-    wname, default_layers = WORKLOADS[args.workload]
     cfg = wl.cfg
     L = args.layers or default_layers
     n_steps_total = args.warmup + args.steps
