@@ -195,6 +195,44 @@ def cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
+def stateless_calls(ok, torch, cfg, k, v, reps: int = 5):
+    """The two stateless entry points on the prefill's tokens, outside the
+    timed decode steps: oscar_rotate_scale (KEY) over all of them, then
+    oscar_quant_pack over their whole 32-token blocks (fp16 Values converted
+    by torch beforehand).  Median of `reps` calls, HIP events on the stream
+    they run on."""
+    T, hkv = k.shape[0], k.shape[1]
+    nb = T // 32
+    kd = torch.from_numpy(np.ascontiguousarray(k).view(np.int16)).cuda()
+    khat = torch.empty_like(kd)
+    knorm = torch.empty(T, dtype=torch.int16, device="cuda")
+    v16 = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).cuda()
+    if cfg.dtype == ok.BF16:
+        v16 = v16.view(torch.bfloat16).to(torch.float16).view(torch.int16)
+    rec = torch.empty(nb, hkv, ok.RECORD_BYTES, dtype=torch.uint8, device="cuda")
+    nrm = torch.empty(nb, 32, dtype=torch.int16, device="cuda")
+
+    def timed(fn):
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms)) * 1000.0
+
+    rot_us = timed(lambda: ok.rotate_scale(kd, cfg.dtype, ok.ROT_KEY, khat_out=khat, norm_out=knorm))
+    qp_us = timed(lambda: ok.quant_pack(khat[:32 * nb], knorm[:32 * nb], v16[:32 * nb], rec, nrm))
+    rot_bytes = T * hkv * 128 * 2 * 2 + T * 2                     # k in, k_hat out, norms
+    qp_bytes = nb * (32 * hkv * 128 * 2 * 2 + 64) + nb * (hkv * 3072 + 64)
+    return {"rotate_scale_key": {"tokens": T, "us": rot_us, "algorithmic_bytes": rot_bytes,
+                                 "achieved_gbs": rot_bytes / (rot_us * 1e-6) / 1e9},
+            "quant_pack": {"blocks": nb, "us": qp_us, "algorithmic_bytes": qp_bytes,
+                           "achieved_gbs": qp_bytes / (qp_us * 1e-6) / 1e9}}
+
+
 def dense_bytes(ctxs, hq: int, hkv: int) -> int:
     """Algorithmic bytes of one bf16 baseline call: every token's bf16 Key and
     Value rows, the bf16 queries in and the fp32 outputs."""
@@ -548,6 +586,7 @@ def main():
         "final_state": [n1, Q1],
         "setup_s": setup_s,
     }
+    res["stateless"] = stateless_calls(ok, torch, cfg, k, v)
     if dense is not None:
         res["bf16_baseline"] = dense.time(q_d, args.steps, args.warmup, 0, attn_us)
     if not args.no_cpu:

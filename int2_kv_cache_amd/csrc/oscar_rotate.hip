@@ -25,32 +25,50 @@ __global__ __launch_bounds__(256) void rotate_query_kernel(const uint16_t* __res
   out[base + lane + 64] = b;
 }
 
-// One block per token, one wave per head (64 * n_heads threads).
-__global__ __launch_bounds__(1024) void rotate_scale_key_kernel(
-    const uint16_t* __restrict__ x, int is_bf16, int n_heads, int head_scope, int hw_rsq,
-    uint16_t* __restrict__ khat, uint16_t* __restrict__ norm) {
-  __shared__ float part[16];
-  const int t = blockIdx.x, h = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const size_t base = (static_cast<size_t>(t) * n_heads + h) * kD;
-  float a = in_to_f32(x[base + lane], is_bf16);
-  float b = in_to_f32(x[base + lane + 64], is_bf16);
-  fht128_wave(a, b);
-  const float hs = wave_tree_sumsq(a, b);
-  float ss = hs;
-  if (!head_scope) {
-    if (lane == 0) part[h] = hs;
-    __syncthreads();
-    ss = tree16(part, n_heads);
+// One wave per token, all of its heads in registers (lane l holds elements l
+// and l + 64 of every head), four tokens per 256-thread block.  The heads'
+// butterflies are independent, so a wave keeps up to 2 * n_heads loads and
+// stores in flight; the sums of squares are the same per-head trees as in
+// the oracle, then the tree over the heads (TOKEN scope) in registers.
+template <int MAXH>
+__global__ __launch_bounds__(256) void rotate_scale_key_kernel(
+    const uint16_t* __restrict__ x, int is_bf16, int n_tokens, int n_heads, int head_scope,
+    int hw_rsq, uint16_t* __restrict__ khat, uint16_t* __restrict__ norm) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= n_tokens) return;  // uniform per wave
+  const size_t base = static_cast<size_t>(t) * n_heads * kD;
+  float a[MAXH], b[MAXH], hs[MAXH];
+#pragma unroll
+  for (int h = 0; h < MAXH; ++h) {
+    if (h < n_heads) {
+      a[h] = in_to_f32(x[base + h * kD + lane], is_bf16);
+      b[h] = in_to_f32(x[base + h * kD + lane + 64], is_bf16);
+    }
   }
-  float nrm, r;
-  scale_from_ss(ss, nrm, r, hw_rsq != 0);
-  khat[base + lane] = f32_to_f16(mul_rn(a, r));
-  khat[base + lane + 64] = f32_to_f16(mul_rn(b, r));
-  if (lane == 0) {
-    if (head_scope)
-      norm[static_cast<size_t>(t) * n_heads + h] = f32_to_f16(nrm);
-    else if (h == 0)
-      norm[t] = f32_to_f16(nrm);
+#pragma unroll
+  for (int h = 0; h < MAXH; ++h) {
+    if (h < n_heads) {
+      fht128_wave(a[h], b[h]);
+      hs[h] = wave_tree_sumsq(a[h], b[h]);
+    } else {
+      hs[h] = 0.0f;
+    }
+  }
+  const float ss_tok = head_scope ? 0.0f : tree16(hs, n_heads);
+#pragma unroll
+  for (int h = 0; h < MAXH; ++h) {
+    if (h < n_heads) {
+      float nrm, r;
+      scale_from_ss(head_scope ? hs[h] : ss_tok, nrm, r, hw_rsq != 0);
+      khat[base + h * kD + lane] = f32_to_f16(mul_rn(a[h], r));
+      khat[base + h * kD + lane + 64] = f32_to_f16(mul_rn(b[h], r));
+      if (lane == 0) {
+        if (head_scope)
+          norm[static_cast<size_t>(t) * n_heads + h] = f32_to_f16(nrm);
+        else if (h == 0)
+          norm[t] = f32_to_f16(nrm);
+      }
+    }
   }
 }
 
@@ -84,10 +102,17 @@ extern "C" oscar_status oscar_rotate_scale(const void* x, oscar_dtype dtype, int
     hipLaunchKernelGGL(rotate_query_kernel, dim3(grid), dim3(256), 0, as_stream(stream),
                        static_cast<const uint16_t*>(x), is_bf16, static_cast<int>(n_vec), q_out);
   } else {
-    hipLaunchKernelGGL(rotate_scale_key_kernel, dim3(n_tokens), dim3(64 * n_heads), 0,
-                       as_stream(stream), static_cast<const uint16_t*>(x), is_bf16, n_heads,
-                       norm_scope == OSCAR_NORM_HEAD ? 1 : 0, mode == OSCAR_ROT_KEY_HW_RSQ ? 1 : 0,
-                       static_cast<uint16_t*>(khat_out), static_cast<uint16_t*>(norm_out));
+    const unsigned grid = static_cast<unsigned>((static_cast<long long>(n_tokens) + 3) / 4);
+    const int hs = norm_scope == OSCAR_NORM_HEAD ? 1 : 0, hw = mode == OSCAR_ROT_KEY_HW_RSQ ? 1 : 0;
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    uint16_t* kh = static_cast<uint16_t*>(khat_out);
+    uint16_t* nm = static_cast<uint16_t*>(norm_out);
+    if (n_heads <= 8)
+      hipLaunchKernelGGL(rotate_scale_key_kernel<8>, dim3(grid), dim3(256), 0, as_stream(stream), xs,
+                         is_bf16, n_tokens, n_heads, hs, hw, kh, nm);
+    else
+      hipLaunchKernelGGL(rotate_scale_key_kernel<16>, dim3(grid), dim3(256), 0, as_stream(stream), xs,
+                         is_bf16, n_tokens, n_heads, hs, hw, kh, nm);
   }
   return launch_status();
 }
