@@ -165,7 +165,8 @@ OSCAR_API oscar_status oscar_cache_layout(const oscar_cache_geom *geom, oscar_ca
  *             KEY_HW_RSQ: KEY with 1/sqrt(ss) from the hardware instruction
  *                    (OSCAR_SCALE_HW_RSQ).
  *   n_heads   >= 1 (QUERY), 1..16 (KEY: the norm spans all heads of a token).
- * Errors: EINVAL (null, n_tokens < 0, n_heads out of range, bad dtype). */
+ * Errors: EINVAL (null, n_tokens < 0, n_heads out of range, bad dtype; for
+ * KEY, x or khat_out not 16-byte aligned). */
 OSCAR_API oscar_status oscar_rotate_scale(const void *x, oscar_dtype dtype, int32_t n_tokens,
                                 int32_t n_heads, oscar_rot_mode mode,
                                 oscar_norm_scope norm_scope, float *q_out,

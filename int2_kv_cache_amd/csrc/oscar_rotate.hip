@@ -25,50 +25,95 @@ __global__ __launch_bounds__(256) void rotate_query_kernel(const uint16_t* __res
   out[base + lane + 64] = b;
 }
 
-// One wave per token, all of its heads in registers (lane l holds elements l
-// and l + 64 of every head), four tokens per 256-thread block.  The heads'
-// butterflies are independent, so a wave keeps up to 2 * n_heads loads and
-// stores in flight; the sums of squares are the same per-head trees as in
-// the oracle, then the tree over the heads (TOKEN scope) in registers.
-template <int MAXH>
+// Lane quad exchange (lanes 4m..4m+3): the value of lane l ^ X, X = 1 or 2.
+template <int X>
+__device__ __forceinline__ float quad_partner(float x) {
+  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xF, 0xF, true));
+}
+
+// Four lanes per (token, head) vector, 32 consecutive elements each; a
+// 256-thread block takes floor(64 / n_heads) tokens.  Butterfly strides 1..16
+// run in registers, strides 32 and 64 across the lane quad (the upper lane of
+// a pair takes partner - own as one exactly rounded fma with -1), then one
+// multiply by 1/sqrt(128): the same fp32 operations, in the same order, as
+// the plain butterfly.  The sum of squares follows the same pairwise tree:
+// levels 1..16 in registers, 32 and 64 across the quad, then over the heads
+// (TOKEN scope) from LDS.
 __global__ __launch_bounds__(256) void rotate_scale_key_kernel(
     const uint16_t* __restrict__ x, int is_bf16, int n_tokens, int n_heads, int head_scope,
     int hw_rsq, uint16_t* __restrict__ khat, uint16_t* __restrict__ norm) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (t >= n_tokens) return;  // uniform per wave
-  const size_t base = static_cast<size_t>(t) * n_heads * kD;
-  float a[MAXH], b[MAXH], hs[MAXH];
+#pragma clang fp contract(off)
+  __shared__ float part[64][16];  // [token in block][head]
+  const int tpb = 64 / n_heads;
+  const int tid = threadIdx.x, tq = tid & 3, vec = tid >> 2;
+  const int tl = vec / n_heads, h = vec % n_heads;
+  const int t = blockIdx.x * tpb + tl;
+  const bool active = tl < tpb && t < n_tokens;
+  float y[32];
+  const size_t off = (static_cast<size_t>(t) * n_heads + h) * kD + 32 * tq;
+  if (active) {
 #pragma unroll
-  for (int h = 0; h < MAXH; ++h) {
-    if (h < n_heads) {
-      a[h] = in_to_f32(x[base + h * kD + lane], is_bf16);
-      b[h] = in_to_f32(x[base + h * kD + lane + 64], is_bf16);
-    }
-  }
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w = reinterpret_cast<const uint4*>(x + off)[q];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int h = 0; h < MAXH; ++h) {
-    if (h < n_heads) {
-      fht128_wave(a[h], b[h]);
-      hs[h] = wave_tree_sumsq(a[h], b[h]);
-    } else {
-      hs[h] = 0.0f;
-    }
-  }
-  const float ss_tok = head_scope ? 0.0f : tree16(hs, n_heads);
-#pragma unroll
-  for (int h = 0; h < MAXH; ++h) {
-    if (h < n_heads) {
-      float nrm, r;
-      scale_from_ss(head_scope ? hs[h] : ss_tok, nrm, r, hw_rsq != 0);
-      khat[base + h * kD + lane] = f32_to_f16(mul_rn(a[h], r));
-      khat[base + h * kD + lane + 64] = f32_to_f16(mul_rn(b[h], r));
-      if (lane == 0) {
-        if (head_scope)
-          norm[static_cast<size_t>(t) * n_heads + h] = f32_to_f16(nrm);
-        else if (h == 0)
-          norm[t] = f32_to_f16(nrm);
+      for (int e = 0; e < 4; ++e) {
+        y[8 * q + 2 * e] = in_to_f32(static_cast<uint16_t>(ww[e]), is_bf16);
+        y[8 * q + 2 * e + 1] = in_to_f32(static_cast<uint16_t>(ww[e] >> 16), is_bf16);
       }
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) y[j] = 0.0f;
+  }
+#pragma unroll
+  for (int hs = 1; hs < 32; hs <<= 1)
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if ((j & hs) == 0) {
+        const float a = y[j], b = y[j + hs];
+        y[j] = a + b;
+        y[j + hs] = a - b;
+      }
+  const float sg1 = (tq & 1) ? -1.0f : 1.0f, sg2 = (tq & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) y[j] = __builtin_fmaf(sg1, y[j], quad_partner<1>(y[j]));
+#pragma unroll
+  for (int j = 0; j < 32; ++j) y[j] = __builtin_fmaf(sg2, y[j], quad_partner<2>(y[j]));
+#pragma unroll
+  for (int j = 0; j < 32; ++j) y[j] = y[j] * kFhtScale;
+  float sq[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) sq[j] = y[j] * y[j];
+#pragma unroll
+  for (int hs = 1; hs < 32; hs <<= 1)
+#pragma unroll
+    for (int j = 0; j < 32; j += 2 * hs) sq[j] = sq[j] + sq[j + hs];
+  float ss = sq[0];
+  ss = ss + quad_partner<1>(ss);
+  ss = ss + quad_partner<2>(ss);
+  if (!head_scope) {
+    if (active && tq == 0) part[tl][h] = ss;
+    __syncthreads();
+    if (active) ss = tree16(part[tl], n_heads);
+  }
+  if (!active) return;
+  float nrm, r;
+  scale_from_ss(ss, nrm, r, hw_rsq != 0);
+  uint32_t kw[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    kw[e] = static_cast<uint32_t>(f32_to_f16(mul_rn(y[2 * e], r))) |
+            (static_cast<uint32_t>(f32_to_f16(mul_rn(y[2 * e + 1], r))) << 16);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    reinterpret_cast<uint4*>(khat + off)[q] = uint4{kw[4 * q], kw[4 * q + 1], kw[4 * q + 2], kw[4 * q + 3]};
+  if (tq == 0) {
+    if (head_scope)
+      norm[static_cast<size_t>(t) * n_heads + h] = f32_to_f16(nrm);
+    else if (h == 0)
+      norm[t] = f32_to_f16(nrm);
   }
 }
 
@@ -88,7 +133,7 @@ extern "C" oscar_status oscar_rotate_scale(const void* x, oscar_dtype dtype, int
   if (mode == OSCAR_ROT_QUERY) {
     if (!q_out) return OSCAR_EINVAL;
   } else if (mode == OSCAR_ROT_KEY || mode == OSCAR_ROT_KEY_HW_RSQ) {
-    if (!khat_out || !norm_out) return OSCAR_EINVAL;
+    if (!khat_out || !norm_out || !aligned(x, 16) || !aligned(khat_out, 16)) return OSCAR_EINVAL;
   } else {
     return OSCAR_EINVAL;
   }
@@ -102,17 +147,12 @@ extern "C" oscar_status oscar_rotate_scale(const void* x, oscar_dtype dtype, int
     hipLaunchKernelGGL(rotate_query_kernel, dim3(grid), dim3(256), 0, as_stream(stream),
                        static_cast<const uint16_t*>(x), is_bf16, static_cast<int>(n_vec), q_out);
   } else {
-    const unsigned grid = static_cast<unsigned>((static_cast<long long>(n_tokens) + 3) / 4);
-    const int hs = norm_scope == OSCAR_NORM_HEAD ? 1 : 0, hw = mode == OSCAR_ROT_KEY_HW_RSQ ? 1 : 0;
-    const uint16_t* xs = static_cast<const uint16_t*>(x);
-    uint16_t* kh = static_cast<uint16_t*>(khat_out);
-    uint16_t* nm = static_cast<uint16_t*>(norm_out);
-    if (n_heads <= 8)
-      hipLaunchKernelGGL(rotate_scale_key_kernel<8>, dim3(grid), dim3(256), 0, as_stream(stream), xs,
-                         is_bf16, n_tokens, n_heads, hs, hw, kh, nm);
-    else
-      hipLaunchKernelGGL(rotate_scale_key_kernel<16>, dim3(grid), dim3(256), 0, as_stream(stream), xs,
-                         is_bf16, n_tokens, n_heads, hs, hw, kh, nm);
+    const int tpb = 64 / n_heads;
+    const unsigned grid = static_cast<unsigned>((static_cast<long long>(n_tokens) + tpb - 1) / tpb);
+    hipLaunchKernelGGL(rotate_scale_key_kernel, dim3(grid), dim3(256), 0, as_stream(stream),
+                       static_cast<const uint16_t*>(x), is_bf16, n_tokens, n_heads,
+                       norm_scope == OSCAR_NORM_HEAD ? 1 : 0, mode == OSCAR_ROT_KEY_HW_RSQ ? 1 : 0,
+                       static_cast<uint16_t*>(khat_out), static_cast<uint16_t*>(norm_out));
   }
   return launch_status();
 }
