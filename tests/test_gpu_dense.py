@@ -137,3 +137,12 @@ def test_dense_qwen3_8b_128k_bench_configuration():
 def test_dense_ragged_batch_8k_32k():
     wl = synth.workload(3, batch=6)
     _run(wl, wl.ctx_lens[:6], seed=2, heads=[0, 9, 18, 31])
+
+
+def test_dense_ragged_batch_48_full():
+    """The whole 48-sequence batch (8K..32K) in one launch, in the split count
+    the bench uses; sampled (sequence, head) outputs against the oracle."""
+    wl = synth.workload(3)
+    assert wl.cfg.batch == 48
+    ctxs = [n - 1 for n in wl.ctx_lens]
+    _run(wl, ctxs, seed=3, heads=[7])

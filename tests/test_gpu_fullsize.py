@@ -18,8 +18,8 @@ if gpu_available():
     from _parity import ATOL, Pair
 
 
-def _run(wl, heads, variants=(2, 1), bench_max_ctx=None):
-    pr = Pair(wl)
+def _run(wl, heads, variants=(2, 1), bench_max_ctx=None, **pair_kw):
+    pr = Pair(wl, **pair_kw)
     for b in range(wl.cfg.batch):
         k, v = wl.prefill(b)
         pr.prefill(b, k, v)
@@ -70,3 +70,44 @@ def test_ragged_batch_48_full():
     wl = synth.workload(3)
     assert wl.cfg.batch == 48
     _run(wl, [(b, (5 * b + 3) % 32) for b in range(0, 48, 6)], variants=(2,))
+
+
+@pytest.mark.parametrize("opt", [dict(norm_scope=1), dict(flush_tokens=128)])
+def test_qwen3_8b_128k_variants(opt):
+    """The HEAD norm scope and the 128-token flush at the headline size, in the
+    bench's split count: whole cache bit-exact, sampled heads within 2e-3."""
+    wl = synth.workload(2)
+    _run(wl, [(0, 3), (0, 26)], variants=(2,), bench_max_ctx=131072 + 105 + 64, **opt)
+
+
+def test_qwen3_8b_128k_hardware_rsqrt():
+    """The hardware-rsqrt scaling at the headline size: attention within 2e-3
+    of the IEEE oracle on sampled heads (k_hat may differ by one fp16 step)."""
+    wl = synth.workload(2)
+    pr = Pair(wl)
+    geom = ok.make_geom(1, wl.cfg.hq, wl.cfg.hkv, pr.max_blocks, pr.geom.num_physical_blocks,
+                        key_scale=ok.SCALE_HW_RSQ)
+    gpu = ok.DeviceCache(geom, block_table=torch.from_numpy(pr.table))
+    k, v = wl.prefill(0)
+    dt = wl.cfg.dtype
+    pr.orc.prefill(0, k, v, dt)
+    ok.prefill_quantize(gpu, 0, _dev(k), _dev(v), dt)
+    kn, vn, q = next(wl.steps(1))
+    pr.orc.append(kn, vn, dt)
+    ok.append_kv(gpu, _dev(kn), _dev(vn), dt)
+    mctx = 131072 + 105 + 64
+    S, nbytes = ok.decode_workspace_bytes(geom, mctx)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(1, wl.cfg.hq, 128, dtype=torch.float32, device="cuda")
+    ok.decode_attn(gpu, _dev(q), dt, out, None, ws, mctx)
+    torch.cuda.synchronize()
+    assert gpu.seq_state.cpu().numpy().tolist() == pr.orc.seq_state.tolist()
+    got = out.cpu().numpy()
+    qr = oracle.rotate_query(q, dt)
+    for i in (0, 11, 31):
+        want, _ = pr.orc.decode_attn_one(qr, 0, i)
+        assert float(np.abs(got[0, i] - want).max()) <= ATOL, i
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
