@@ -396,7 +396,8 @@ def batch48(args):
         "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": total_ms / steps,
         "higher_is_better": True,
-        "dtype": "int2 cache; fp16 MFMA operands, fp32 accumulate",
+        "dtype": "fp16",
+        "dtype_detail": "INT2 cache; fp16 MFMA operands, fp32 accumulate",
         "data": "synthetic (seeded; K outliers/sinks/log-normal norms, V and q N(0,1))",
         "config": {"workload": "qwen3-8b-shape decode, batch 48, contexts 8K..32K, 36 layers",
                    "batch": B, "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv,
@@ -558,8 +559,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("int2 cache; fp32 vector math" if args.variant == 1 else
-                  "int2 cache; fp16 MFMA operands, fp32 accumulate"),
+        "dtype": "fp32" if args.variant == 1 else "fp16",
+        "dtype_detail": ("INT2 cache; fp32 vector math" if args.variant == 1 else
+                         "INT2 cache; fp16 MFMA operands, fp32 accumulate"),
         "data": "synthetic (seeded; K outliers/sinks/log-normal norms, V and q N(0,1))",
         "config": {"workload": wname,
                    "batch": 1, "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv,
