@@ -13,6 +13,12 @@ Recipe (the shapes and distributions of the five workloads):
            workload a segment pattern (text x1 for 2048 tokens, vision x5 for
            8192, audio x0.3 for 4096, repeating) plus 0.1% of the tokens at x30.
            m_t is shared by all heads of token t.
+  * Optional flat sinks (Workload.flat_sinks): the sink tokens' g is instead an
+           isotropic N(0, 1) vector rescaled to the norm the outlier-bearing g
+           of that token had -- low-norm tokens whose energy is spread evenly
+           over the channels, the shape the pages give for attention sinks (an
+           extra draw after the multipliers; off by default, which leaves every
+           other stream unchanged).
   * Values V ~ N(0, 1).  The pages rotate V offline by a Hadamard matrix; an
            orthonormal rotation of an i.i.d. standard normal vector is again
            i.i.d. standard normal, so drawing N(0, 1) directly gives exactly the
@@ -94,6 +100,7 @@ class Workload:
     seed: int
     ctx_lens: list = field(default_factory=list)   # tokens attended at step 1
     outlier_idx: list = field(default_factory=list)  # per KV head: channel ids
+    flat_sinks: bool = False   # sink tokens isotropic instead of outlier-shaped
 
     @property
     def batch(self):
@@ -104,6 +111,13 @@ class Workload:
         for h, idx in enumerate(self.outlier_idx):
             g[:, h, idx] = 20.0 * g[:, h, idx] + 5.0
         m = mult_fn(rng, np.arange(t0, t0 + T))
+        if self.flat_sinks:
+            sinks = np.arange(t0, t0 + T) < 4
+            if sinks.any():
+                iso = rng.standard_normal((int(sinks.sum()), self.cfg.hkv, D), dtype=np.float32)
+                scale = np.linalg.norm(g[sinks].reshape(len(iso), -1), axis=1) / \
+                    np.linalg.norm(iso.reshape(len(iso), -1), axis=1)
+                g[sinks] = iso * scale[:, None, None]
         return g * m[:, None, None]
 
     def _mult_prefill(self, rng, t):

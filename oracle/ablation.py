@@ -10,9 +10,13 @@ Four ways to store Keys in INT2 with the same quantizer (per channel over
 For each: the relative reconstruction error of every token's Key (all heads)
 and the relative error of attention outputs against unquantized fp64
 attention with the same queries (scaled to a score spread of 2.5) and exact
-Values.  The pages claim that rotation flattens
+Values; and the mean relative error of the normal tokens that share a 32-token
+block with the sink tokens (the first 4).  The pages claim that rotation flattens
 outlier channels and scaling equalises token norms, so that 2-bit codes lose
-less; this measures it on the synthetic workloads.  Run: python -m oracle.ablation
+less, and that scaling without rotation blows up the ranges of blocks holding
+flat low-norm sinks (the Scaling-Induced Outlier Artifact: a sink scaled to the
+common norm is large in every channel where normal tokens are small); the
+flat-sink workload measures that.  Run: python -m oracle.ablation
 """
 from __future__ import annotations
 
@@ -109,22 +113,26 @@ def run(workload, n_tokens: int, seed: int = 0) -> dict:
         den = np.sqrt((ref ** 2).reshape(n_tokens, -1).sum(1))
         rel = num / np.maximum(den, 1e-30)
         res[var] = {"rel_mean": float(rel.mean()), "rel_p99": float(np.percentile(rel, 99)),
+                    "sink_block_rel_mean": float(rel[4:32].mean()),
                     "attn_err": attention_error(ref, rec, qv, v)}
     return res
 
 
 def main():
     from int2_kv_cache_amd import synth
+    flat = synth.workload(2, ctx=8193)
+    flat.flat_sinks = True
     cases = [("tiny (1 KV head, 4 outlier channels, sigma 0.3)", synth.workload(0), 1024),
              ("Qwen3-8B-shaped (8 KV heads, 4-8 outlier channels, sigma 0.4)", synth.workload(2, ctx=8193), 8192),
+             ("the same with flat sinks", flat, 8192),
              ("multimodal segments (x1 / x5 / x0.3, 0.1% at x30)", synth.workload(4, ctx=12289), 12288)]
     for name, wl, n in cases:
         print(name)
         r = run(wl, n)
         for var in VARIANTS:
             x = r[var]
-            print("  %-9s Key rel. error mean %.4f  p99 %.4f  attention rel. error %.4f"
-                  % (var, x["rel_mean"], x["rel_p99"], x["attn_err"]))
+            print("  %-9s Key rel. error mean %.4f  p99 %.4f  sink block %.4f  attention rel. error %.4f"
+                  % (var, x["rel_mean"], x["rel_p99"], x["sink_block_rel_mean"], x["attn_err"]))
 
 
 if __name__ == "__main__":
