@@ -62,6 +62,7 @@ def lib():
         vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         sig = {
             "orc_f32_to_f16": (ctypes.c_uint16, [f32]),
+            "orc_f32_to_f16_sat": (ctypes.c_uint16, [f32]),
             "orc_f16_to_f32": (f32, [ctypes.c_uint16]),
             "orc_bf16_to_f32": (f32, [ctypes.c_uint16]),
             "orc_to_f16": (None, [vp, i32, sz, vp]),
@@ -83,6 +84,8 @@ def lib():
             "orc_value_row": (None, [vp, i32, i32, i32, vp]),
             "orc_decode_attn": (None, [vp, vp, vp, vp]),
             "orc_decode_attn_one": (None, [vp, vp, i32, i32, vp, vp]),
+            "orc_decode_attn_partial": (None, [vp, vp, i32, i32, i32, i32, vp, vp, vp]),
+            "orc_lse_merge": (None, [i32, vp, vp, vp, vp, vp]),
             "orc_dense_attn": (None, [vp, vp, vp, i32, i32, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
@@ -130,6 +133,26 @@ def f32_to_f16(x) -> np.ndarray:
     x = np.asarray(x, dtype=np.float32).ravel()
     L = lib()
     return np.array([L.orc_f32_to_f16(float(v)) for v in x], dtype=np.uint16)
+
+
+def f32_to_f16_sat(x) -> np.ndarray:
+    """fp32 -> fp16 bits of a stored value: clamped to +-65504, then RNE."""
+    x = np.asarray(x, dtype=np.float32).ravel()
+    L = lib()
+    return np.array([L.orc_f32_to_f16_sat(float(v)) for v in x], dtype=np.uint16)
+
+
+def lse_merge(m: np.ndarray, l: np.ndarray, o: np.ndarray):
+    """Merge split-K partials of one query head: m, l [S] (natural log), o
+    [S][128] (unnormalised).  Returns out [128] fp32 and lse fp32."""
+    m = np.ascontiguousarray(m, np.float64)
+    l = np.ascontiguousarray(l, np.float64)
+    o = np.ascontiguousarray(o, np.float64)
+    assert m.shape == l.shape and o.shape == (m.size, D)
+    out = np.zeros(D, np.float32)
+    lse = np.zeros(1, np.float32)
+    lib().orc_lse_merge(m.size, _p(m), _p(l), _p(o), _p(out), _p(lse))
+    return out, lse[0]
 
 
 def in_to_f16(x: np.ndarray, dtype: int) -> np.ndarray:
@@ -284,6 +307,15 @@ class OracleCache:
         lse = np.zeros(1, np.float32)
         lib().orc_decode_attn_one(self.ref, _p(qrot), b, i, _p(out), _p(lse))
         return out, lse[0]
+
+    def decode_attn_partial(self, qrot: np.ndarray, b: int, i: int, t0: int, t1: int):
+        """Split-K partial over tokens [t0, t1): (m, l, o[128]), fp64."""
+        qrot = np.ascontiguousarray(qrot, dtype=np.float32)
+        m = np.zeros(1, np.float64)
+        l = np.zeros(1, np.float64)
+        o = np.zeros(D, np.float64)
+        lib().orc_decode_attn_partial(self.ref, _p(qrot), b, i, t0, t1, _p(m), _p(l), _p(o))
+        return m[0], l[0], o
 
     # views of the valid state (what parity compares)
     def n(self, b: int) -> int:

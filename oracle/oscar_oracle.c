@@ -57,6 +57,17 @@ uint16_t orc_f32_to_f16(float f)
     return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(m - 1024.0));
 }
 
+/* fp32 -> binary16 for a stored value (a Value row entry, a token norm):
+ * the value is first clamped to the finite binary16 range [-65504, 65504],
+ * then rounded as above, so a stored value is never infinite.  The pages
+ * only say the residual cache holds FP16 ([POP] 三); what happens to a bf16
+ * input beyond FP16's range is a reading: it saturates.  fmaxf returns its
+ * other operand for a NaN, so a NaN input is stored as -65504. */
+uint16_t orc_f32_to_f16_sat(float f)
+{
+    return orc_f32_to_f16(fminf(fmaxf(f, -65504.0f), 65504.0f));
+}
+
 float orc_f16_to_f32(uint16_t h)
 {
     int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
@@ -85,11 +96,12 @@ float orc_in_to_f32(uint16_t x, int dtype)
 }
 
 /* Values enter the cache in fp16 ([POP] 三: the residual cache holds full
- * precision FP16).  bf16/fp16 -> fp32 is exact; fp32 -> fp16 rounds RNE. */
+ * precision FP16).  bf16/fp16 -> fp32 is exact; fp32 -> fp16 saturates and
+ * rounds RNE (orc_f32_to_f16_sat). */
 void orc_to_f16(const uint16_t *x, int dtype, size_t n, uint16_t *out)
 {
     for (size_t i = 0; i < n; i++)
-        out[i] = orc_f32_to_f16(orc_in_to_f32(x[i], dtype));
+        out[i] = orc_f32_to_f16_sat(orc_in_to_f32(x[i], dtype));
 }
 
 /* ------------------------------------------------------------------------ */
@@ -171,7 +183,8 @@ float orc_tree_sumsq(const float *y, int n)
  *                          index h*128 + c.
  *   HEAD scope (variant):  one norm per KV head over its 128 values.
  * r = 1/sqrt(ss) with IEEE fp32 sqrt and divide; k_hat = fp16(y * r);
- * norm = fp16(sqrt(ss)).  ss == 0 gives r = 0, k_hat = 0, norm = 0.
+ * norm = fp16(sqrt(ss)), saturated at 65504 like every stored fp16 value
+ * (|k_hat| <= 1 needs no clamp).  ss == 0 gives r = 0, k_hat = 0, norm = 0.
  * k: [n_tokens][hkv][128]; khat: same shape fp16; norm: TOKEN [n_tokens],
  * HEAD [n_tokens][hkv]. */
 void orc_rotate_scale_key(const uint16_t *k, int dtype, int n_tokens, int hkv,
@@ -193,7 +206,7 @@ void orc_rotate_scale_key(const uint16_t *k, int dtype, int n_tokens, int hkv,
             float r = ss > 0.0f ? 1.0f / s : 0.0f;
             for (int i = 0; i < glen; i++)
                 khat[(size_t)t * w + g * glen + i] = orc_f32_to_f16(y[g * glen + i] * r);
-            norm[(size_t)t * groups + g] = orc_f32_to_f16(s);
+            norm[(size_t)t * groups + g] = orc_f32_to_f16_sat(s);
         }
     }
     free(y);
@@ -232,8 +245,10 @@ void orc_quant_group32(const uint16_t *x16, size_t stride, float *delta,
     for (int t = 0; t < 32; t++) {
         int q = 0;
         if (d > 0.0f) {
-            float r = rintf((x[t] - mn) / d);
-            q = r < 0.0f ? 0 : (r > 3.0f ? 3 : (int)r);
+            /* clamp to [0, 3]; fmaxf maps a NaN quotient (possible only for
+             * non-finite inputs) to 0, so the conversion is always defined */
+            float r = fminf(fmaxf(rintf((x[t] - mn) / d), 0.0f), 3.0f);
+            q = (int)r;
         }
         codes[t] = (uint8_t)q;
     }
@@ -443,15 +458,16 @@ void orc_append_one(orc_cache *c, int b, const uint16_t *k_tok,
     }
     int slot = n % ORC_R;
     uint16_t *khat = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)hkv * ORC_D);
-    uint16_t norm[64];
+    uint16_t *norm = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)hkv);
     orc_rotate_scale_key(k_tok, dtype, 1, hkv, c->norm_scope, khat, norm);
     for (int h = 0; h < hkv; h++) {
         memcpy(ring_k(c, b, h, slot), khat + h * ORC_D, ORC_D * sizeof(uint16_t));
         for (int ch = 0; ch < ORC_D; ch++)
             ring_v_ch(c, b, h, ch)[slot] =
-                orc_f32_to_f16(orc_in_to_f32(v_tok[h * ORC_D + ch], dtype));
+                orc_f32_to_f16_sat(orc_in_to_f32(v_tok[h * ORC_D + ch], dtype));
         *ring_norm(c, b, h, slot) = c->norm_scope == ORC_NORM_TOKEN ? norm[0] : norm[h];
     }
+    free(norm);
     free(khat);
     st[0] = n + 1;
     st[1] = Q;
@@ -574,6 +590,76 @@ void orc_decode_attn_one(const orc_cache *c, const float *qrot, int b, int i,
     if (lse)
         *lse = n > 0 ? (float)(m + log(l)) : -INFINITY;
     free(s);
+}
+
+/* Split-K building blocks (FlashDecoding, the substrate named in [SUM]
+ * 技术新颖性).  A partial over the tokens [t0, t1) of sequence b, query head
+ * i, in fp64 and natural-log units:
+ *   m = max_t s_t,  l = sum_t e^(s_t - m),  o[c] = sum_t e^(s_t - m) v_t[c]
+ * (not normalised); an empty range gives m = -inf, l = 0, o = 0.  The scores
+ * and rows are those of orc_decode_attn_one. */
+void orc_decode_attn_partial(const orc_cache *c, const float *qrot, int b, int i,
+                             int t0, int t1, double *m_out, double *l_out,
+                             double *o_out)
+{
+    const int hq = c->num_q_heads, hkv = c->num_kv_heads;
+    const int h = i / (hq / hkv);
+    const float *q = qrot + ((size_t)b * hq + i) * ORC_D;
+    const int n = t1 > t0 ? t1 - t0 : 0;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double row[ORC_D];
+    double m = -INFINITY, l = 0.0;
+    for (int ch = 0; ch < ORC_D; ch++)
+        o_out[ch] = 0.0;
+    for (int t = 0; t < n; t++) {
+        orc_key_row(c, b, h, t0 + t, row);
+        double dot = 0.0;
+        for (int ch = 0; ch < ORC_D; ch++)
+            dot += (double)q[ch] * row[ch];
+        s[t] = dot / sqrt((double)ORC_D);
+        if (s[t] > m)
+            m = s[t];
+    }
+    for (int t = 0; t < n; t++) {
+        double p = exp(s[t] - m);
+        l += p;
+        orc_value_row(c, b, h, t0 + t, row);
+        for (int ch = 0; ch < ORC_D; ch++)
+            o_out[ch] += p * row[ch];
+    }
+    *m_out = m;
+    *l_out = l;
+    free(s);
+}
+
+/* Cross-split log-sum-exp merge of n_parts partials (m[s], l[s], o[s][128])
+ * of one query head:  M = max_s m_s,  L = sum_s l_s e^(m_s - M),
+ * out = sum_s o_s e^(m_s - M) / L,  lse = M + ln L.  Partials with m = -inf
+ * carry no tokens and weigh 0; all empty gives out = 0, lse = -inf. */
+void orc_lse_merge(int n_parts, const double *m, const double *l,
+                   const double *o, float *out, float *lse)
+{
+    double M = -INFINITY;
+    for (int s = 0; s < n_parts; s++)
+        if (m[s] > M)
+            M = m[s];
+    double L = 0.0, acc[ORC_D];
+    for (int ch = 0; ch < ORC_D; ch++)
+        acc[ch] = 0.0;
+    if (M != -INFINITY) {
+        for (int s = 0; s < n_parts; s++) {
+            if (m[s] == -INFINITY)
+                continue;
+            double w = exp(m[s] - M);
+            L += w * l[s];
+            for (int ch = 0; ch < ORC_D; ch++)
+                acc[ch] += w * o[(size_t)s * ORC_D + ch];
+        }
+    }
+    for (int ch = 0; ch < ORC_D; ch++)
+        out[ch] = M != -INFINITY ? (float)(acc[ch] / L) : 0.0f;
+    if (lse)
+        *lse = M != -INFINITY ? (float)(M + log(L)) : -INFINITY;
 }
 
 /* All sequences and query heads: qrot, out [B][Hq][128]; lse [B][Hq] or NULL. */

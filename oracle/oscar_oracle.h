@@ -63,6 +63,7 @@ typedef struct {
 
 /* number conversions */
 uint16_t orc_f32_to_f16(float f);
+uint16_t orc_f32_to_f16_sat(float f);  /* clamp to +-65504, then round */
 float orc_f16_to_f32(uint16_t h);
 float orc_bf16_to_f32(uint16_t b);
 float orc_in_to_f32(uint16_t x, int dtype);
@@ -115,6 +116,12 @@ void orc_decode_attn(const orc_cache *c, const float *qrot, float *out,
                      float *lse);
 void orc_decode_attn_one(const orc_cache *c, const float *qrot, int b, int i,
                          float *out, float *lse);
+/* split-K pieces: a partial (m, l, o) over tokens [t0, t1), and the merge */
+void orc_decode_attn_partial(const orc_cache *c, const float *qrot, int b, int i,
+                             int t0, int t1, double *m_out, double *l_out,
+                             double *o_out);
+void orc_lse_merge(int n_parts, const double *m, const double *l,
+                   const double *o, float *out, float *lse);
 
 /* unquantized decode attention of one sequence (the BF16 baseline), fp64:
  * q [Hq][128], k and v [n][Hkv][128], out [Hq][128], lse [Hq] or NULL */

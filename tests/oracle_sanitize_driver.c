@@ -126,6 +126,30 @@ int main(void)
     ok &= run_cache(8, 2, ORC_NORM_HEAD, 32, 129, 40, 12);
     ok &= run_cache(8, 8, ORC_NORM_TOKEN, 128, 257, 130, 20);
     ok &= run_cache(4, 1, ORC_NORM_TOKEN, 32, 160, 100, 4);
+    /* more KV heads than any fixed-size buffer of 64 would hold */
+    ok &= run_cache(80, 80, ORC_NORM_HEAD, 32, 40, 2, 4);
+    ok &= run_cache(80, 80, ORC_NORM_TOKEN, 32, 40, 2, 4);
+    /* values beyond fp16's range, non-finite and NaN inputs: saturated on
+     * the way into the cache, no undefined conversion in the quantizer */
+    {
+        const int T = 64, H = 2, D = ORC_D;
+        uint16_t *x = fp16_vec((size_t)T * H * D, 4.0f);
+        const uint16_t odd[] = {0x7c00u, 0xfc00u, 0x7e00u, 0x7bffu, 0xfbffu};
+        for (size_t i = 0; i < (size_t)T * H * D; i += 37)
+            x[i] = odd[(i / 37) % 5];
+        uint16_t *v16 = malloc((size_t)T * H * D * sizeof(uint16_t));
+        orc_to_f16(x, ORC_FP16, (size_t)T * H * D, v16);
+        uint8_t *rec = malloc((size_t)2 * H * ORC_REC_BYTES);
+        uint16_t *pn = malloc((size_t)2 * H * ORC_G * sizeof(uint16_t));
+        uint16_t *nrm = calloc((size_t)T * H, sizeof(uint16_t));
+        orc_quant_pack(x, nrm, x, 2, H, ORC_NORM_HEAD, rec, pn);
+        orc_quant_pack(v16, nrm, v16, 2, H, ORC_NORM_HEAD, rec, pn);
+        free(x);
+        free(v16);
+        free(rec);
+        free(pn);
+        free(nrm);
+    }
     /* unquantized attention (the bf16 baseline), including n = 0 */
     {
         const int n = 77, hq = 8, hkv = 2, D = ORC_D;

@@ -15,13 +15,18 @@ pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
 # ----------------------------------------------------------- conversions
 def test_fp16_from_every_bf16_matches_numpy(orc):
-    """All 65536 bf16 patterns -> fp16 (RNE) agree with numpy's float16."""
+    """All 65536 bf16 patterns -> fp16 (RNE) agree with numpy's float16; as
+    stored Values (saturating: clipped to +-65504 first) they agree with
+    numpy's float16 of the clipped value."""
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     f32 = synth.bits_to_f32(bits, synth.BF16)
     finite = np.isfinite(f32)
+    plain = np.array([orc.lib().orc_f32_to_f16(float(x)) for x in f32[finite]], np.uint16)
+    assert np.array_equal(plain, f32[finite].astype(np.float16).view(np.uint16))
     ours = orc.in_to_f16(bits, orc.BF16)
-    ref = f32.astype(np.float16).view(np.uint16)
+    ref = np.clip(f32, -65504, 65504).astype(np.float16).view(np.uint16)
     assert np.array_equal(ours[finite], ref[finite])
+    assert np.array_equal(ours[np.isinf(f32)], np.where(f32[np.isinf(f32)] > 0, 0x7BFF, 0xFBFF))
 
 
 def test_fp16_roundtrip_every_fp16(orc):
