@@ -91,12 +91,19 @@ typedef enum {
 #define OSCAR_FLAG_BADSTATE 4u  /* a block id outside the pool, or an inconsistent
                                    {n, Q}: the affected work is skipped */
 
-/* Cache geometry (host struct). */
+/* Cache geometry (host struct).  The method's fixed sizes are fields too,
+ * so that a caller states them and a mismatch is an error rather than a
+ * silent reinterpretation: the structured summary "OScaR：…" (方法步骤详情 and
+ * 实验结果) fixes INT2 with 32-token Key blocks and 32-channel Value groups,
+ * and the popular-science article (三) a 128-token fp16 residual window. */
 typedef struct {
     int32_t batch;               /* B sequences */
     int32_t num_q_heads;         /* Hq */
     int32_t num_kv_heads;        /* Hkv; Hq % Hkv == 0, Hq/Hkv in {1,2,4,8} */
-    int32_t head_dim;            /* must be 128 */
+    int32_t head_dim;            /* must be 128 (OSCAR_HEAD_DIM) */
+    int32_t block_tokens;        /* Key quantization block G: must be 32 */
+    int32_t residual_tokens;     /* fp16 residual window R: must be 128 */
+    int32_t v_group;             /* Value quantization group: must be 32 */
     int32_t norm_scope;          /* oscar_norm_scope: TOKEN (default) or HEAD,
                                     which sizes the two norm buffers below */
     int32_t max_blocks_per_seq;  /* block-table row length */
@@ -147,8 +154,13 @@ typedef struct {
     size_t pool, pool_norm, res_k, res_v, res_norm, block_table, seq_state, error_flag;
 } oscar_cache_sizes;
 
-/* Host-only.  Fills *out with the byte size of every cache buffer.
- * EINVAL on a null pointer or an unsupported geometry. */
+/* Host-only infrastructure (no defining passage: the pages fix no memory
+ * layout).  Fills *out with the byte size of every cache buffer.
+ * EINVAL on a null pointer or an unsupported geometry: head_dim != 128,
+ * block_tokens != 32, residual_tokens != 128, v_group != 32, Hq % Hkv != 0,
+ * Hq/Hkv outside {1,2,4,8}, Hkv outside 1..16, batch or block counts < 1,
+ * an unknown norm_scope, flush_tokens outside {0,32,128}, an unknown
+ * key_scale.  Every entry point taking a geometry validates it the same way. */
 OSCAR_API oscar_status oscar_cache_layout(const oscar_cache_geom *geom, oscar_cache_sizes *out);
 
 /* Canalized Rotation and Omni-Token Scaling on a batch of tokens (summary
@@ -161,7 +173,8 @@ OSCAR_API oscar_status oscar_cache_layout(const oscar_cache_geom *geom, oscar_ca
  *             KEY:   y = FHT(x) per head; ss = pairwise-tree sum of squares
  *                    over all heads (TOKEN) or per head (HEAD); khat_out
  *                    [n_tokens][n_heads][128] fp16 = fp16(y * (1/sqrt(ss)));
- *                    norm_out fp16 [n_tokens] (TOKEN) or [n_tokens][n_heads].
+ *                    norm_out fp16 [n_tokens] (TOKEN) or [n_tokens][n_heads],
+ *                    sqrt(ss) saturated at 65504.
  *             KEY_HW_RSQ: KEY with 1/sqrt(ss) from the hardware instruction
  *                    (OSCAR_SCALE_HW_RSQ).
  *   n_heads   >= 1 (QUERY), 1..16 (KEY: the norm spans all heads of a token).
@@ -185,6 +198,8 @@ OSCAR_API oscar_status oscar_rotate_scale(const void *x, oscar_dtype dtype, int3
  * Keys: per channel over the block's 32 tokens; Values: per token over each
  * 32-channel group; delta = (max-min)/3, zero = min, code =
  * clamp(rint((x-zero)/delta), 0, 3) in IEEE fp32, delta == 0 -> code 0.
+ * Inputs must be finite (as every fp16 value the other entry points store
+ * is); an infinite or NaN input gives unspecified codes and parameters.
  * Errors: EINVAL (null, counts out of range, rec_out or v16 not 16-byte
  * aligned). */
 OSCAR_API oscar_status oscar_quant_pack(const void *khat16, const void *knorm16, const void *v16,
@@ -201,7 +216,10 @@ OSCAR_API oscar_status oscar_quant_pack(const void *khat16, const void *knorm16,
  *                    drop the append if (Q+F)/32 > max_blocks_per_seq); Q += F;
  *   rotate+scale k_new[b], store k_hat, norm and fp16(v_new[b]) in slot
  *   n % 128; n += 1.
- *   k_new, v_new  device, [B][Hkv][128] fp16 or bf16.
+ * Stored fp16 values saturate: a Value entry or a norm beyond +-65504
+ * (+-inf included) is stored as +-65504, a NaN Value as -65504; |k_hat| <= 1.
+ *   k_new, v_new  device, [B][Hkv][128] fp16 or bf16; Keys must be finite
+ *                 with a sum of squares below fp32's range.
  * Errors: EINVAL. */
 OSCAR_API oscar_status oscar_append_kv(const oscar_cache_geom *geom, const oscar_cache *cache,
                              const void *k_new, const void *v_new, oscar_dtype dtype,
@@ -210,7 +228,8 @@ OSCAR_API oscar_status oscar_append_kv(const oscar_cache_geom *geom, const oscar
 /* Bulk prefill of an empty sequence `seq` with n_tokens tokens (reading notes,
  * End-to-End Flow: prefill Keys pass FHT, per-token scaling and INT2
  * per-channel quantization before entering the cache).  The resulting cache
- * state is byte-identical, on its valid region, to n_tokens appends.
+ * state is byte-identical, on its valid region, to n_tokens appends
+ * (saturation included).
  *   k, v  device, [n_tokens][Hkv][128] fp16 or bf16, 16-byte aligned.
  * Errors: EINVAL (also when the blocks needed exceed max_blocks_per_seq, or
  * k / v are not 16-byte aligned);
@@ -219,8 +238,11 @@ OSCAR_API oscar_status oscar_prefill_quantize(const oscar_cache_geom *geom, cons
                                     int32_t seq, const void *k, const void *v,
                                     int32_t n_tokens, oscar_dtype dtype, void *stream);
 
-/* Split count the library would pick for max_ctx (num_splits == 0) and the
- * workspace bytes decode attention needs with that split count. */
+/* Infrastructure (no defining passage): the split count the library would
+ * pick for max_ctx (num_splits == 0) and the workspace bytes decode attention
+ * needs with that split count.  Host-only.
+ * Errors: EINVAL (bad geometry, null bytes, max_ctx < 0, num_splits outside
+ * 0..1024). */
 OSCAR_API oscar_status oscar_decode_workspace_bytes(const oscar_cache_geom *geom, int32_t max_ctx,
                                           int32_t num_splits, int32_t *splits_out,
                                           size_t *bytes);
@@ -235,11 +257,21 @@ OSCAR_API oscar_status oscar_decode_workspace_bytes(const oscar_cache_geom *geom
  *            kernel), or fp32 already-rotated q' (dtype OSCAR_FP32).
  *   out      device, [B][Hq][128] fp32 (rotated-V basis).
  *   lse      device, [B][Hq] fp32 log-sum-exp of the scaled scores, or NULL.
- *   workspace device, >= oscar_decode_workspace_bytes(...) bytes, 256-B aligned:
- *            per-split partials (m, l, o); no contents carried between calls.
+ *   workspace device, >= oscar_decode_workspace_bytes(...) bytes, 256-B aligned,
+ *            zero-filled by the caller once, before its first use.  Its
+ *            first 256 KiB hold one arrival counter per (sequence, KV head)
+ *            for the cross-split merge that the launch does itself (B * Hkv
+ *            <= 65536); every call leaves them zero again, so the workspace
+ *            stays valid for any later call whose size fits (any geometry or
+ *            split count).  The rest holds the per-split partials (m, l, o),
+ *            rewritten by every call.  Two calls in flight at the same time
+ *            must not share a workspace.
  *   num_splits  0 = pick from max_ctx; else 1..1024 splits per (b, KV head).
+ *   variant  AUTO / MFMA: one launch (matrix-core attention; the last split
+ *            of each (b, KV head) to finish merges all of them); VALU: the
+ *            vector-ALU kernel and a separate merge launch.
  *   max_ctx  an upper bound on every sequence's n (used to size the split).
- * Errors: EINVAL, EWORKSPACE, ELAUNCH. */
+ * Errors: EINVAL (also B * Hkv > 65536), EWORKSPACE, ELAUNCH. */
 OSCAR_API oscar_status oscar_decode_attn(const oscar_cache_geom *geom, const oscar_cache *cache,
                                const void *q, oscar_dtype q_dtype, float *out, float *lse,
                                void *workspace, size_t ws_bytes, int32_t num_splits,
@@ -273,8 +305,10 @@ OSCAR_API oscar_status oscar_dense_write_kv(const oscar_cache_geom *geom, void *
                                   const void *k, const void *v, int32_t n_tokens,
                                   int32_t *error_flag, void *stream);
 
-/* Split count the bf16 kernel would pick for max_ctx (num_splits == 0) and
- * the workspace bytes it needs with that split count. */
+/* Infrastructure (no defining passage): the split count the bf16 kernel
+ * would pick for max_ctx (num_splits == 0) and the workspace bytes it needs
+ * with that split count.  Host-only; errors as for
+ * oscar_decode_workspace_bytes. */
 OSCAR_API oscar_status oscar_dense_workspace_bytes(const oscar_cache_geom *geom, int32_t max_ctx,
                                          int32_t num_splits, int32_t *splits_out,
                                          size_t *bytes);
@@ -297,7 +331,8 @@ OSCAR_API oscar_status oscar_dense_decode_attn(const oscar_cache_geom *geom, con
                                      int32_t num_splits, int32_t max_ctx, int32_t *error_flag,
                                      void *stream);
 
-/* Static string for a status code. */
+/* Infrastructure (no defining passage): a static, never-freed string naming
+ * a status code ("unknown status" for any other value).  Host-only. */
 OSCAR_API const char *oscar_status_str(oscar_status s);
 
 #ifdef __cplusplus

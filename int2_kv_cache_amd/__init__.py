@@ -24,7 +24,7 @@ ROT_QUERY, ROT_KEY, ROT_KEY_HW_RSQ = 0, 1, 2
 SCALE_IEEE, SCALE_HW_RSQ = 0, 1
 ATTN_AUTO, ATTN_VALU, ATTN_MFMA = 0, 1, 2
 FLAG_CAPACITY, FLAG_NONEMPTY, FLAG_BADSTATE = 1, 2, 4
-HEAD_DIM, BLOCK_TOKENS, RESIDUAL_TOKENS, RECORD_BYTES = 128, 32, 128, 3072
+HEAD_DIM, BLOCK_TOKENS, RESIDUAL_TOKENS, V_GROUP, RECORD_BYTES = 128, 32, 128, 32, 3072
 
 API = ("oscar_cache_layout", "oscar_rotate_scale", "oscar_quant_pack", "oscar_append_kv",
        "oscar_prefill_quantize", "oscar_decode_workspace_bytes", "oscar_decode_attn",
@@ -41,6 +41,8 @@ class OscarError(RuntimeError):
 class Geom(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_tokens", ctypes.c_int32), ("residual_tokens", ctypes.c_int32),
+                ("v_group", ctypes.c_int32),
                 ("norm_scope", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_physical_blocks", ctypes.c_int32), ("flush_tokens", ctypes.c_int32),
                 ("key_scale", ctypes.c_int32)]
@@ -118,9 +120,11 @@ def _stream(stream=None):
 
 def make_geom(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, num_physical_blocks,
               norm_scope=NORM_TOKEN, head_dim=HEAD_DIM, flush_tokens=32,
-              key_scale=SCALE_IEEE) -> Geom:
-    return Geom(batch, num_q_heads, num_kv_heads, head_dim, norm_scope, max_blocks_per_seq,
-                num_physical_blocks, flush_tokens, key_scale)
+              key_scale=SCALE_IEEE, block_tokens=BLOCK_TOKENS,
+              residual_tokens=RESIDUAL_TOKENS, v_group=V_GROUP) -> Geom:
+    return Geom(batch, num_q_heads, num_kv_heads, head_dim, block_tokens, residual_tokens,
+                v_group, norm_scope, max_blocks_per_seq, num_physical_blocks, flush_tokens,
+                key_scale)
 
 
 def cache_layout(geom: Geom) -> CacheSizes:
@@ -203,6 +207,42 @@ def decode_attn(cache: DeviceCache, q, q_dtype: int, out, lse, workspace, max_ct
     _check("oscar_decode_attn", lib().oscar_decode_attn(
         ctypes.byref(cache.geom), ctypes.byref(cache.bufs), _ptr(q), q_dtype, _ptr(out),
         _ptr(lse), _ptr(workspace), nbytes, num_splits, max_ctx, variant, _stream(stream)))
+
+
+# ---------------------------------------------------------------- prepared calls
+
+class PreparedCall:
+    """One C-ABI call whose arguments were marshalled once: calling it only
+    crosses into the library.  The tensors it was prepared with must stay
+    alive and in place (their device addresses are baked in), and the
+    stream is fixed at preparation."""
+    __slots__ = ("fn", "name", "args")
+
+    def __init__(self, name: str, args: tuple):
+        self.fn = getattr(lib(), name)
+        self.name = name
+        self.args = args
+
+    def __call__(self):
+        s = self.fn(*self.args)
+        if s != OK:
+            raise OscarError(self.name, s)
+
+
+def prepare_append_kv(cache: DeviceCache, k_new, v_new, dtype: int, stream=None) -> PreparedCall:
+    return PreparedCall("oscar_append_kv", (
+        ctypes.byref(cache.geom), ctypes.byref(cache.bufs), _ptr(k_new), _ptr(v_new), dtype,
+        _stream(stream)))
+
+
+def prepare_decode_attn(cache: DeviceCache, q, q_dtype: int, out, lse, workspace, max_ctx: int,
+                        num_splits: int = 0, variant: int = ATTN_AUTO,
+                        stream=None) -> PreparedCall:
+    nbytes = workspace.numel() * workspace.element_size()
+    return PreparedCall("oscar_decode_attn", (
+        ctypes.byref(cache.geom), ctypes.byref(cache.bufs), _ptr(q), q_dtype, _ptr(out),
+        _ptr(lse), _ptr(workspace), ctypes.c_size_t(nbytes), num_splits, max_ctx, variant,
+        _stream(stream)))
 
 
 # ---------------------------------------------------------------- bf16 baseline

@@ -26,7 +26,9 @@ oscar_status check_device() {
 
 oscar_status check_geom(const oscar_cache_geom* g) {
   if (!g) return OSCAR_EINVAL;
-  if (g->head_dim != OSCAR_HEAD_DIM) return OSCAR_EINVAL;
+  if (g->head_dim != OSCAR_HEAD_DIM || g->block_tokens != OSCAR_BLOCK_TOKENS ||
+      g->residual_tokens != OSCAR_RESIDUAL_TOKENS || g->v_group != OSCAR_V_GROUP)
+    return OSCAR_EINVAL;
   if (g->batch < 1 || g->num_kv_heads < 1 || g->num_kv_heads > 16) return OSCAR_EINVAL;
   if (g->num_q_heads < g->num_kv_heads || g->num_q_heads % g->num_kv_heads) return OSCAR_EINVAL;
   const int grp = g->num_q_heads / g->num_kv_heads;

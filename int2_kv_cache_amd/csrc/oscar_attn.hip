@@ -37,6 +37,12 @@ struct AttnArgs {
   int32_t* error_flag;
   float2* ws_ml;  // [B][Hq][S] (m, l)
   float* ws_o;    // [B][Hq][S][128]
+  // arrival counters of the cross-split merge, [B][Hkv]: zero before a
+  // launch, and zero again after it (the merging workgroup resets its own)
+  int32_t* counters;
+  float* out;     // [B][Hq][128]
+  float* lse;     // [B][Hq] or null
+  int merge_in_kernel;  // 0: partials only, a separate launch merges them
 };
 
 // The 32 token norms of block p for KV head h, and window slot 0 of (b, h).
@@ -504,10 +510,36 @@ __device__ __forceinline__ void progress_prio(int k, int cnt) {
     __builtin_amdgcn_s_setprio(0);
 }
 
-template <int GRP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
+// Agent-scope (whole device) relaxed atomic stores and loads of fp32: they
+// go to the device's coherence point (global_store / global_load with sc1),
+// so a workgroup on another XCD, whose L2 is a different cache, reads what
+// they wrote without any cache write-back or invalidation.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroups of NW waves (NW = 12: one workgroup fills a CU with three waves
+// per SIMD; NW = 4 or 6: three or two workgroups share a CU).  The grid is
+// one-dimensional, B * Hkv * S workgroups, workgroup (b * Hkv + h) * S + s.
+// The dispatcher deals consecutive workgroup ids round-robin to the eight
+// XCDs, so consecutive splits of one (sequence, KV head) land on different
+// XCDs and every XCD gets an even share of every sequence, ragged or not.
+//
+// PUB selects how a split's partial is published to the merging workgroup:
+// 0 = ordinary stores with an agent-scope release (the arrival counter's
+// read-modify-write) and acquire (a fence in the merging workgroup); 1 =
+// agent-scope atomic stores and loads (coherent at the device level by
+// themselves), each wave waiting for its stores to complete before the
+// workgroup counts itself in.
+template <int GRP, int NW, int PUB>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void attn_mfma_kernel(AttnArgs A) {
   static_assert(GRP == 1 || GRP == 2 || GRP == 4 || GRP == 8, "group size");
+  static_assert(NW == 4 || NW == 6 || NW == 12, "waves per workgroup");
+  constexpr int NT = 64 * NW;
   constexpr int NCOL = 2 * GRP;                 // used B columns (hi + lo)
   constexpr int TPL = GRP >= 2 ? GRP / 2 : 1;   // softmax tokens per lane
   constexpr int LPH = 32 / TPL;                 // softmax lanes per head
@@ -524,20 +556,23 @@ void attn_mfma_kernel(AttnArgs A) {
   // order, and a wave's LDS operations complete in order)
   constexpr int kTileBytes = 4 * 8 * GRP * 16;
   static_assert(2 * GRP * kRowPad * 4 <= kTileBytes, "scores and probabilities fit a tile");
-  __shared__ __attribute__((aligned(16))) uint8_t lds_tile[4][kTileBytes];
-  __shared__ float lds_fac[4][GRP];                      // per wave: rescale factors
-  __shared__ float lds_zs[4][4][GRP];                    // per wave: Value zero-point sums
-  __shared__ float lds_ml[2][4][GRP];                    // per wave: final (m, l)
+  __shared__ __attribute__((aligned(16))) uint8_t lds_tile[NW][kTileBytes];
+  __shared__ float lds_fac[NW][GRP];                     // per wave: rescale factors
+  __shared__ float lds_zs[NW][4][GRP];                   // per wave: Value zero-point sums
+  __shared__ float lds_ml[2][NW][GRP];                   // per wave: final (m, l)
   // the two stages of each wave's record pipeline; after the loop they hold
   // the waves' partial outputs for the merge
-  __shared__ __attribute__((aligned(16))) uint8_t stage0[4][kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t stage1[4][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[NW][kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[NW][kStage];
+  __shared__ int lds_last;
 
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wid = static_cast<int>(blockIdx.x);
+  const int pair = wid / A.splits, s = wid - pair * A.splits;
+  const int b = pair / A.hkv, h = pair - b * A.hkv;
   // wave index as a wave-uniform (scalar) value: unit indices and record
   // addresses then stay in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), L = tid & 63;
-  typedef u32x4 BTiles[4][8 * GRP];
+  typedef u32x4 BTiles[4][8 * GRP];   // [K step][row]
   typedef float Rows[GRP][kRowPad];
   BTiles& Wbk = *reinterpret_cast<BTiles*>(lds_tile[wave]);
   BTiles& Wbv = *reinterpret_cast<BTiles*>(lds_tile[wave]);
@@ -567,12 +602,12 @@ void attn_mfma_kernel(AttnArgs A) {
   const bool sm_on = sm_head < GRP;
   const int krow = brow_k<NCOL>((col % NCOL) + NCOL * g4), vrow = brow_v<NCOL>((col % NCOL) + NCOL * g4);
 
-  // The wave's units are u = first + 4k.  The first cnt are INT2 blocks; at
-  // most one more (k = cnt) is a chunk of the fp16 window, since the window
-  // spans at most 4 consecutive units.
+  // The wave's units are u = first + NW k.  The first cnt are INT2 blocks;
+  // at most one more (k = cnt) is a chunk of the fp16 window, since the
+  // window spans at most 4 consecutive units and NW >= 4.
   const int first = u0 + wave;
-  const int n_units = u1 > first ? (u1 - first + 3) / 4 : 0;
-  const int cnt = nb > first ? min(n_units, (nb - first + 3) / 4) : 0;
+  const int n_units = u1 > first ? (u1 - first + NW - 1) / NW : 0;
+  const int cnt = nb > first ? min(n_units, (nb - first + NW - 1) / NW) : 0;
   const bool has_ring = n_units > cnt;
 
   // Physical block ids of the wave's INT2 blocks, 64 at a time: lane j holds
@@ -581,18 +616,18 @@ void attn_mfma_kernel(AttnArgs A) {
   const int* tab = A.block_table + static_cast<size_t>(b) * A.max_blocks + first;
   auto load_ids = [&](int k0) {
     int id = 0;
-    if (L < cnt - k0) id = tab[4 * (k0 + L)];
+    if (L < cnt - k0) id = tab[NW * (k0 + L)];
     const bool bad = static_cast<unsigned>(id) >= static_cast<unsigned>(A.nphys);
     if (__any(bad) && L == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
     return bad ? 0 : id;
   };
-  // The query heads of this wave (wave, wave + 4) load first: their latency
+  // The query heads of this wave (wave, wave + NW) load first: their latency
   // overlaps the block-table read and the first record's.
-  constexpr int QPW = (GRP + 3) / 4;
+  constexpr int QPW = (GRP + NW - 1) / NW;
   float qx[QPW], qy[QPW];
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
-    const int i = wave + 4 * j;
+    const int i = wave + NW * j;
     qx[j] = qy[j] = 0.0f;
     if (i < GRP) {
       const size_t base = (static_cast<size_t>(b) * A.hq + h * GRP + i) * kD;
@@ -625,6 +660,29 @@ void attn_mfma_kernel(AttnArgs A) {
   };
   auto unit_nrm = [&](int p) { return rsrc(block_norms(A, p, h), 64); };
 
+  // The wave's chunk of the fp16 window (if any) is its first unit: its
+  // loads go out before the records' copies, so that waiting for them does
+  // not wait for the copies (vector loads complete in order).
+  const int ring_tb = Q + kG * (first + NW * cnt - nb);
+  const int ring_valid = has_ring ? min(32, n - ring_tb) : 0;
+  u32x4 rk[2][4], rv[8];
+  float rnt[TPL];
+  if (has_ring) {
+    const int slot0 = ring_tb % kR;  // a multiple of 32: the chunk is 32 consecutive slots
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        rk[tau][kk] = *reinterpret_cast<const u32x4*>(
+            A.res_k + (bh * kR + slot0 + 16 * tau + col) * kD + 32 * g4 + 8 * kk);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      rv[ct] = *reinterpret_cast<const u32x4*>(A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
+#pragma unroll
+    for (int j = 0; j < TPL; ++j)
+      rnt[j] = f16_to_f32(window_norms(A, b, h)[slot0 + ((sm_t0 + j) & 31)]);
+  }
+
   // Block j of the wave goes through stage j % 2.  Its DMA is issued two
   // blocks ahead (unconditionally: past the end it re-reads the last block)
   // so that two records are in flight while one is processed.
@@ -640,7 +698,7 @@ void attn_mfma_kernel(AttnArgs A) {
 
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
-    const int i = wave + 4 * j;
+    const int i = wave + NW * j;
     if (i < GRP) {
       if (A.q_mode != 2) fht128_wave(qx[j], qy[j]);
       // q' carries the score scale 1/sqrt(128) * log2(e): every score
@@ -763,21 +821,11 @@ void attn_mfma_kernel(AttnArgs A) {
 
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Alpha unit c: head c % GRP, channels c0 .. c0+7 with
-  // c0 = 32 ((c / GRP) & 3) + 8 (c / (4 GRP)); slot i holds channel c0 + s(i).
-  float qa[NR][8];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const int c = L + 64 * r;
-    const int hh = c % GRP, c0 = 32 * ((c / GRP) & 3) + 8 * ((c / (4 * GRP)) & 3);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qa[r][i] = qs[hh * kD + c0 + slot_pos(i)];
-  }
-  // the softmax lane's share of q'.z
-  float zq[CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) zq[j] = sm_on ? qs[sm_head * kD + sm_c0 + j] : 0.0f;
 
+
+  // the INT2 blocks' per-lane query operands (filled after the window chunk)
+  float qa[NR][8];
+  float zq[CPL];
 
   // ---------------- quantized blocks, software-pipelined one block ahead
   auto process_int2 = [&](const UnitRegs<NR, CPL>& cur, auto&& after_qk, auto&& after_softmax) {
@@ -839,6 +887,53 @@ void attn_mfma_kernel(AttnArgs A) {
       o[2 * d + 1] = mfma_f16(code_tile<1>(e, od), bvd, o[2 * d + 1]);
     }
   };
+  // ---------------- the fp16 window chunk, first (its loads were issued
+  // before the records' copies; splits weigh a chunk as kRingWeight blocks)
+  if (has_ring) {
+    // q' hi/lo B tiles, channels 32 g4 + 8 kk + 0..7 in natural order
+    u32x4 bq[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      float x[8];
+      const float* q = qs + (col % GRP) * kD + 32 * g4 + 8 * kk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = q[i];
+      u32x4 hi, lo;
+      split8(x, hi, lo);
+      bq[kk] = col < GRP ? hi : lo;  // columns >= 2 GRP are unused
+    }
+    f32x4 cs[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mfma_f16(rk[tau][kk], bq[kk], acc);
+      cs[tau] = acc;
+    }
+    store_scores(cs);
+    softmax_block(rnt, 0.0f, ring_valid, true);
+    pv_tiles(nullptr);
+    const u32x4 b0 = Wbv[0][vrow];
+    lds_order();  // the INT2 blocks write this tile region next
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) o[ct] = mfma_f16(rv[ct], b0, o[ct]);
+  }
+
+  // The INT2 blocks' query operands, read from LDS once the window chunk's
+  // registers are dead.
+  // Alpha unit c: head c % GRP, channels c0 .. c0+7 with
+  // c0 = 32 ((c / GRP) & 3) + 8 (c / (4 GRP)); slot i holds channel c0 + s(i).
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int c = L + 64 * r;
+    const int hh = c % GRP, c0 = 32 * ((c / GRP) & 3) + 8 * ((c / (4 * GRP)) & 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qa[r][i] = qs[hh * kD + c0 + slot_pos(i)];
+  }
+  // the softmax lane's share of q'.z
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) zq[j] = sm_on ? qs[sm_head * kD + sm_c0 + j] : 0.0f;
+
   // One register set: block k + 1 is read from its stage into it in two
   // halves while block k is processed (Key part after k's softmax, Value part
   // after k's P.V); block k's stage is refilled with block k + 2 once k's
@@ -882,55 +977,6 @@ void attn_mfma_kernel(AttnArgs A) {
   }
   __builtin_amdgcn_s_setprio(0);
 
-  // ---------------- the fp16 window chunk, last (its loads are issued here,
-  // when the INT2 registers are free; splits weigh a chunk as kRingWeight
-  // blocks to make up for the exposed latency)
-  if (has_ring) {
-    const int tb = Q + kG * (first + 4 * cnt - nb);
-    const int ring_valid = n - tb < 32 ? n - tb : 32;
-    const int slot0 = tb % kR;  // a multiple of 32: the chunk is 32 consecutive slots
-    u32x4 rk[2][4], rv[8];
-    float rnt[TPL];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        rk[tau][kk] = *reinterpret_cast<const u32x4*>(
-            A.res_k + (bh * kR + slot0 + 16 * tau + col) * kD + 32 * g4 + 8 * kk);
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-      rv[ct] = *reinterpret_cast<const u32x4*>(A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
-#pragma unroll
-    for (int j = 0; j < TPL; ++j)
-      rnt[j] = f16_to_f32(window_norms(A, b, h)[slot0 + ((sm_t0 + j) & 31)]);
-    // q' hi/lo B tiles, channels 32 g4 + 8 kk + 0..7 in natural order
-    u32x4 bq[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      float x[8];
-      const float* q = qs + (col % GRP) * kD + 32 * g4 + 8 * kk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = q[i];
-      u32x4 hi, lo;
-      split8(x, hi, lo);
-      bq[kk] = col < GRP ? hi : lo;  // columns >= 2 GRP are unused
-    }
-    f32x4 cs[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = mfma_f16(rk[tau][kk], bq[kk], acc);
-      cs[tau] = acc;
-    }
-    store_scores(cs);
-    softmax_block(rnt, 0.0f, ring_valid, cnt == 0);
-    pv_tiles(nullptr);
-    const u32x4 b0 = Wbv[0][vrow];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) o[ct] = mfma_f16(rv[ct], b0, o[ct]);
-  }
-
   // ---------------- this wave's partial: l, Z, o for each head
   const float lsum = group_sum<LPH>(l_part);
 #pragma unroll
@@ -966,38 +1012,138 @@ void attn_mfma_kernel(AttnArgs A) {
   }
   __syncthreads();
 
-  // ---------------- merge the 4 waves into this split's partial
-  const size_t pbase = (static_cast<size_t>(b) * A.hq + h * GRP) * A.splits;
-  // every operand is read before any is combined (no branch between the
-  // LDS reads); a wave with no tokens has m = -inf and weight 0
-  constexpr int NI = (GRP * kD + 255) / 256;
-  float mw[NI][4], lw[NI][4], ow[NI][4];
+  // ---------------- merge the NW waves into this split's partial
+  const int S = A.splits;
+  const size_t pbase = (static_cast<size_t>(b) * A.hq + h * GRP) * S;
+  constexpr int NI = (GRP * kD + NT - 1) / NT;
+  float Mi[NI], Li[NI], Oi[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int idx = tid + 256 * i, hh = (idx >> 7) % GRP, c = idx & 127;
+    const int idx = tid + NT * i, hh = (idx >> 7) % GRP, c = idx & 127;
+    // every operand is read before any is combined; a wave with no tokens
+    // has m = -inf and weight 0
+    float mw[NW], lw[NW], ow[NW];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      mw[i][w] = lds_ml[0][w][hh];
-      lw[i][w] = lds_ml[1][w][hh];
-      ow[i][w] = wo_at(w, hh)[c];
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = lds_ml[0][w][hh];
+      lw[w] = lds_ml[1][w][hh];
+      ow[w] = wo_at(w, hh)[c];
     }
-  }
+    float M = mw[0];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int idx = tid + 256 * i, hh = idx >> 7, c = idx & 127;
-    if (idx >= GRP * kD) break;
-    const float M = fmaxf(fmaxf(mw[i][0], mw[i][1]), fmaxf(mw[i][2], mw[i][3]));
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, mw[w]);
     float Lw = 0.0f, Ow = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float sc = mw[i][w] == -INFINITY ? 0.0f : exp2f(mw[i][w] - M);
-      Lw += sc * lw[i][w];
-      Ow += sc * ow[i][w];
+    for (int w = 0; w < NW; ++w) {
+      const float sc = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - M);
+      Lw += sc * lw[w];
+      Ow += sc * ow[w];
     }
-    const size_t part = pbase + static_cast<size_t>(hh) * A.splits + s;
-    A.ws_o[part * kD + c] = Ow;
-    if (c == 0) A.ws_ml[part] = make_float2(M, Lw);
+    Mi[i] = M;
+    Li[i] = Lw;
+    Oi[i] = Ow;
   }
+  // out = o / l, lse = (m + log2 l) ln 2 (scores are in log2 units); a
+  // (sequence, head) with no tokens gets zeros and -inf
+  auto finish = [&](int idx, float M, float Lw, float Ow) {
+    const int hh = idx >> 7, c = idx & 127;
+    const size_t row = static_cast<size_t>(b) * A.hq + h * GRP + hh;
+    const bool empty = M == -INFINITY;
+    A.out[row * kD + c] = empty ? 0.0f : Ow * (1.0f / Lw);
+    if (c == 0 && A.lse) A.lse[row] = empty ? -INFINITY : (M + log2f(Lw)) * 0.6931471805599453f;
+  };
+  if (S == 1) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (tid + NT * i < GRP * kD) finish(tid + NT * i, Mi[i], Li[i], Oi[i]);
+    return;
+  }
+
+  // ---------------- cross-split merge, in this launch: every split publishes
+  // its partial and counts itself in; the last of the S to arrive merges
+  // all S partials, in split order (the result does not depend on which
+  // workgroup that is), and resets the counter for the next launch.
+  float* ml = reinterpret_cast<float*>(A.ws_ml);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = tid + NT * i, hh = idx >> 7, c = idx & 127;
+    if (idx >= GRP * kD) break;
+    const size_t part = pbase + static_cast<size_t>(hh) * S + s;
+    if constexpr (PUB == 1) {
+      store_dev(A.ws_o + part * kD + c, Oi[i]);
+      if (c == 0) {
+        store_dev(ml + 2 * part, Mi[i]);
+        store_dev(ml + 2 * part + 1, Li[i]);
+      }
+    } else {
+      A.ws_o[part * kD + c] = Oi[i];
+      if (c == 0) A.ws_ml[part] = make_float2(Mi[i], Li[i]);
+    }
+  }
+  if (!A.merge_in_kernel) return;
+  // every wave's stores have completed (reached the L2, or with PUB 1 the
+  // device's coherence point) before the workgroup counts itself in
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __syncthreads();
+  if (tid == 0) {
+    int prev;
+    if constexpr (PUB == 1)
+      prev = __hip_atomic_fetch_add(A.counters + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      prev = __hip_atomic_fetch_add(A.counters + pair, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    lds_last = prev == S - 1;
+  }
+  __syncthreads();
+  // (PUB 0: the counter's acquire, on this workgroup's CU, precedes the
+  // barrier that every thread passed before reading the partials)
+  if (!lds_last) return;
+  // all of a thread's partials are requested at once (one round trip for
+  // up to 32 splits at one output per thread)
+  constexpr int kChunk = NI == 1 ? 32 : 16;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int idx = tid + NT * i, hh = idx >> 7, c = idx & 127;
+    if (idx >= GRP * kD) break;
+    const size_t base = pbase + static_cast<size_t>(hh) * S;
+    float M = -INFINITY, Lw = 0.0f, Ow = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += kChunk) {
+      float mc[kChunk], lc[kChunk], oc[kChunk];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const int sj = s0 + j;
+        mc[j] = -INFINITY;
+        lc[j] = oc[j] = 0.0f;
+        if (sj < S) {
+          if constexpr (PUB == 1) {
+            mc[j] = load_dev(ml + 2 * (base + sj));
+            lc[j] = load_dev(ml + 2 * (base + sj) + 1);
+            oc[j] = load_dev(A.ws_o + (base + sj) * kD + c);
+          } else {
+            const float2 v = A.ws_ml[base + sj];
+            mc[j] = v.x;
+            lc[j] = v.y;
+            oc[j] = A.ws_o[(base + sj) * kD + c];
+          }
+        }
+      }
+      float mb = M;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) mb = fmaxf(mb, mc[j]);
+      if (mb == -INFINITY) continue;
+      const float f = M == -INFINITY ? 0.0f : exp2f(M - mb);
+      Lw *= f;
+      Ow *= f;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const float w = mc[j] == -INFINITY ? 0.0f : exp2f(mc[j] - mb);
+        Lw += w * lc[j];
+        Ow += w * oc[j];
+      }
+      M = mb;
+    }
+    finish(idx, M, Lw, Ow);
+  }
+  if (tid == 0) __hip_atomic_store(A.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- reduce
@@ -1086,28 +1232,61 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(const float2* __restric
   }
 }
 
-int auto_splits(const oscar_cache_geom* g, int max_ctx) {
-  // about three 4-wave workgroups per CU on 256 CUs while that leaves a
-  // workgroup 32 blocks or more, else two per CU (fewer partials and waves
-  // when each wave has only a few blocks: measured 20.2 vs 21.3 us at 32K,
-  // 25.9 vs 26.6 us at 64K); at least 4 blocks per workgroup; where a
-  // workgroup would hold 256 blocks or more, twice as many workgroups (two
-  // rounds: the dispatcher's refill evens out ragged sequences and uneven
-  // CUs; measured 5 % faster on 48 sequences of 8K..32K)
+// Build-time overrides of the launch shape, for A/B timing of alternatives
+// (0 = chosen per call below).
+#ifndef OSCAR_ATTN_NW
+#define OSCAR_ATTN_NW 0
+#endif
+#ifndef OSCAR_ATTN_PUB
+#define OSCAR_ATTN_PUB 1
+#endif
+
+// Launch shape of the matrix-core kernel: waves per workgroup and splits per
+// (sequence, KV head).  The chip holds 256 CUs x 12 waves at three waves per
+// SIMD.  Few (sequence, KV head) pairs: one 12-wave workgroup per CU, as
+// many splits as fill all 256 CUs once (a CU left idle costs its share of the
+// bandwidth), while every wave still gets a unit.  Many pairs: three 4-wave
+// workgroups per CU, and twice that many splits where a workgroup would
+// otherwise hold 256 blocks or more (two rounds: the dispatcher's refill
+// evens out ragged sequences).
+struct AttnShape {
+  int nw, splits, merge_in_kernel;
+};
+#ifndef OSCAR_ATTN_MERGE_MANY
+#define OSCAR_ATTN_MERGE_MANY 1   // merge in the kernel also with many pairs
+#endif
+AttnShape attn_shape(const oscar_cache_geom* g, int max_ctx, int num_splits) {
   const int units = (max_ctx + kG - 1) / kG + 1;
   const int pairs = g->batch * g->num_kv_heads;
-  int s = (768 + pairs - 1) / pairs;
-  if (units / s < 32) s = (512 + pairs - 1) / pairs;
-  if (units / s >= 256) s *= 2;
-  const int cap = units / 4 > 1 ? units / 4 : 1;
-  if (s > cap) s = cap;
-  if (s > 1024) s = 1024;
-  return s < 1 ? 1 : s;
+  int nw = OSCAR_ATTN_NW ? OSCAR_ATTN_NW : (pairs >= 128 ? 4 : 12);
+  int s = num_splits;
+  if (!s) {
+    s = (256 * (12 / nw) + pairs - 1) / pairs;
+    if (nw == 4 && units / s >= 256) s *= 2;
+    const int cap = units / (nw == 12 ? nw : 4 * nw) > 1 ? units / (nw == 12 ? nw : 4 * nw) : 1;
+    if (s > cap) s = cap;
+    if (s > 1024) s = 1024;
+    if (s < 1) s = 1;
+  }
+  return AttnShape{nw, s, (pairs >= 128 && !OSCAR_ATTN_MERGE_MANY) ? 0 : 1};
 }
+int auto_splits(const oscar_cache_geom* g, int max_ctx) { return attn_shape(g, max_ctx, 0).splits; }
 
+// Workspace of the matrix-core path: the merge's arrival counters first, at
+// a fixed place and size (one int32 per (sequence, KV head), for up to
+// kMaxPairs pairs), so that a workspace zero-filled once stays valid for any
+// later call whatever its geometry or split count; then the partials in the
+// layout the separate merge launch reads (workspace_bytes below).
+constexpr int kMaxPairs = 65536;
+constexpr size_t kCounterBytes = static_cast<size_t>(kMaxPairs) * sizeof(int32_t);
+
+// Partials: ws_ml [B][Hq][S] float2, then (256-B aligned) ws_o [B][Hq][S][128].
 size_t workspace_bytes(const oscar_cache_geom* g, int splits) {
   const size_t n = static_cast<size_t>(g->batch) * g->num_q_heads * splits;
-  return n * sizeof(float2) + n * kD * sizeof(float) + 256;
+  return ((n * sizeof(float2) + 255) / 256) * 256 + n * kD * sizeof(float) + 256;
+}
+static size_t attn_workspace_bytes(const oscar_cache_geom* g, int splits) {
+  return kCounterBytes + workspace_bytes(g, splits);
 }
 
 void launch_lse_reduce(const float2* ws_ml, const float* ws_o, int hq, int batch, int splits,
@@ -1117,11 +1296,14 @@ void launch_lse_reduce(const float2* ws_ml, const float* ws_o, int hq, int batch
 }
 
 template <int GRP>
-void launch_attn(const AttnArgs& A, dim3 grid, hipStream_t st, bool mfma) {
-  if (mfma)
-    hipLaunchKernelGGL(attn_mfma_kernel<GRP>, grid, dim3(256), 0, st, A);
+void launch_mfma(const AttnArgs& A, int nwg, int nw, hipStream_t st) {
+  constexpr int P = OSCAR_ATTN_PUB;
+  if (nw == 12)
+    hipLaunchKernelGGL((attn_mfma_kernel<GRP, 12, P>), dim3(nwg), dim3(768), 0, st, A);
+  else if (nw == 6)
+    hipLaunchKernelGGL((attn_mfma_kernel<GRP, 6, P>), dim3(nwg), dim3(384), 0, st, A);
   else
-    hipLaunchKernelGGL(attn_valu_kernel<GRP>, grid, dim3(256), 0, st, A);
+    hipLaunchKernelGGL((attn_mfma_kernel<GRP, 4, P>), dim3(nwg), dim3(256), 0, st, A);
 }
 
 }  // namespace oscar
@@ -1134,9 +1316,9 @@ extern "C" oscar_status oscar_decode_workspace_bytes(const oscar_cache_geom* geo
   oscar_status st = check_geom(geom);
   if (st != OSCAR_OK) return st;
   if (!bytes || max_ctx < 0 || num_splits < 0 || num_splits > 1024) return OSCAR_EINVAL;
-  const int s = num_splits ? num_splits : auto_splits(geom, max_ctx);
+  const int s = attn_shape(geom, max_ctx, num_splits).splits;
   if (splits_out) *splits_out = s;
-  *bytes = workspace_bytes(geom, s);
+  *bytes = attn_workspace_bytes(geom, s);
   return OSCAR_OK;
 }
 
@@ -1153,8 +1335,10 @@ extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const os
   if (!aligned(workspace, 256) || !aligned(q, 4) || !aligned(out, 16)) return OSCAR_EINVAL;
   if (variant != OSCAR_ATTN_AUTO && variant != OSCAR_ATTN_VALU && variant != OSCAR_ATTN_MFMA)
     return OSCAR_EINVAL;
-  const int S = num_splits ? num_splits : auto_splits(geom, max_ctx);
-  if (ws_bytes < workspace_bytes(geom, S)) return OSCAR_EWORKSPACE;
+  if (static_cast<long long>(geom->batch) * geom->num_kv_heads > kMaxPairs) return OSCAR_EINVAL;
+  const AttnShape shape = attn_shape(geom, max_ctx, num_splits);
+  const int S = shape.splits;
+  if (ws_bytes < attn_workspace_bytes(geom, S)) return OSCAR_EWORKSPACE;
   st = check_device();
   if (st != OSCAR_OK) return st;
 
@@ -1176,21 +1360,41 @@ extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const os
   A.error_flag = cache->error_flag;
   A.splits = S;
   const size_t npart = static_cast<size_t>(geom->batch) * geom->num_q_heads * S;
-  A.ws_ml = static_cast<float2*>(workspace);
-  A.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                    ((npart * sizeof(float2) + 255) / 256) * 256);
-  const dim3 grid(S, geom->num_kv_heads, geom->batch);
+  char* part_base = static_cast<char*>(workspace) + kCounterBytes;
+  A.counters = static_cast<int32_t*>(workspace);
+  A.ws_ml = reinterpret_cast<float2*>(part_base);
+  A.ws_o = reinterpret_cast<float*>(part_base + ((npart * sizeof(float2) + 255) / 256) * 256);
+  A.out = out;
+  A.lse = lse;
   hipStream_t hs = as_stream(stream);
   const int grp = geom->num_q_heads / geom->num_kv_heads;
-  const bool mfma = variant != OSCAR_ATTN_VALU;
+  if (variant == OSCAR_ATTN_VALU) {
+    // the vector-ALU kernel writes partials; a second launch merges them
+    const dim3 grid(S, geom->num_kv_heads, geom->batch);
+    switch (grp) {
+      case 1: hipLaunchKernelGGL(attn_valu_kernel<1>, grid, dim3(256), 0, hs, A); break;
+      case 2: hipLaunchKernelGGL(attn_valu_kernel<2>, grid, dim3(256), 0, hs, A); break;
+      case 4: hipLaunchKernelGGL(attn_valu_kernel<4>, grid, dim3(256), 0, hs, A); break;
+      default: hipLaunchKernelGGL(attn_valu_kernel<8>, grid, dim3(256), 0, hs, A); break;
+    }
+    st = launch_status();
+    if (st != OSCAR_OK) return st;
+    launch_lse_reduce(A.ws_ml, A.ws_o, geom->num_q_heads, geom->batch, S, out, lse, hs);
+    return launch_status();
+  }
+  // the matrix-core kernel; with few (sequence, KV head) pairs it merges
+  // the splits itself (one launch), with many the separate merge launch
+  // spreads the merging over the chip
+  A.merge_in_kernel = shape.merge_in_kernel;
+  const int nwg = geom->batch * geom->num_kv_heads * S;
   switch (grp) {
-    case 1: launch_attn<1>(A, grid, hs, mfma); break;
-    case 2: launch_attn<2>(A, grid, hs, mfma); break;
-    case 4: launch_attn<4>(A, grid, hs, mfma); break;
-    default: launch_attn<8>(A, grid, hs, mfma); break;
+    case 1: launch_mfma<1>(A, nwg, shape.nw, hs); break;
+    case 2: launch_mfma<2>(A, nwg, shape.nw, hs); break;
+    case 4: launch_mfma<4>(A, nwg, shape.nw, hs); break;
+    default: launch_mfma<8>(A, nwg, shape.nw, hs); break;
   }
   st = launch_status();
-  if (st != OSCAR_OK) return st;
+  if (st != OSCAR_OK || A.merge_in_kernel || S == 1) return st;
   launch_lse_reduce(A.ws_ml, A.ws_o, geom->num_q_heads, geom->batch, S, out, lse, hs);
   return launch_status();
 }

@@ -332,9 +332,9 @@ __global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16
     rk[lane] = f32_to_f16(mul_rn(a, r));
     rk[lane + 64] = f32_to_f16(mul_rn(bb, r));
     uint16_t* rv = ca.res_v + bh * kD * kR + slot;
-    rv[static_cast<size_t>(lane) * kR] = f32_to_f16(in_to_f32(vin[0], is_bf16));
-    rv[static_cast<size_t>(lane + 64) * kR] = f32_to_f16(in_to_f32(vin[1], is_bf16));
-    if (lane == 0 && (ca.head_norm || h == 0)) ca.res_norm[res_norm_at(ca, b, h, slot)] = f32_to_f16(nrm);
+    rv[static_cast<size_t>(lane) * kR] = f32_to_f16_sat(in_to_f32(vin[0], is_bf16));
+    rv[static_cast<size_t>(lane + 64) * kR] = f32_to_f16_sat(in_to_f32(vin[1], is_bf16));
+    if (lane == 0 && (ca.head_norm || h == 0)) ca.res_norm[res_norm_at(ca, b, h, slot)] = f32_to_f16_sat(nrm);
   }
   if (tid == 0) {
     st[0] = n + 1;
@@ -473,9 +473,9 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
     const int t = t0 + tl;
     if (t < n_tokens) {
       if (ring)
-        ca.res_norm[res_norm_at(ca, seq, h, t % kR)] = f32_to_f16(nrm);
+        ca.res_norm[res_norm_at(ca, seq, h, t % kR)] = f32_to_f16_sat(nrm);
       else
-        ca.pool_norm[pool_norm_at(ca, p, h, tl)] = f32_to_f16(nrm);
+        ca.pool_norm[pool_norm_at(ca, p, h, tl)] = f32_to_f16_sat(nrm);
     }
   }
   __syncthreads();
@@ -502,7 +502,7 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
         uint16_t* rv = ca.res_v + bh * kD * kR + slot;
 #pragma unroll
         for (int j = 0; j < 32; ++j)
-          rv[static_cast<size_t>(32 * tq + j) * kR] = f32_to_f16(in_to_f32(vs[j], is_bf16));
+          rv[static_cast<size_t>(32 * tq + j) * kR] = f32_to_f16_sat(in_to_f32(vs[j], is_bf16));
       } else {
         dst = reinterpret_cast<uint4*>(khs + (t * hkv + h) * kD + 32 * tq);
       }
@@ -559,7 +559,7 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint16_t xh = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
-        x[8 * q + e] = f16_to_f32(f32_to_f16(in_to_f32(xh, is_bf16)));
+        x[8 * q + e] = f16_to_f32(f32_to_f16_sat(in_to_f32(xh, is_bf16)));
       }
     }
     const Range r = range32(x);

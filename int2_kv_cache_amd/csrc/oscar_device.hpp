@@ -41,6 +41,13 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 __device__ __forceinline__ uint16_t f32_to_f16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
+// fp32 -> fp16 bits of a stored value (a Value row entry, a token norm):
+// clamped to the finite fp16 range first, so nothing stored is infinite; the
+// max returns its other operand for a NaN, which is therefore stored as
+// -65504.  (The pages only say FP16; saturation is this code's reading.)
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
+  return f32_to_f16(fminf(fmaxf(f, -65504.0f), 65504.0f));
+}
 __device__ __forceinline__ float in_to_f32(uint16_t x, int is_bf16) {
   return is_bf16 ? bf16_to_f32(x) : f16_to_f32(x);
 }

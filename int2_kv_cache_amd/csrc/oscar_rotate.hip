@@ -111,9 +111,9 @@ __global__ __launch_bounds__(256) void rotate_scale_key_kernel(
     reinterpret_cast<uint4*>(khat + off)[q] = uint4{kw[4 * q], kw[4 * q + 1], kw[4 * q + 2], kw[4 * q + 3]};
   if (tq == 0) {
     if (head_scope)
-      norm[static_cast<size_t>(t) * n_heads + h] = f32_to_f16(nrm);
+      norm[static_cast<size_t>(t) * n_heads + h] = f32_to_f16_sat(nrm);
     else if (h == 0)
-      norm[t] = f32_to_f16(nrm);
+      norm[t] = f32_to_f16_sat(nrm);
   }
 }
 

@@ -12,6 +12,17 @@ from int2_kv_cache_amd import synth
 ATOL = 2e-3   # max-abs tolerance on attention outputs (fp32 accumulation)
 
 
+def fp32_score_tol(lse: float, v_range: float) -> float:
+    """Tolerance for inputs whose scores are large: ATOL plus what rounding
+    the scores to fp32 alone can do.  A score s (natural log units, about
+    |lse| for the tokens that carry weight) is held to a relative 2^-24, so
+    each weight can move by ~2^-24 |s| relative, and the output by that times
+    the range of the Values; 2^-20 leaves a factor 16 for the dot products'
+    own rounding.  For unit-scale inputs (|lse| ~ 20, range ~ 10) this adds
+    ~2e-4; for Values x1000 with scores ~ 1e3 it is ~10."""
+    return ATOL + 2.0 ** -20 * abs(lse) * v_range
+
+
 def dev_u16(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
 
@@ -34,6 +45,18 @@ def assert_same_bits(got: np.ndarray, want: np.ndarray, what: str = ""):
     raise AssertionError("%s: %d of %d differ; first at %s got %s want %s; max |diff| %d"
                          % (what, len(bad), got.size, bad[:4].tolist(), gi[:4].tolist(),
                             wi[:4].tolist(), int(np.abs(gi - wi).max())))
+
+
+def oracle_outputs(orc: "oracle.OracleCache", qr: np.ndarray, pairs):
+    """The oracle's (out, lse) for every (sequence, query head) in `pairs`,
+    spread over the host's threads (at most 16): the oracle's C code runs
+    outside the interpreter lock and is re-entrant."""
+    import concurrent.futures as cf
+    import os
+    pairs = list(pairs)
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+        res = list(ex.map(lambda bi: orc.decode_attn_one(qr, bi[0], bi[1]), pairs))
+    return dict(zip(pairs, res))
 
 
 def blocks_needed(ctx: int) -> int:
@@ -109,7 +132,7 @@ class Pair:
         mctx = max_ctx or (max(o for o in [self.orc.n(b) for b in range(cfg.batch)]) + 1)
         S, nbytes = ok.decode_workspace_bytes(self.geom, mctx, splits)
         if ws is None:
-            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
         assert ws.numel() >= nbytes
         out = torch.empty(cfg.batch, cfg.hq, 128, dtype=torch.float32, device="cuda")
         lse = torch.empty(cfg.batch, cfg.hq, dtype=torch.float32, device="cuda")

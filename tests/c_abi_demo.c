@@ -83,6 +83,9 @@ int main(int argc, char **argv)
     g.num_q_heads = hq;
     g.num_kv_heads = hkv;
     g.head_dim = OSCAR_HEAD_DIM;
+    g.block_tokens = OSCAR_BLOCK_TOKENS;
+    g.residual_tokens = OSCAR_RESIDUAL_TOKENS;
+    g.v_group = OSCAR_V_GROUP;
     g.norm_scope = OSCAR_NORM_TOKEN;
     g.max_blocks_per_seq = max_ctx / OSCAR_BLOCK_TOKENS + 1;
     g.num_physical_blocks = g.max_blocks_per_seq;

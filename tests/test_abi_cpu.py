@@ -39,7 +39,9 @@ def test_cache_layout_sizes():
 
 @pytest.mark.parametrize("bad", [
     dict(head_dim=64), dict(num_q_heads=6, num_kv_heads=4), dict(num_kv_heads=17, num_q_heads=34),
-    dict(batch=0), dict(num_q_heads=24, num_kv_heads=8), dict(max_blocks_per_seq=0)])
+    dict(batch=0), dict(num_q_heads=24, num_kv_heads=8), dict(max_blocks_per_seq=0),
+    dict(block_tokens=64), dict(block_tokens=0), dict(residual_tokens=256),
+    dict(residual_tokens=0), dict(v_group=128), dict(v_group=0), dict(flush_tokens=64)])
 def test_cache_layout_rejects(bad):
     args = dict(batch=1, num_q_heads=4, num_kv_heads=1, max_blocks_per_seq=4,
                 num_physical_blocks=4)

@@ -52,7 +52,7 @@ def _run(wl, ctxs, grp=None, splits=0, max_ctx=None, chunks=1, seed=0, heads=Non
     q = synth.to_bf16_bits(rng.standard_normal((B, hq, 128)))
     mc = max(ctxs) if max_ctx is None else max_ctx
     s, nbytes = ok.dense_workspace_bytes(geom, mc, splits)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.full((B, hq, 128), float("nan"), device="cuda")
     lse = torch.full((B, hq), float("nan"), device="cuda")
     ok.dense_decode_attn(cache, dev_u16(q), out, lse, ws, mc, splits)
@@ -119,7 +119,7 @@ def test_dense_flags():
     cache.error_flag.zero_()
     cache.ctx_lens.fill_(65)  # above the table's capacity: attends to nothing
     s, nbytes = ok.dense_workspace_bytes(geom, 64)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.full((1, 4, 128), float("nan"), device="cuda")
     ok.dense_decode_attn(cache, dev_u16(np.zeros((1, 4, 128), np.uint16)), out, None, ws, 64)
     torch.cuda.synchronize()

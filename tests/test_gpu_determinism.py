@@ -43,7 +43,7 @@ def _setup(batch=2, ctx=900, steps=40):
 
 def _decode(c, q, dt, geom, max_ctx):
     S, nbytes = ok.decode_workspace_bytes(geom, max_ctx)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty(geom.batch, geom.num_q_heads, 128, dtype=torch.float32, device="cuda")
     lse = torch.empty(geom.batch, geom.num_q_heads, dtype=torch.float32, device="cuda")
     ok.decode_attn(c, dev_u16(q), dt, out, lse, ws, max_ctx)
@@ -81,7 +81,7 @@ def test_bf16_baseline_is_deterministic():
     c.ctx_lens.fill_(2999)
     q = dev_u16(next(wl.steps(1))[2])
     S, nbytes = ok.dense_workspace_bytes(geom, 2999)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(2):
         out = torch.empty(1, wl.cfg.hq, 128, dtype=torch.float32, device="cuda")

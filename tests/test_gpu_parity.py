@@ -16,7 +16,7 @@ if gpu_available():
     import int2_kv_cache_amd as ok
     import oracle
     from int2_kv_cache_amd import synth
-    from _parity import ATOL, Pair, assert_same_bits, dev_u16, host_u16
+    from _parity import ATOL, Pair, assert_same_bits, dev_u16, fp32_score_tol, host_u16
 
 
 @pytest.mark.parametrize("dtype", [0, 1])
@@ -268,9 +268,14 @@ def test_attention_prerotated_query():
     assert np.abs(got - want).max() <= ATOL
 
 
+COUNTER_BYTES = 256 * 1024   # the workspace's arrival counters (zeroed once)
+
+
 def test_attention_workspace_reuse():
-    """One workspace serves calls with different split counts and kernels:
-    no call depends on what an earlier one left in it."""
+    """One workspace, its counter region zeroed once and its partials region
+    full of garbage, serves calls with different split counts and kernels:
+    no call depends on partials an earlier one left, and every call leaves
+    the counters zero for the next."""
     wl = synth.workload(3, batch=3, ctx=None)
     wl.ctx_lens = [3000, 700, 129]
     pr = Pair(wl)
@@ -282,9 +287,37 @@ def test_attention_workspace_reuse():
     want, _ = pr.orc.decode_attn(oracle.rotate_query(q, wl.cfg.dtype))
     _, nbytes = ok.decode_workspace_bytes(pr.geom, 3001, 64)
     ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device="cuda")
-    for S, var in [(64, 2), (5, 2), (1, 1), (0, 2), (64, 1), (3, 2)]:
+    ws[:COUNTER_BYTES] = 0
+    for S, var in [(64, 2), (5, 2), (1, 1), (0, 2), (64, 1), (3, 2), (1, 2), (2, 2)]:
         got, _ = pr.attend(q, variant=var, splits=S, max_ctx=3001, ws=ws)
         assert np.abs(got - want).max() <= ATOL, (S, var)
+        assert not ws[:COUNTER_BYTES].any().item(), (S, var)
+
+
+def test_attention_workspace_shared_by_geometries():
+    """A workspace zeroed once serves two different caches (batch 3 and
+    batch 1, other head counts) in alternation."""
+    wa = synth.workload(3, batch=3, ctx=None)
+    wa.ctx_lens = [2100, 900, 300]
+    wb = synth.workload(0, ctx=1500)
+    pa, pb = Pair(wa), Pair(wb)
+    for pr, wl in ((pa, wa), (pb, wb)):
+        for b in range(wl.cfg.batch):
+            k, v = wl.prefill(b)
+            pr.prefill(b, k, v)
+    qa = next(wa.steps(1))[2]
+    qb = next(wb.steps(1))[2]
+    want_a, _ = pa.orc.decode_attn(oracle.rotate_query(qa, wa.cfg.dtype))
+    want_b, _ = pb.orc.decode_attn(oracle.rotate_query(qb, wb.cfg.dtype))
+    na = ok.decode_workspace_bytes(pa.geom, 2200, 0)[1]
+    nb = ok.decode_workspace_bytes(pb.geom, 1600, 0)[1]
+    ws = torch.zeros(max(na, nb), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        got, _ = pa.attend(qa, max_ctx=2200, ws=ws)
+        assert np.abs(got - want_a).max() <= ATOL
+        got, _ = pb.attend(qb, max_ctx=1600, ws=ws)
+        assert np.abs(got - want_b).max() <= ATOL
+    assert not ws[:COUNTER_BYTES].any().item()
 
 
 def test_abi_rejects_bad_arguments():
@@ -405,3 +438,86 @@ def test_flush128_capacity_drops_whole_flush():
         pr.append(kn, vn)
     pr.compare_state()
     assert int(pr.gpu.error_flag.cpu()[0]) == ok.FLAG_CAPACITY
+
+
+def _scaled_bits(bits, dtype, factor):
+    return synth.cast_bits(synth.bits_to_f32(bits, dtype) * np.float32(factor), dtype)
+
+
+def _saturating_inputs(wl, huge_keys: bool, seed: int = 17):
+    """Prefill tokens and 12 decode steps whose bf16 Values include entries
+    beyond fp16's range (1e5, -2e5, +-3e38, +-inf) and NaN; with huge_keys,
+    some Keys scaled so that their token norm exceeds 65504."""
+    cfg = wl.cfg
+    k, v = wl.prefill(0, 290)
+    rng = np.random.default_rng(seed)
+    odd = np.float32([1e5, -2e5, 7e4, 3e38, -3e38, np.inf, -np.inf, np.nan])
+    vf = synth.bits_to_f32(v, cfg.dtype).copy()
+    idx = rng.integers(0, vf.size, size=600)
+    vf.ravel()[idx] = odd[rng.integers(0, odd.size, size=idx.size)]
+    kf = synth.bits_to_f32(k, cfg.dtype).copy()
+    if huge_keys:
+        kf[[3, 100, 250, 280]] *= 5000.0
+    steps = []
+    for s_, (kn, vn, q) in enumerate(wl.steps(12)):
+        if huge_keys and s_ % 5 == 0:
+            kn = _scaled_bits(kn, cfg.dtype, 5000.0)
+        vnf = synth.bits_to_f32(vn, cfg.dtype).copy()
+        vnf.ravel()[rng.integers(0, vnf.size, size=40)] = odd[rng.integers(0, odd.size, size=40)]
+        steps.append((kn, synth.to_bf16_bits(vnf), q))
+    return synth.to_bf16_bits(kf), synth.to_bf16_bits(vf), steps
+
+
+def test_values_and_norms_beyond_fp16_range_saturate():
+    """bf16 Values beyond fp16's range and NaN, and Keys whose token norm
+    exceeds 65504, through prefill and appends (with a flush): the cache is
+    bit-exact with the oracle's saturating reading and attention stays
+    finite.  (The scores of tokens with norm 65504 reach ~6e3 and their dot
+    products cancel heavily; no fp32 attention matches an fp64 one to 2e-3
+    on them, so their outputs are checked for finiteness only.)"""
+    wl = synth.workload(2, ctx=330)
+    pr = Pair(wl)
+    k, v, steps = _saturating_inputs(wl, huge_keys=True)
+    pr.prefill(0, k, v)
+    for kn, vn, q in steps:
+        pr.append(kn, vn)
+    pr.compare_state()
+    got, glse = pr.attend(q)
+    assert np.isfinite(got).all() and np.isfinite(glse).all()
+
+
+def test_saturated_values_attention():
+    """Saturated Values (entries +-65504) with ordinary Keys: bit-exact cache,
+    and every head within 2e-3 plus what fp32 rounding of Values this large
+    allows (fp32_score_tol)."""
+    wl = synth.workload(2, ctx=330)
+    cfg = wl.cfg
+    pr = Pair(wl)
+    k, v, steps = _saturating_inputs(wl, huge_keys=False, seed=23)
+    pr.prefill(0, k, v)
+    for kn, vn, q in steps:
+        pr.append(kn, vn)
+    pr.compare_state()
+    got, _ = pr.attend(q)
+    want, wlse = pr.orc.decode_attn(oracle.rotate_query(q, cfg.dtype))
+    for i in range(cfg.hq):
+        tol = fp32_score_tol(float(wlse[0, i]), 2 * 65504.0)
+        assert float(np.abs(got[0, i] - want[0, i]).max()) <= tol, i
+
+
+def test_zero_key_tokens_through_prefill_and_append():
+    """Zero Keys (norm 0: k_hat = 0, norm = 0) in a quantized block, in the
+    window and as an appended token: bit-exact cache, every head within 2e-3."""
+    wl = synth.workload(2, ctx=320)
+    pr = Pair(wl)
+    k, v = wl.prefill(0, 290)
+    k = k.copy()
+    k[[0, 5, 31, 200, 280]] = 0
+    pr.prefill(0, k, v)
+    for s, (kn, vn, q) in enumerate(wl.steps(6)):
+        pr.append(np.zeros_like(kn) if s in (1, 4) else kn, vn)
+    pr.compare_state()
+    got, glse = pr.attend(q)
+    want, wlse = pr.orc.decode_attn(oracle.rotate_query(q, wl.cfg.dtype))
+    assert float(np.abs(got - want).max()) <= ATOL
+    assert np.allclose(glse, wlse, rtol=1e-4, atol=1e-4)

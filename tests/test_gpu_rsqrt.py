@@ -88,7 +88,7 @@ def test_hw_rsq_cache_stagewise_and_attention(n_prefill, n_append):
     if q is None:
         q = next(wl.steps(1))[2]
     S, nbytes = ok.decode_workspace_bytes(hw_geom, n + 1)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     out = torch.empty(1, wl.cfg.hq, 128, dtype=torch.float32, device="cuda")
     ok.decode_attn(gpu, dev_u16(q), dt, out, None, ws, n + 1)
     torch.cuda.synchronize()
