@@ -90,6 +90,8 @@ typedef enum {
 #define OSCAR_FLAG_NONEMPTY 2u  /* prefill into a sequence with n != 0 */
 #define OSCAR_FLAG_BADSTATE 4u  /* a block id outside the pool, or an inconsistent
                                    {n, Q}: the affected work is skipped */
+#define OSCAR_FLAG_POSITION 8u  /* a token position at or beyond rope_max_pos:
+                                   the append is dropped */
 
 /* Cache geometry (host struct).  The method's fixed sizes are fields too,
  * so that a caller states them and a mismatch is an error rather than a
@@ -113,6 +115,11 @@ typedef struct {
                                     whole window as four blocks */
     int32_t key_scale;           /* oscar_key_scale used by append and prefill:
                                     0 = IEEE (default), 1 = hardware rsqrt */
+    int32_t rope_max_pos;        /* 0: queries and Keys arrive already rotated
+                                    by position (RoPE applied by the caller);
+                                    > 0: the library applies RoPE itself, from
+                                    the table cache->rope of this many
+                                    positions (see oscar_cache) */
 } oscar_cache_geom;
 
 /* Cache buffers (device pointers, caller-owned).  Layout, per the record
@@ -136,6 +143,20 @@ typedef struct {
  *   block_table [B][max_blocks_per_seq] int32 physical block ids (caller fills)
  *   seq_state   [B][2] int32 = {n tokens, Q quantized tokens}; zero = empty
  *   error_flag  [1] int32 sticky bits (OSCAR_FLAG_*); caller zeroes it
+ *   append_sync [B] int32, library-private (oscar_append_kv's per-sequence
+ *               arrival counters); caller zeroes it once, every call leaves
+ *               it zero
+ *   rope        NULL when geom->rope_max_pos == 0; else read-only
+ *               [rope_max_pos][64][2] fp32 (cos, sin): the rotary position
+ *               embedding of the model.  The popular-science article (五)
+ *               names RoPE as the reason the Key and query rotation must run
+ *               online: the library applies it right before the FHT, channel
+ *               pairs (i, i + 64) of token position p rotated by the angle of
+ *               row p, column i:  x_i <- x_i c - x_{i+64} s,
+ *               x_{i+64} <- x_{i+64} c + x_i s  (fp32 products, then one add).
+ *               Keys take the position of the token in its sequence (0 for
+ *               the first), the query of a decode step the position of the
+ *               step's own token (n - 1 after its append).
  * Token t of a sequence lives in block t/32 (t < Q) or ring slot t % 128
  * (Q <= t < n).  All buffers zero-initialised by the caller before first use. */
 typedef struct {
@@ -147,11 +168,14 @@ typedef struct {
     int32_t *block_table;
     int32_t *seq_state;
     int32_t *error_flag;
+    int32_t *append_sync;
+    const float *rope;
 } oscar_cache;
 
 /* Byte sizes of each cache buffer for a geometry. */
 typedef struct {
-    size_t pool, pool_norm, res_k, res_v, res_norm, block_table, seq_state, error_flag;
+    size_t pool, pool_norm, res_k, res_v, res_norm, block_table, seq_state, error_flag,
+        append_sync;
 } oscar_cache_sizes;
 
 /* Host-only infrastructure (no defining passage: the pages fix no memory
@@ -178,6 +202,7 @@ OSCAR_API oscar_status oscar_cache_layout(const oscar_cache_geom *geom, oscar_ca
  *             KEY_HW_RSQ: KEY with 1/sqrt(ss) from the hardware instruction
  *                    (OSCAR_SCALE_HW_RSQ).
  *   n_heads   >= 1 (QUERY), 1..16 (KEY: the norm spans all heads of a token).
+ * No RoPE here: stateless inputs are taken as already rotated by position.
  * Errors: EINVAL (null, n_tokens < 0, n_heads out of range, bad dtype; for
  * KEY, x or khat_out not 16-byte aligned). */
 OSCAR_API oscar_status oscar_rotate_scale(const void *x, oscar_dtype dtype, int32_t n_tokens,
@@ -216,6 +241,9 @@ OSCAR_API oscar_status oscar_quant_pack(const void *khat16, const void *knorm16,
  *                    drop the append if (Q+F)/32 > max_blocks_per_seq); Q += F;
  *   rotate+scale k_new[b], store k_hat, norm and fp16(v_new[b]) in slot
  *   n % 128; n += 1.
+ * One workgroup per (sequence, KV head) does that head's share (its part of
+ * the flush, its row of the window); the last of a sequence's workgroups to
+ * finish writes {n, Q}, counted in append_sync[b].
  * Stored fp16 values saturate: a Value entry or a norm beyond +-65504
  * (+-inf included) is stored as +-65504, a NaN Value as -65504; |k_hat| <= 1.
  *   k_new, v_new  device, [B][Hkv][128] fp16 or bf16; Keys must be finite
@@ -333,6 +361,25 @@ OSCAR_API oscar_status oscar_dense_decode_attn(const oscar_cache_geom *geom, con
 
 /* Infrastructure (no defining passage): a static, never-freed string naming
  * a status code ("unknown status" for any other value).  Host-only. */
+/* Offline absorption of the Value rotation into the projection weights
+ * (reading notes §II Step One, query-side symmetric processing; summary
+ * "OScaR：…", 方法步骤详情 (3)).  Keeping V' = H V per KV head in the cache
+ * takes W_v' = H W_v, and the attention output, which is then H o per query
+ * head, is turned back by W_o' = W_o H; after this one-time transform the
+ * Value rotation costs nothing at decode time.  H is the 128-point Sylvester
+ * Hadamard matrix times 1/sqrt(128) (symmetric, its own inverse), applied as
+ * the plain fp32 butterfly, strides 1..64, then x fp32(1/sqrt(128)).
+ *   w, out   device, row-major fp32 [rows][cols]; out may equal w (in place).
+ *   axis 0   every column of every 128-row block is replaced by H times it:
+ *            W_v' for W_v stored [Hkv*128][d_model] (nn.Linear layout).
+ *   axis 1   every 128-column block of every row is replaced by it times H:
+ *            W_o' for W_o stored [d_model][Hq*128]; also a Value bias b_v
+ *            taken as [1][Hkv*128] (H b = b H).
+ * Errors: EINVAL (null, negative sizes, axis not 0 or 1, rows (axis 0) or
+ * cols (axis 1) not a multiple of 128, a grid beyond 2^31 - 1 blocks). */
+OSCAR_API oscar_status oscar_absorb_value_rotation(const float *w, float *out, int64_t rows,
+                                                   int64_t cols, int32_t axis, void *stream);
+
 OSCAR_API const char *oscar_status_str(oscar_status s);
 
 #ifdef __cplusplus

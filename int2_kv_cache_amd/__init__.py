@@ -23,13 +23,13 @@ NORM_TOKEN, NORM_HEAD = 0, 1
 ROT_QUERY, ROT_KEY, ROT_KEY_HW_RSQ = 0, 1, 2
 SCALE_IEEE, SCALE_HW_RSQ = 0, 1
 ATTN_AUTO, ATTN_VALU, ATTN_MFMA = 0, 1, 2
-FLAG_CAPACITY, FLAG_NONEMPTY, FLAG_BADSTATE = 1, 2, 4
+FLAG_CAPACITY, FLAG_NONEMPTY, FLAG_BADSTATE, FLAG_POSITION = 1, 2, 4, 8
 HEAD_DIM, BLOCK_TOKENS, RESIDUAL_TOKENS, V_GROUP, RECORD_BYTES = 128, 32, 128, 32, 3072
 
 API = ("oscar_cache_layout", "oscar_rotate_scale", "oscar_quant_pack", "oscar_append_kv",
        "oscar_prefill_quantize", "oscar_decode_workspace_bytes", "oscar_decode_attn",
        "oscar_dense_write_kv", "oscar_dense_workspace_bytes", "oscar_dense_decode_attn",
-       "oscar_status_str")
+       "oscar_absorb_value_rotation", "oscar_status_str")
 
 
 class OscarError(RuntimeError):
@@ -45,20 +45,21 @@ class Geom(ctypes.Structure):
                 ("v_group", ctypes.c_int32),
                 ("norm_scope", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_physical_blocks", ctypes.c_int32), ("flush_tokens", ctypes.c_int32),
-                ("key_scale", ctypes.c_int32)]
+                ("key_scale", ctypes.c_int32), ("rope_max_pos", ctypes.c_int32)]
 
 
 class CacheBufs(ctypes.Structure):
     _fields_ = [("pool", ctypes.c_void_p), ("pool_norm", ctypes.c_void_p),
                 ("res_k", ctypes.c_void_p), ("res_v", ctypes.c_void_p),
                 ("res_norm", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
-                ("seq_state", ctypes.c_void_p), ("error_flag", ctypes.c_void_p)]
+                ("seq_state", ctypes.c_void_p), ("error_flag", ctypes.c_void_p),
+                ("append_sync", ctypes.c_void_p), ("rope", ctypes.c_void_p)]
 
 
 class CacheSizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("pool", "pool_norm", "res_k", "res_v", "res_norm", "block_table",
-                 "seq_state", "error_flag")]
+                 "seq_state", "error_flag", "append_sync")]
 
 
 _lib = None
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
                                                   P(ctypes.c_size_t)]
         L.oscar_dense_decode_attn.argtypes = [P(Geom), vp, vp, vp, vp, vp, vp, vp, vp,
                                               ctypes.c_size_t, i32, i32, vp, vp]
+        L.oscar_absorb_value_rotation.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, i32,
+                                                  vp]
         for name in API:
             getattr(L, name).restype = ctypes.c_int
         L.oscar_status_str.restype = ctypes.c_char_p
@@ -121,10 +124,10 @@ def _stream(stream=None):
 def make_geom(batch, num_q_heads, num_kv_heads, max_blocks_per_seq, num_physical_blocks,
               norm_scope=NORM_TOKEN, head_dim=HEAD_DIM, flush_tokens=32,
               key_scale=SCALE_IEEE, block_tokens=BLOCK_TOKENS,
-              residual_tokens=RESIDUAL_TOKENS, v_group=V_GROUP) -> Geom:
+              residual_tokens=RESIDUAL_TOKENS, v_group=V_GROUP, rope_max_pos=0) -> Geom:
     return Geom(batch, num_q_heads, num_kv_heads, head_dim, block_tokens, residual_tokens,
                 v_group, norm_scope, max_blocks_per_seq, num_physical_blocks, flush_tokens,
-                key_scale)
+                key_scale, rope_max_pos)
 
 
 def cache_layout(geom: Geom) -> CacheSizes:
@@ -137,7 +140,9 @@ class DeviceCache:
     """Cache buffers as torch tensors on the current device, sized by
     oscar_cache_layout and zero-initialised (torch is the allocator)."""
 
-    def __init__(self, geom: Geom, block_table=None, device="cuda"):
+    def __init__(self, geom: Geom, block_table=None, device="cuda", rope_table=None):
+        """rope_table: [geom.rope_max_pos][64][2] fp32 (cos, sin), required
+        when geom.rope_max_pos > 0."""
         import torch
         self.geom = geom
         sz = cache_layout(geom)
@@ -160,9 +165,15 @@ class DeviceCache:
         self.block_table = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
         self.seq_state = torch.zeros(B, 2, dtype=torch.int32, device=device)
         self.error_flag = torch.zeros(1, dtype=torch.int32, device=device)
+        self.append_sync = torch.zeros(B, dtype=torch.int32, device=device)
+        self.rope = None
+        if rope_table is not None:
+            self.rope = torch.as_tensor(rope_table, dtype=torch.float32).to(device).contiguous()
+            assert tuple(self.rope.shape) == (geom.rope_max_pos, 64, 2)
         self.bufs = CacheBufs(*(t.data_ptr() for t in (
             self.pool, self.pool_norm, self.res_k, self.res_v, self.res_norm,
-            self.block_table, self.seq_state, self.error_flag)))
+            self.block_table, self.seq_state, self.error_flag, self.append_sync)),
+            self.rope.data_ptr() if self.rope is not None else None)
 
 
 def rotate_scale(x, dtype: int, mode: int, norm_scope: int = NORM_TOKEN, q_out=None,
@@ -172,6 +183,20 @@ def rotate_scale(x, dtype: int, mode: int, norm_scope: int = NORM_TOKEN, q_out=N
     _check("oscar_rotate_scale", lib().oscar_rotate_scale(
         _ptr(x), dtype, n_tokens, n_heads, mode, norm_scope, _ptr(q_out), _ptr(khat_out),
         _ptr(norm_out), _stream(stream)))
+
+
+def absorb_value_rotation(w, axis: int, out=None, stream=None):
+    """w: 2-D contiguous fp32 device tensor.  axis 0: H times every 128-row
+    block (W_v' = H W_v); axis 1: every 128-column block times H
+    (W_o' = W_o H).  Returns `out` (a new tensor unless given; may be w)."""
+    assert w.dtype.is_floating_point and w.element_size() == 4 and w.dim() == 2
+    assert w.is_contiguous()
+    if out is None:
+        import torch
+        out = torch.empty_like(w)
+    _check("oscar_absorb_value_rotation", lib().oscar_absorb_value_rotation(
+        _ptr(w), _ptr(out), w.shape[0], w.shape[1], axis, _stream(stream)))
+    return out
 
 
 def quant_pack(khat16, knorm16, v16, rec_out, norm_out, norm_scope=NORM_TOKEN, stream=None):

@@ -37,6 +37,7 @@ oscar_status check_geom(const oscar_cache_geom* g) {
   if (g->norm_scope != OSCAR_NORM_TOKEN && g->norm_scope != OSCAR_NORM_HEAD) return OSCAR_EINVAL;
   if (g->flush_tokens != 0 && g->flush_tokens != 32 && g->flush_tokens != 128) return OSCAR_EINVAL;
   if (g->key_scale != OSCAR_SCALE_IEEE && g->key_scale != OSCAR_SCALE_HW_RSQ) return OSCAR_EINVAL;
+  if (g->rope_max_pos < 0) return OSCAR_EINVAL;
   return OSCAR_OK;
 }
 
@@ -44,12 +45,13 @@ oscar_status check_cache(const oscar_cache_geom* g, const oscar_cache* c) {
   oscar_status st = check_geom(g);
   if (st != OSCAR_OK) return st;
   if (!c || !c->pool || !c->pool_norm || !c->res_k || !c->res_v || !c->res_norm ||
-      !c->block_table || !c->seq_state || !c->error_flag)
+      !c->block_table || !c->seq_state || !c->error_flag || !c->append_sync)
     return OSCAR_EINVAL;
   if (!aligned(c->pool, 256) || !aligned(c->pool_norm, 16) || !aligned(c->res_k, 16) ||
       !aligned(c->res_v, 16) || !aligned(c->res_norm, 16) || !aligned(c->block_table, 4) ||
-      !aligned(c->seq_state, 8) || !aligned(c->error_flag, 4))
+      !aligned(c->seq_state, 8) || !aligned(c->error_flag, 4) || !aligned(c->append_sync, 4))
     return OSCAR_EINVAL;
+  if (g->rope_max_pos > 0 && (!c->rope || !aligned(c->rope, 8))) return OSCAR_EINVAL;
   return OSCAR_OK;
 }
 
@@ -71,6 +73,7 @@ extern "C" oscar_status oscar_cache_layout(const oscar_cache_geom* g, oscar_cach
   out->block_table = B * static_cast<size_t>(g->max_blocks_per_seq) * sizeof(int32_t);
   out->seq_state = B * 2 * sizeof(int32_t);
   out->error_flag = sizeof(int32_t);
+  out->append_sync = B * sizeof(int32_t);
   return OSCAR_OK;
 }
 

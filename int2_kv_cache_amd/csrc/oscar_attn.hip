@@ -43,7 +43,23 @@ struct AttnArgs {
   float* out;     // [B][Hq][128]
   float* lse;     // [B][Hq] or null
   int merge_in_kernel;  // 0: partials only, a separate launch merges them
+  // null, or [rope_max_pos][64] (cos, sin): a raw (fp16 / bf16) query is
+  // rotated by position n - 1, the step's own token, before its FHT
+  const float* rope;
+  int rope_max_pos;
 };
+
+// The (cos, sin) of the decode query's position n - 1 for lane L (channel
+// pair L, L + 64), or (1, 0) when no RoPE applies; a position past the
+// table flags the call and leaves the query unrotated.
+__device__ __forceinline__ float2 query_rope(const AttnArgs& A, int n, int L) {
+  if (!A.rope || A.q_mode == 2 || n < 1) return make_float2(1.0f, 0.0f);
+  if (n - 1 >= A.rope_max_pos) {
+    if (L == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_POSITION));
+    return make_float2(1.0f, 0.0f);
+  }
+  return reinterpret_cast<const float2*>(A.rope)[static_cast<size_t>(n - 1) * 64 + L];
+}
 
 // The 32 token norms of block p for KV head h, and window slot 0 of (b, h).
 __device__ __forceinline__ const uint16_t* block_norms(const AttnArgs& A, int p, int h) {
@@ -53,10 +69,12 @@ __device__ __forceinline__ const uint16_t* window_norms(const AttnArgs& A, int b
   return A.res_norm + (A.head_norm ? (static_cast<size_t>(b) * A.hkv + h) * kR : static_cast<size_t>(b) * kR);
 }
 
-// Rotated query heads of KV head h into qs[GRP][128] (fp32).
+// Rotated query heads of KV head h into qs[GRP][128] (fp32): RoPE at the
+// position of the step's own token (n - 1) if enabled, then the FHT.
 template <int GRP>
-__device__ __forceinline__ void load_rotated_q(const AttnArgs& A, int b, int h, float* qs) {
+__device__ __forceinline__ void load_rotated_q(const AttnArgs& A, int b, int h, int n, float* qs) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const float2 cs = query_rope(A, n, lane);
   for (int i = wave; i < GRP; i += nw) {
     const size_t base = (static_cast<size_t>(b) * A.hq + h * GRP + i) * kD;
     float a, bb;
@@ -67,6 +85,7 @@ __device__ __forceinline__ void load_rotated_q(const AttnArgs& A, int b, int h, 
       const uint16_t* q16 = static_cast<const uint16_t*>(A.q);
       a = in_to_f32(q16[base + lane], A.q_mode);
       bb = in_to_f32(q16[base + lane + 64], A.q_mode);
+      rope_pair(a, bb, cs.x, cs.y);
       fht128_wave(a, bb);
     }
     qs[i * kD + lane] = a;
@@ -98,7 +117,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs A) {
   const int u0 = static_cast<int>((static_cast<long long>(s) * U) / A.splits);
   const int u1 = static_cast<int>((static_cast<long long>(s + 1) * U) / A.splits);
 
-  load_rotated_q<GRP>(A, b, h, qs);
+  load_rotated_q<GRP>(A, b, h, n, qs);
   if (tid < GRP) {
     mrun[tid] = -INFINITY;
     lrun[tid] = 0.0f;
@@ -696,11 +715,15 @@ void attn_mfma_kernel(AttnArgs A) {
   if (cnt > 0) dma_block(0, st0);
   if (cnt > 1) dma_block(1, st1);
 
+  const float2 qcs = query_rope(A, n, L);
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
     const int i = wave + NW * j;
     if (i < GRP) {
-      if (A.q_mode != 2) fht128_wave(qx[j], qy[j]);
+      if (A.q_mode != 2) {
+        rope_pair(qx[j], qy[j], qcs.x, qcs.y);
+        fht128_wave(qx[j], qy[j]);
+      }
       // q' carries the score scale 1/sqrt(128) * log2(e): every score
       // comes out in the log2 domain of the softmax
       qs[i * kD + L] = qx[j] * kScale;
@@ -1366,6 +1389,8 @@ extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const os
   A.ws_o = reinterpret_cast<float*>(part_base + ((npart * sizeof(float2) + 255) / 256) * 256);
   A.out = out;
   A.lse = lse;
+  A.rope = geom->rope_max_pos > 0 ? cache->rope : nullptr;
+  A.rope_max_pos = geom->rope_max_pos;
   hipStream_t hs = as_stream(stream);
   const int grp = geom->num_q_heads / geom->num_kv_heads;
   if (variant == OSCAR_ATTN_VALU) {

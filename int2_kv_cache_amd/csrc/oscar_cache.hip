@@ -188,12 +188,15 @@ struct CacheArgs {
   const int32_t* block_table;
   int32_t* seq_state;
   int32_t* error_flag;
+  int32_t* append_sync;  // [B] arrival counters of the append's workgroups
   int hkv;
   int max_blocks;
   int nphys;
   int head_norm;    // 1: a norm per (token, KV head) ([P][Hkv][32], [B][Hkv][128])
   int flush_blocks;  // blocks quantized when the window is full: 1 or 4
   int hw_rsq;        // 1: scaling factor from the hardware rsqrt
+  const float* rope;  // null, or [rope_max_pos][64] (cos, sin) of each position
+  int rope_max_pos;
 };
 // Token norm slots: TOKEN scope [P][32] and [B][128]; HEAD scope [P][Hkv][32]
 // and [B][Hkv][128].
@@ -210,135 +213,162 @@ __device__ __forceinline__ bool state_ok(int n, int Q, int max_blocks) {
   return Q >= 0 && (Q & 31) == 0 && n >= Q && n - Q <= kR && Q / kG <= max_blocks;
 }
 
-// grid B, 1024 threads (wave h < Hkv rotates head h; all of them share a flush).
-__global__ __launch_bounds__(1024) void append_kernel(CacheArgs ca, const uint16_t* __restrict__ k_new,
-                                                      const uint16_t* __restrict__ v_new,
-                                                      int is_bf16) {
-  // block flush: the Key and Value code images (Hkv <= 16)
-  __shared__ __attribute__((aligned(16))) uint32_t fl_img_k[16 * 2 * kD];
-  __shared__ __attribute__((aligned(16))) uint32_t fl_img_v[16 * 4 * kVImgRow];
+// grid B * Hkv: workgroup b * Hkv + h appends head h of sequence b's new
+// token (and, when the window is full, quantizes head h's share of the
+// flushed block); 512 threads, so that each of up to 8 heads of the new
+// token rotates in a wave of its own (two per wave for 9..16 heads).  Every workgroup of a sequence reads {n, Q}
+// first; the last of them to finish (counted in append_sync[b]) writes the
+// new state and resets the counter, so no workgroup can see a half-updated
+// state.  In TOKEN scope every workgroup rotates all heads of the new token
+// (2 KB) so that it has the norm over all heads without talking to the
+// others; the same tree order as a single workgroup gives the same bits.
+__global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_t* __restrict__ k_new,
+                                                     const uint16_t* __restrict__ v_new,
+                                                     int is_bf16) {
+  __shared__ __attribute__((aligned(16))) uint32_t img_k[2 * kD];
+  __shared__ __attribute__((aligned(16))) uint32_t img_v[4 * kVImgRow];
+  // a flushed block of head h: its 32 Key rows [slot][channel] and its Value
+  // columns [channel][slot], copied from the window with one 16-byte load per
+  // thread each
+  __shared__ __attribute__((aligned(16))) uint16_t fk[32 * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t fv[kD * 32];
   __shared__ float part[16];
-  const int b = blockIdx.x, tid = threadIdx.x;
   const int hkv = ca.hkv;
+  const int b = blockIdx.x / hkv, h = blockIdx.x - b * hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // the new token's inputs do not depend on the state: load them first
-  const int h = tid >> 6, lane = tid & 63;
-  uint16_t kin[2] = {0, 0}, vin[2] = {0, 0};
-  if (h < hkv) {
-    const size_t base = (static_cast<size_t>(b) * hkv + h) * kD;
-    kin[0] = k_new[base + lane];
-    kin[1] = k_new[base + lane + 64];
-    vin[0] = v_new[base + lane];
-    vin[1] = v_new[base + lane + 64];
+  // (wave w holds heads w and w + 8)
+  uint16_t kin[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int hh = wave + 8 * j;
+    kin[j][0] = kin[j][1] = 0;
+    if (hh < hkv) {
+      const size_t base = (static_cast<size_t>(b) * hkv + hh) * kD;
+      kin[j][0] = k_new[base + lane];
+      kin[j][1] = k_new[base + lane + 64];
+    }
   }
+  uint16_t vin = 0;
+  if (tid < kD) vin = v_new[(static_cast<size_t>(b) * hkv + h) * kD + tid];
   int32_t* st = ca.seq_state + 2 * b;
   const int n = st[0];
   int Q = st[1];
   if (!state_ok(n, Q, ca.max_blocks)) {
-    if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
+    if (tid == 0 && h == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
     return;
   }
-
+  if (ca.rope && n >= ca.rope_max_pos) {  // no (cos, sin) for position n
+    if (tid == 0 && h == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_POSITION));
+    return;
+  }
+  const size_t bh = static_cast<size_t>(b) * hkv + h;
   if (n - Q == kR) {
-    // The window is full: its oldest 32 (one block) or 128 (four blocks)
-    // tokens become blocks Q/32 ..; every block id is checked first, so a
-    // flush happens whole or not at all.
     const int nfb = ca.flush_blocks, j0 = Q / kG;
     if (j0 + nfb > ca.max_blocks) {
-      if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_CAPACITY));
+      if (tid == 0 && h == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_CAPACITY));
       return;
     }
     for (int i = 0; i < nfb; ++i) {
       const int pi = ca.block_table[static_cast<size_t>(b) * ca.max_blocks + j0 + i];
       if (pi < 0 || pi >= ca.nphys) {
-        if (tid == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
+        if (tid == 0 && h == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
         return;
       }
     }
     for (int fi = 0; fi < nfb; ++fi) {
       const int p = ca.block_table[static_cast<size_t>(b) * ca.max_blocks + j0 + fi];
       const int s0 = (Q + kG * fi) % kR;
-      for (int i = tid; i < (ca.head_norm ? hkv : 1) * 32; i += blockDim.x)
-        ca.pool_norm[pool_norm_at(ca, p, i >> 5, i & 31)] = ca.res_norm[res_norm_at(ca, b, i >> 5, s0 + (i & 31))];
-      const size_t bh0 = static_cast<size_t>(b) * hkv;
-      auto rec_of = [&](int hh) { return ca.pool + (static_cast<size_t>(p) * hkv + hh) * kRec; };
-      // ranges and codes, as in the bulk prefill: Key (head, channel) over
-      // the block's 32 window tokens, Value (token, head, group) over 32
-      // channels; the codes go to the LDS images
-      const int nku = hkv * kD, nvu = 32 * hkv * 4;
-      for (int u = tid; u < nku + nvu; u += blockDim.x) {
-        float x[32];
-        uint32_t cw[2];
-        if (u < nku) {
-          const int hh = u >> 7, c = u & 127;
-          const uint16_t* rk = ca.res_k + ((bh0 + hh) * kR + s0) * kD + c;
+      if (tid < 32 && (ca.head_norm || h == 0))
+        ca.pool_norm[pool_norm_at(ca, p, h, tid)] = ca.res_norm[res_norm_at(ca, b, h, s0 + tid)];
+      uint8_t* rec = ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec;
+      // Key rows of slots s0 .. s0 + 31 (contiguous), Value slots s0 .. s0 + 31
+      // of each channel (64 contiguous bytes per channel)
+      reinterpret_cast<uint4*>(fk)[tid] =
+          reinterpret_cast<const uint4*>(ca.res_k + (bh * kR + s0) * kD)[tid];
+      reinterpret_cast<uint4*>(fv)[tid] = reinterpret_cast<const uint4*>(
+          ca.res_v + (bh * kD + (tid >> 2)) * kR + s0)[tid & 3];
+      __syncthreads();
+      float x[32];
+      uint32_t cw[2];
+      if (tid < kD) {
+        // Key channel tid over the block's 32 window tokens
 #pragma unroll
-          for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(rk[t * kD]);
-          const Range r = range32(x);
-          uint8_t* rec = rec_of(hh);
-          reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(r.delta);
-          reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = static_cast<uint16_t>(r.zm);
-          codes32(x, r, cw);
-          fl_img_k[(2 * hh) * kD + c] = cw[0];
-          fl_img_k[(2 * hh + 1) * kD + c] = cw[1];
-        } else {
-          // slot fastest across lanes: the window's Values are channel-major
-          const int w = u - nku, t = w & 31, hh = (w >> 5) / 4, g = (w >> 5) & 3;
-          const uint16_t* rv = ca.res_v + ((bh0 + hh) * kD + 32 * g) * kR + s0 + t;
+        for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(fk[t * kD + tid]);
+        const Range r = range32(x);
+        reinterpret_cast<uint16_t*>(rec + kRecKDelta)[tid] = f32_to_f16(r.delta);
+        reinterpret_cast<uint16_t*>(rec + kRecKZero)[tid] = static_cast<uint16_t>(r.zm);
+        codes32(x, r, cw);
+        img_k[tid] = cw[0];
+        img_k[kD + tid] = cw[1];
+      } else if (tid < 2 * kD) {
+        // Value (token t, group g) over 32 channels; slot fastest across lanes
+        const int u = tid - kD, t = u & 31, g = u >> 5;
 #pragma unroll
-          for (int i = 0; i < 32; ++i) x[i] = f16_to_f32(rv[static_cast<size_t>(i) * kR]);
-          const Range r = range32(x);
-          reinterpret_cast<uint32_t*>(rec_of(hh) + kRecVParam)[32 * g + t] =
-              static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
-          codes32(x, r, cw);
-          *reinterpret_cast<uint2*>(fl_img_v + (hh * 4 + g) * kVImgRow + 2 * t) = uint2{cw[0], cw[1]};
-        }
+        for (int i = 0; i < 32; ++i) x[i] = f16_to_f32(fv[(32 * g + i) * 32 + t]);
+        const Range r = range32(x);
+        reinterpret_cast<uint32_t*>(rec + kRecVParam)[32 * g + t] =
+            static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
+        codes32(x, r, cw);
+        *reinterpret_cast<uint2*>(img_v + g * kVImgRow + 2 * t) = uint2{cw[0], cw[1]};
       }
       __syncthreads();
-      // the record's code words from the images
-      const int nkw = hkv * 32 * 8;
-      for (int u = tid; u < 2 * nkw; u += blockDim.x) {
-        if (u < nkw) {
-          const int hh = u >> 8, t = (u >> 3) & 31, j = u & 7;
-          *reinterpret_cast<uint32_t*>(rec_of(hh) + kRecKCodes + 32 * t + 4 * j) =
-              key_word(fl_img_k + 2 * hh * kD, t, j);
-        } else {
-          const int w = u - nkw, hh = w >> 8, oct = (w >> 6) & 3, m = (w >> 2) & 15, d = w & 3;
-          *reinterpret_cast<uint32_t*>(rec_of(hh) + kRecVCodes + 16 * (16 * oct + m) + 4 * d) =
-              value_word(fl_img_v + 4 * hh * kVImgRow, oct, m, d);
-        }
+      if (tid < 256) {
+        const int t = tid >> 3, j = tid & 7;  // Key word j of token t
+        *reinterpret_cast<uint32_t*>(rec + kRecKCodes + 32 * t + 4 * j) = key_word(img_k, t, j);
+      } else {
+        const int w = tid - 256, oct = (w >> 6) & 3, m = (w >> 2) & 15, d = w & 3;
+        *reinterpret_cast<uint32_t*>(rec + kRecVCodes + 16 * (16 * oct + m) + 4 * d) =
+            value_word(img_v, oct, m, d);
       }
       __syncthreads();  // the next block reuses the images
     }
     Q += kG * nfb;
   }
 
-  // Rotate + scale the new token; store it in slot n % 128.
+  // Rotate + scale the new token; head h goes to slot n % 128.
   const int slot = n % kR;
-  float a = 0.0f, bb = 0.0f;
-  if (h < hkv) {
-    a = in_to_f32(kin[0], is_bf16);
-    bb = in_to_f32(kin[1], is_bf16);
-    fht128_wave(a, bb);
-    const float hs = wave_tree_sumsq(a, bb);
-    if (lane == 0) part[h] = hs;
+  float a[2], bb[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int hh = wave + 8 * j;
+    a[j] = bb[j] = 0.0f;
+    if (hh < hkv) {
+      a[j] = in_to_f32(kin[j][0], is_bf16);
+      bb[j] = in_to_f32(kin[j][1], is_bf16);
+      if (ca.rope) {  // the new token sits at position n
+        const float2 cs = reinterpret_cast<const float2*>(ca.rope)[static_cast<size_t>(n) * 64 + lane];
+        rope_pair(a[j], bb[j], cs.x, cs.y);
+      }
+      fht128_wave(a[j], bb[j]);
+      const float hs = wave_tree_sumsq(a[j], bb[j]);
+      if (lane == 0) part[hh] = hs;
+    }
   }
   __syncthreads();
-  if (h < hkv) {
+  if (wave == (h & 7)) {
+    // head h's rotated values: register set h / 8 of this wave
+    const float ya = h >= 8 ? a[1] : a[0], yb = h >= 8 ? bb[1] : bb[0];
     float nrm, r;
     // TOKEN: the tree over all heads; HEAD: the head's own (within-head) tree
     scale_from_ss(ca.head_norm ? part[h] : tree16(part, hkv), nrm, r, ca.hw_rsq != 0);
-    const size_t bh = static_cast<size_t>(b) * hkv + h;
     uint16_t* rk = ca.res_k + (bh * kR + slot) * kD;
-    rk[lane] = f32_to_f16(mul_rn(a, r));
-    rk[lane + 64] = f32_to_f16(mul_rn(bb, r));
-    uint16_t* rv = ca.res_v + bh * kD * kR + slot;
-    rv[static_cast<size_t>(lane) * kR] = f32_to_f16_sat(in_to_f32(vin[0], is_bf16));
-    rv[static_cast<size_t>(lane + 64) * kR] = f32_to_f16_sat(in_to_f32(vin[1], is_bf16));
+    rk[lane] = f32_to_f16(mul_rn(ya, r));
+    rk[lane + 64] = f32_to_f16(mul_rn(yb, r));
     if (lane == 0 && (ca.head_norm || h == 0)) ca.res_norm[res_norm_at(ca, b, h, slot)] = f32_to_f16_sat(nrm);
   }
+  if (tid < kD) ca.res_v[(bh * kD + tid) * kR + slot] = f32_to_f16_sat(in_to_f32(vin, is_bf16));
+  // every thread has read {n, Q} before the workgroup counts itself in; the
+  // last of the sequence's workgroups writes the new state
+  __syncthreads();
   if (tid == 0) {
-    st[0] = n + 1;
-    st[1] = Q;
+    const int prev = __hip_atomic_fetch_add(ca.append_sync + b, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == hkv - 1) {
+      st[0] = n + 1;
+      st[1] = Q;
+      __hip_atomic_store(ca.append_sync + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -369,8 +399,9 @@ size_t prefill_lds_bytes(int hkv) {
 // NT threads: 512 for Hkv <= 8 (two workgroups share a CU, so that one's
 // loads overlap the other's arithmetic), 1024 above.  Four waves per SIMD
 // either way (at most 128 registers).
-// BF16: the input type (bf16 or fp16) as a compile-time choice.
-template <int NT, int BF16>
+// BF16: the input type (bf16 or fp16) as a compile-time choice; ROPE: the
+// Keys are rotated by position before the FHT (ca.rope non-null).
+template <int NT, int BF16, int ROPE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, int n_tokens, int Qn) {
@@ -427,6 +458,28 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
     } else {
 #pragma unroll
       for (int j = 0; j < 32; ++j) x[j] = 0.0f;
+    }
+    if constexpr (ROPE != 0) {
+      // token t0 + t at its position; element 32 tq + j pairs with element
+      // 32 (tq ^ 2) + j of the lane quad (channels i and i + 64)
+      const float2* cs = reinterpret_cast<const float2*>(ca.rope) +
+                         static_cast<size_t>(valid ? t0 + t : 0) * 64 + 32 * (tq & 1);
+      // eight elements at a time: both lanes of a pair read each other's
+      // elements of the chunk before either overwrites them
+      const bool lower = tq < 2;
+#pragma unroll
+      for (int j0 = 0; j0 < 32; j0 += 8) {
+        float mate[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mate[j] = quad_xor<2>(x[j0 + j]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float2 r = valid ? cs[j0 + j] : make_float2(1.0f, 0.0f);
+          float lo = lower ? x[j0 + j] : mate[j], hi = lower ? mate[j] : x[j0 + j];
+          rope_pair(lo, hi, r.x, r.y);
+          x[j0 + j] = lower ? lo : hi;
+        }
+      }
     }
     {
 #pragma clang fp contract(off)
@@ -605,12 +658,15 @@ CacheArgs make_args(const oscar_cache_geom* g, const oscar_cache* c) {
   a.block_table = c->block_table;
   a.seq_state = c->seq_state;
   a.error_flag = c->error_flag;
+  a.append_sync = c->append_sync;
   a.hkv = g->num_kv_heads;
   a.max_blocks = g->max_blocks_per_seq;
   a.nphys = g->num_physical_blocks;
   a.head_norm = g->norm_scope == OSCAR_NORM_HEAD ? 1 : 0;
   a.flush_blocks = g->flush_tokens == 128 ? 4 : 1;
   a.hw_rsq = g->key_scale == OSCAR_SCALE_HW_RSQ ? 1 : 0;
+  a.rope = g->rope_max_pos > 0 ? c->rope : nullptr;
+  a.rope_max_pos = g->rope_max_pos;
   return a;
 }
 
@@ -646,7 +702,8 @@ extern "C" oscar_status oscar_append_kv(const oscar_cache_geom* geom, const osca
   if (dtype != OSCAR_FP16 && dtype != OSCAR_BF16) return OSCAR_EINVAL;
   st = check_device();
   if (st != OSCAR_OK) return st;
-  hipLaunchKernelGGL(append_kernel, dim3(geom->batch), dim3(1024), 0, as_stream(stream),
+  hipLaunchKernelGGL(append_kernel, dim3(geom->batch * geom->num_kv_heads), dim3(512), 0,
+                     as_stream(stream),
                      make_args(geom, cache), static_cast<const uint16_t*>(k_new),
                      static_cast<const uint16_t*>(v_new), dtype == OSCAR_BF16 ? 1 : 0);
   return launch_status();
@@ -667,6 +724,8 @@ extern "C" oscar_status oscar_prefill_quantize(const oscar_cache_geom* geom,
   const int Qb = geom->flush_tokens == 128 ? (n_tokens > kR ? 4 * ((n_tokens - 1) / kR) : 0)
                                            : ((n_tokens > kR ? n_tokens - kR : 0) + 31) / 32;
   if (Qb > geom->max_blocks_per_seq) return OSCAR_EINVAL;
+  // positions 0 .. n_tokens - 1 must all have a (cos, sin) row
+  if (geom->rope_max_pos > 0 && n_tokens > geom->rope_max_pos) return OSCAR_EINVAL;
   st = check_device();
   if (st != OSCAR_OK) return st;
   if (n_tokens == 0) return OSCAR_OK;
@@ -682,11 +741,18 @@ extern "C" oscar_status oscar_prefill_quantize(const oscar_cache_geom* geom,
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                        static_cast<int>(n_tokens), Q);
   };
-  const bool bf16 = dtype == OSCAR_BF16;
-  if (geom->num_kv_heads <= 8)
-    bf16 ? launch(&prefill_kernel<512, 1>, 512) : launch(&prefill_kernel<512, 0>, 512);
-  else
-    bf16 ? launch(&prefill_kernel<1024, 1>, 1024) : launch(&prefill_kernel<1024, 0>, 1024);
+  const bool bf16 = dtype == OSCAR_BF16, rope = geom->rope_max_pos > 0;
+  if (geom->num_kv_heads <= 8) {
+    if (rope)
+      bf16 ? launch(&prefill_kernel<512, 1, 1>, 512) : launch(&prefill_kernel<512, 0, 1>, 512);
+    else
+      bf16 ? launch(&prefill_kernel<512, 1, 0>, 512) : launch(&prefill_kernel<512, 0, 0>, 512);
+  } else {
+    if (rope)
+      bf16 ? launch(&prefill_kernel<1024, 1, 1>, 1024) : launch(&prefill_kernel<1024, 0, 1>, 1024);
+    else
+      bf16 ? launch(&prefill_kernel<1024, 1, 0>, 1024) : launch(&prefill_kernel<1024, 0, 0>, 1024);
+  }
   st = launch_status();
   if (st != OSCAR_OK) return st;
   hipLaunchKernelGGL(prefill_finish_kernel, dim3(1), dim3(64), 0, as_stream(stream),

@@ -147,6 +147,17 @@ __device__ __forceinline__ float mul_rn(float a, float b) {
   return p;
 }
 
+// Rotary position embedding of one channel pair (x_i, x_{i+64}) with the
+// (cos, sin) of its position: a <- a c - b s, b <- b c + a s, each product
+// rounded to fp32 (not fused), then one add -- the oracle's sequence.  RoPE
+// sits right before the FHT; it is why that rotation runs online ([POP] 五).
+__device__ __forceinline__ void rope_pair(float& a, float& b, float c, float s) {
+#pragma clang fp contract(off)
+  const float ac = mul_rn(a, c), bs = mul_rn(b, s), bc = mul_rn(b, c), as = mul_rn(a, s);
+  a = ac - bs;
+  b = bc + as;
+}
+
 // Correctly rounded fp32 square root for x >= 0.  v_sqrt_f32 is accurate to
 // 1 ulp; the result is then fixed among its neighbours s-, s, s+.  With u the
 // spacing of the neighbours, x - s*s+ and x - s-*s are integer multiples of u^2

@@ -117,9 +117,78 @@ __global__ __launch_bounds__(256) void rotate_scale_key_kernel(
   }
 }
 
+// Offline absorption of the Value rotation into the projection weights
+// (reading notes §II Step One, query-side symmetric processing; summary
+// 方法步骤详情 (3)): storing V' = H V per KV head means W_v' = H W_v, and
+// the attention output, then in the rotated basis, is turned back by
+// W_o' = W_o H.  Both are the plain fp32 FHT (strides 1..64, then x
+// 1/sqrt(128)) of 128-element vectors of the weight matrix.
+
+// axis 1: vectors along a row; with cols % 128 == 0 they are the consecutive
+// 128-element runs of the row-major matrix.  One wave per vector.
+__global__ __launch_bounds__(256) void absorb_rows_kernel(const float* __restrict__ w,
+                                                          long long n_vec, float* out) {
+  const long long v = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (v >= n_vec) return;  // uniform per wave
+  const int lane = threadIdx.x & 63;
+  const size_t base = static_cast<size_t>(v) * kD;
+  float a = w[base + lane];
+  float b = w[base + lane + 64];
+  fht128_wave(a, b);
+  out[base + lane] = a;
+  out[base + lane + 64] = b;
+}
+
+// axis 0: vectors down a column, 128 rows apart from one 128-row block.  One
+// thread per (row block, column): neighbouring threads read neighbouring
+// columns, so every row access of a wave is one contiguous run.
+__global__ __launch_bounds__(256) void absorb_cols_kernel(const float* __restrict__ w,
+                                                          long long cols, long long n_thr,
+                                                          float* out) {
+#pragma clang fp contract(off)
+  const long long t = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= n_thr) return;
+  const long long blk = t / cols, j = t % cols;
+  const size_t base = static_cast<size_t>(blk) * kD * cols + j;
+  float x[kD];
+#pragma unroll
+  for (int i = 0; i < kD; ++i) x[i] = w[base + static_cast<size_t>(i) * cols];
+#pragma unroll
+  for (int hs = 1; hs < kD; hs <<= 1)
+#pragma unroll
+    for (int i = 0; i < kD; ++i)
+      if ((i & hs) == 0) {
+        const float a = x[i], b = x[i + hs];
+        x[i] = a + b;
+        x[i + hs] = a - b;
+      }
+#pragma unroll
+  for (int i = 0; i < kD; ++i) out[base + static_cast<size_t>(i) * cols] = x[i] * kFhtScale;
+}
+
 }  // namespace oscar
 
 using namespace oscar;
+
+extern "C" oscar_status oscar_absorb_value_rotation(const float* w, float* out, int64_t rows,
+                                                    int64_t cols, int32_t axis, void* stream) {
+  if (!w || !out || rows < 0 || cols < 0 || (axis != 0 && axis != 1)) return OSCAR_EINVAL;
+  if ((axis == 0 ? rows : cols) % kD != 0) return OSCAR_EINVAL;
+  if (rows != 0 && cols > (1LL << 62) / rows) return OSCAR_EINVAL;
+  const long long total = static_cast<long long>(rows) * cols;
+  const long long blocks = axis == 1 ? (total / kD + 3) / 4 : (total / kD + 255) / 256;
+  if (blocks > 0x7fffffffLL) return OSCAR_EINVAL;
+  oscar_status st = check_device();
+  if (st != OSCAR_OK) return st;
+  if (total == 0) return OSCAR_OK;
+  if (axis == 1)
+    hipLaunchKernelGGL(absorb_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       as_stream(stream), w, total / kD, out);
+  else
+    hipLaunchKernelGGL(absorb_cols_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       as_stream(stream), w, static_cast<long long>(cols), total / kD, out);
+  return launch_status();
+}
 
 extern "C" oscar_status oscar_rotate_scale(const void* x, oscar_dtype dtype, int32_t n_tokens,
                                            int32_t n_heads, oscar_rot_mode mode,

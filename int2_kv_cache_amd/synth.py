@@ -168,6 +168,16 @@ class Workload:
                    cast_bits(q, cfg.dtype))
 
 
+def rope_table(max_pos: int, theta: float = 1.0e6) -> np.ndarray:
+    """The model's rotary-position table, an input like its weights:
+    [max_pos][64] (cos, sin) pairs in fp32 for the angles pos * theta^(-i/64)
+    of channel pairs (i, i + 64), computed in fp64 and rounded once.  theta
+    1e6 is Qwen3's base (Llama-3.1 uses 5e5)."""
+    inv = theta ** (-np.arange(64, dtype=np.float64) / 64.0)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
 def workload(cfg_id: int, *, ctx: int | None = None, batch: int | None = None,
              seed: int | None = None) -> Workload:
     """Build workload cfg_id; ctx/batch override the sizes for small cases."""

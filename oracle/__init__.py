@@ -49,6 +49,7 @@ class Cache(ctypes.Structure):
         ("res_k", ctypes.c_void_p), ("res_v", ctypes.c_void_p),
         ("res_norm", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
         ("seq_state", ctypes.c_void_p), ("error_flag", ctypes.c_void_p),
+        ("rope", ctypes.c_void_p), ("rope_max_pos", ctypes.c_int32),
     ]
 
 
@@ -71,6 +72,10 @@ def lib():
             "orc_rotate_query": (None, [vp, i32, sz, vp]),
             "orc_tree_sumsq": (f32, [vp, i32]),
             "orc_rotate_scale_key": (None, [vp, i32, i32, i32, i32, vp, vp]),
+            "orc_rotate_scale_key_pos": (None, [vp, i32, i32, i32, i32, vp, i32, vp, vp]),
+            "orc_rope": (None, [vp, vp]),
+            "orc_rotate_query_pos": (None, [vp, i32, sz, vp, vp]),
+            "orc_absorb_value_rotation": (None, [vp, vp, i32, i32, i32]),
             "orc_quant_group32": (None, [vp, sz, vp, vp, vp]),
             "orc_kcode_byte": (sz, [i32, i32]),
             "orc_kcode_shift": (i32, [i32, i32]),
@@ -180,18 +185,61 @@ def rotate_query(q: np.ndarray, dtype: int) -> np.ndarray:
     return out
 
 
+def rope(x: np.ndarray, cs: np.ndarray) -> np.ndarray:
+    """RoPE of one 128-vector (fp32) with a (cos, sin) row cs [64][2]."""
+    y = np.ascontiguousarray(x, dtype=np.float32).copy()
+    cs = np.ascontiguousarray(cs, dtype=np.float32)
+    assert y.shape == (D,) and cs.shape == (D // 2, 2)
+    lib().orc_rope(_p(y), _p(cs))
+    return y
+
+
+def rotate_query_pos(q: np.ndarray, dtype: int, cs) -> np.ndarray:
+    """RoPE (every vector at the position of the (cos, sin) row cs, or none
+    when cs is None) then the FHT, fp32 out."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    out = np.empty(q.shape, dtype=np.float32)
+    csp = None
+    if cs is not None:
+        cs = np.ascontiguousarray(cs, dtype=np.float32)
+        assert cs.shape == (D // 2, 2)
+        csp = _p(cs)
+    lib().orc_rotate_query_pos(_p(q), dtype, q.size // D, csp, _p(out))
+    return out
+
+
+def absorb_value_rotation(w: np.ndarray, axis: int) -> np.ndarray:
+    """W_v' = H W_v per 128-row block (axis 0) or W_o' = W_o H per 128-column
+    block (axis 1), fp32."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    assert (rows if axis == 0 else cols) % D == 0
+    out = np.empty_like(w)
+    lib().orc_absorb_value_rotation(_p(w), _p(out), rows, cols, axis)
+    return out
+
+
 def tree_sumsq(y: np.ndarray) -> np.float32:
     y = np.ascontiguousarray(y, dtype=np.float32)
     return np.float32(lib().orc_tree_sumsq(_p(y), y.size))
 
 
-def rotate_scale_key(k: np.ndarray, dtype: int, norm_scope: int = NORM_TOKEN):
-    """k: [T, Hkv, 128] raw bits -> (khat fp16 bits [T,Hkv,128], norm fp16 bits)."""
+def rotate_scale_key(k: np.ndarray, dtype: int, norm_scope: int = NORM_TOKEN,
+                     rope_table=None, pos0: int = 0):
+    """k: [T, Hkv, 128] raw bits -> (khat fp16 bits [T,Hkv,128], norm fp16 bits).
+    With rope_table ([positions][64][2] fp32), token t is first rotated by
+    position pos0 + t."""
     k = np.ascontiguousarray(k, dtype=np.uint16)
     T, hkv, _ = k.shape
     khat = np.empty_like(k)
     norm = np.empty((T,) if norm_scope == NORM_TOKEN else (T, hkv), dtype=np.uint16)
-    lib().orc_rotate_scale_key(_p(k), dtype, T, hkv, norm_scope, _p(khat), _p(norm))
+    rp = None
+    if rope_table is not None:
+        rope_table = np.ascontiguousarray(rope_table, dtype=np.float32)
+        assert rope_table.shape[0] >= pos0 + T
+        rp = _p(rope_table)
+    lib().orc_rotate_scale_key_pos(_p(k), dtype, T, hkv, norm_scope, rp, pos0, _p(khat),
+                                   _p(norm))
     return khat, norm
 
 
@@ -239,7 +287,8 @@ class OracleCache:
 
     def __init__(self, batch: int, hq: int, hkv: int, max_blocks: int,
                  num_phys: int | None = None, norm_scope: int = NORM_TOKEN,
-                 block_table: np.ndarray | None = None, flush_tokens: int = 32):
+                 block_table: np.ndarray | None = None, flush_tokens: int = 32,
+                 rope_table: np.ndarray | None = None):
         self.batch, self.hq, self.hkv = batch, hq, hkv
         self.norm_scope = norm_scope
         self.max_blocks = max_blocks
@@ -260,10 +309,16 @@ class OracleCache:
         self.error_flag = np.zeros(1, np.int32)
         assert flush_tokens in (32, 128)
         self.flush_tokens = flush_tokens
+        self.rope_table = None
+        if rope_table is not None:
+            self.rope_table = np.ascontiguousarray(rope_table, dtype=np.float32)
+            assert self.rope_table.shape[1:] == (D // 2, 2)
         self._s = Cache(batch, hq, hkv, norm_scope, max_blocks, self.num_phys, flush_tokens,
                         _p(self.pool), _p(self.pool_norm), _p(self.res_k),
                         _p(self.res_v), _p(self.res_norm), _p(self.block_table),
-                        _p(self.seq_state), _p(self.error_flag))
+                        _p(self.seq_state), _p(self.error_flag),
+                        _p(self.rope_table) if self.rope_table is not None else None,
+                        self.rope_table.shape[0] if self.rope_table is not None else 0)
 
     @property
     def ref(self):

@@ -151,6 +151,78 @@ void orc_rotate_query(const uint16_t *q, int dtype, size_t n_vec, float *out)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Rotary position embedding (the reason the rotation must be online)       */
+/* ------------------------------------------------------------------------ */
+
+/* The model rotates queries and Keys by their position (RoPE) before they
+ * reach the cache, which is why the Hadamard rotation cannot be folded into
+ * the projection weights offline and has to run online after it ([POP] 五).
+ * The pages do not give RoPE's form; this is the common "rotate half" form:
+ * channels i and i + 64 (i < 64) form a pair rotated by an angle whose cosine
+ * and sine are cs[2i], cs[2i + 1] (a caller-supplied table, so that every
+ * implementation multiplies by the same numbers):
+ *     x[i]      <- x[i] c - x[i + 64] s
+ *     x[i + 64] <- x[i + 64] c + x[i] s
+ * each product rounded to fp32, then one fp32 add or subtract. */
+void orc_rope(float *x, const float *cs)
+{
+    for (int i = 0; i < ORC_D / 2; i++) {
+        const float a = x[i], b = x[i + ORC_D / 2];
+        const float c = cs[2 * i], s = cs[2 * i + 1];
+        const float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+        x[i] = ac - bs;
+        x[i + ORC_D / 2] = bc + as;
+    }
+}
+
+/* Query side with RoPE: every vector at the position whose (cos, sin) row is
+ * cs (NULL: no RoPE), then the FHT. */
+void orc_rotate_query_pos(const uint16_t *q, int dtype, size_t n_vec,
+                          const float *cs, float *out)
+{
+    for (size_t v = 0; v < n_vec; v++) {
+        float *y = out + v * ORC_D;
+        for (int c = 0; c < ORC_D; c++)
+            y[c] = orc_in_to_f32(q[v * ORC_D + c], dtype);
+        if (cs)
+            orc_rope(y, cs);
+        orc_fht128(y);
+    }
+}
+
+/* The Value rotation is absorbed into the weights offline: V' = H V per KV
+ * head means W_v' = H W_v (the FHT down each 128-row block of every column),
+ * and the attention output o' = H o is turned back by W_o' = W_o H (the FHT
+ * along each 128-column block of every row; H is symmetric) ([SUM]
+ * 方法步骤详情 (3); [RN] §II Step One, Query-side symmetric processing).
+ * w, out: row-major fp32 [rows][cols]; axis 0 needs rows % 128 == 0, axis 1
+ * cols % 128 == 0. */
+void orc_absorb_value_rotation(const float *w, float *out, int rows, int cols,
+                               int axis)
+{
+    float x[ORC_D];
+    if (axis == 0) {
+        for (int h = 0; h < rows / ORC_D; h++)
+            for (int j = 0; j < cols; j++) {
+                for (int i = 0; i < ORC_D; i++)
+                    x[i] = w[(size_t)(h * ORC_D + i) * cols + j];
+                orc_fht128(x);
+                for (int i = 0; i < ORC_D; i++)
+                    out[(size_t)(h * ORC_D + i) * cols + j] = x[i];
+            }
+    } else {
+        for (int r = 0; r < rows; r++)
+            for (int h = 0; h < cols / ORC_D; h++) {
+                for (int i = 0; i < ORC_D; i++)
+                    x[i] = w[(size_t)r * cols + h * ORC_D + i];
+                orc_fht128(x);
+                for (int i = 0; i < ORC_D; i++)
+                    out[(size_t)r * cols + h * ORC_D + i] = x[i];
+            }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Omni-Token Scaling                                                        */
 /* ------------------------------------------------------------------------ */
 
@@ -190,14 +262,24 @@ float orc_tree_sumsq(const float *y, int n)
 void orc_rotate_scale_key(const uint16_t *k, int dtype, int n_tokens, int hkv,
                           int norm_scope, uint16_t *khat, uint16_t *norm)
 {
+    orc_rotate_scale_key_pos(k, dtype, n_tokens, hkv, norm_scope, NULL, 0, khat, norm);
+}
+
+void orc_rotate_scale_key_pos(const uint16_t *k, int dtype, int n_tokens, int hkv,
+                              int norm_scope, const float *rope, int pos0,
+                              uint16_t *khat, uint16_t *norm)
+{
     const int w = hkv * ORC_D;
     float *y = (float *)malloc(sizeof(float) * (size_t)w);
     for (int t = 0; t < n_tokens; t++) {
         const uint16_t *kt = k + (size_t)t * w;
         for (int i = 0; i < w; i++)
             y[i] = orc_in_to_f32(kt[i], dtype);
-        for (int h = 0; h < hkv; h++)
+        for (int h = 0; h < hkv; h++) {
+            if (rope)
+                orc_rope(y + h * ORC_D, rope + (size_t)(pos0 + t) * ORC_D);
             orc_fht128(y + h * ORC_D);
+        }
         int groups = norm_scope == ORC_NORM_TOKEN ? 1 : hkv;
         int glen = norm_scope == ORC_NORM_TOKEN ? w : ORC_D;
         for (int g = 0; g < groups; g++) {
@@ -446,6 +528,10 @@ void orc_append_one(orc_cache *c, int b, const uint16_t *k_tok,
     int32_t *st = c->seq_state + 2 * b;
     int n = st[0], Q = st[1];
     const int hkv = c->num_kv_heads;
+    if (c->rope && n >= c->rope_max_pos) {
+        *c->error_flag |= 8;   /* no (cos, sin) for this position: dropped */
+        return;
+    }
     if (n - Q == ORC_R) {
         const int nf = c->flush_tokens == ORC_R ? ORC_R : ORC_G;   /* tokens per flush */
         if ((Q + nf) / ORC_G > c->max_blocks_per_seq) {
@@ -459,7 +545,8 @@ void orc_append_one(orc_cache *c, int b, const uint16_t *k_tok,
     int slot = n % ORC_R;
     uint16_t *khat = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)hkv * ORC_D);
     uint16_t *norm = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)hkv);
-    orc_rotate_scale_key(k_tok, dtype, 1, hkv, c->norm_scope, khat, norm);
+    /* the new token sits at position n */
+    orc_rotate_scale_key_pos(k_tok, dtype, 1, hkv, c->norm_scope, c->rope, n, khat, norm);
     for (int h = 0; h < hkv; h++) {
         memcpy(ring_k(c, b, h, slot), khat + h * ORC_D, ORC_D * sizeof(uint16_t));
         for (int ch = 0; ch < ORC_D; ch++)

@@ -58,7 +58,11 @@ typedef struct {
     uint16_t *res_norm;     /* TOKEN: [B][128 slots]; HEAD: [B][Hkv][128 slots] */
     const int32_t *block_table; /* [B][max_blocks_per_seq] physical block ids */
     int32_t *seq_state;     /* [B][2] = {n tokens, Q quantized tokens} */
-    int32_t *error_flag;    /* sticky bit 1: block table capacity exceeded */
+    int32_t *error_flag;    /* sticky bit 1: block table capacity exceeded;
+                               bit 8: a position beyond the RoPE table */
+    const float *rope;      /* NULL, or [rope_max_pos][64] (cos, sin) pairs:
+                               Keys are rotated by position before the FHT */
+    int32_t rope_max_pos;
 } orc_cache;
 
 /* number conversions */
@@ -74,10 +78,27 @@ float orc_fht_scale(void);
 void orc_fht128(float *x);
 void orc_rotate_query(const uint16_t *q, int dtype, size_t n_vec, float *out);
 
+/* rotary position embedding of one 128-vector: pairs (i, i + 64) rotated by
+ * the angle whose (cos, sin) is cs[2i], cs[2i + 1] */
+void orc_rope(float *x, const float *cs);
+void orc_rotate_query_pos(const uint16_t *q, int dtype, size_t n_vec,
+                          const float *cs, float *out);
+
+/* offline absorption of the Value rotation into weights: the FHT over every
+ * 128-block along axis 0 (rows: W_v [H*128][cols]) or axis 1 (columns:
+ * W_o [rows][H*128]) of a row-major fp32 matrix */
+void orc_absorb_value_rotation(const float *w, float *out, int rows, int cols,
+                               int axis);
+
 /* Omni-Token Scaling */
 float orc_tree_sumsq(const float *y, int n);
 void orc_rotate_scale_key(const uint16_t *k, int dtype, int n_tokens, int hkv,
                           int norm_scope, uint16_t *khat, uint16_t *norm);
+/* the same with RoPE first: token t at position pos0 + t, cos/sin from rope
+ * ([positions][64] pairs; NULL = no RoPE) */
+void orc_rotate_scale_key_pos(const uint16_t *k, int dtype, int n_tokens, int hkv,
+                              int norm_scope, const float *rope, int pos0,
+                              uint16_t *khat, uint16_t *norm);
 
 /* INT2 quantizer on one group of 32 fp16 values taken with a stride */
 void orc_quant_group32(const uint16_t *x16, size_t stride, float *delta,

@@ -73,7 +73,8 @@ class Pair:
     """The same cache on the GPU and in the oracle."""
 
     def __init__(self, wl: synth.Workload, max_ctx: int | None = None, table=None,
-                 norm_scope: int = ok.NORM_TOKEN, flush_tokens: int = 32):
+                 norm_scope: int = ok.NORM_TOKEN, flush_tokens: int = 32,
+                 rope_table: np.ndarray | None = None):
         cfg = wl.cfg
         self.wl = wl
         mctx = max_ctx or (max(wl.ctx_lens) + 8)
@@ -81,11 +82,13 @@ class Pair:
         self.table = table if table is not None else shuffled_table(cfg.batch, self.max_blocks)
         nphys = cfg.batch * self.max_blocks
         self.geom = ok.make_geom(cfg.batch, cfg.hq, cfg.hkv, self.max_blocks, nphys,
-                                 norm_scope=norm_scope, flush_tokens=flush_tokens)
-        self.gpu = ok.DeviceCache(self.geom, block_table=torch.from_numpy(self.table))
+                                 norm_scope=norm_scope, flush_tokens=flush_tokens,
+                                 rope_max_pos=0 if rope_table is None else len(rope_table))
+        self.gpu = ok.DeviceCache(self.geom, block_table=torch.from_numpy(self.table),
+                                  rope_table=rope_table)
         self.orc = oracle.OracleCache(cfg.batch, cfg.hq, cfg.hkv, self.max_blocks, nphys,
                                       block_table=self.table, norm_scope=norm_scope,
-                                      flush_tokens=flush_tokens)
+                                      flush_tokens=flush_tokens, rope_table=rope_table)
         self.dtype = cfg.dtype
 
     def prefill(self, b: int, k: np.ndarray, v: np.ndarray, gpu_bulk: bool = True):

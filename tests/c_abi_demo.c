@@ -106,13 +106,15 @@ int main(int argc, char **argv)
     c.block_table = dev_copy(table, sz.block_table);
     c.seq_state = dev_alloc(sz.seq_state);
     c.error_flag = dev_alloc(sz.error_flag);
+    c.append_sync = dev_alloc(sz.append_sync);
+    c.rope = NULL;   /* inputs arrive rotated by position (rope_max_pos 0) */
     void *dk = dev_copy(k, (size_t)n * row * 2), *dv = dev_copy(v, (size_t)n * row * 2);
     void *dkn = dev_copy(kn, row * 2), *dvn = dev_copy(vn, row * 2);
     void *dq = dev_copy(q, (size_t)hq * OSCAR_HEAD_DIM * 2);
     float *dout = dev_alloc((size_t)hq * OSCAR_HEAD_DIM * sizeof(float));
     float *dlse = dev_alloc((size_t)hq * sizeof(float));
     if (!c.pool || !c.pool_norm || !c.res_k || !c.res_v || !c.res_norm || !c.block_table ||
-        !c.seq_state || !c.error_flag || !dk || !dv || !dkn || !dvn || !dq || !dout || !dlse)
+        !c.seq_state || !c.error_flag || !c.append_sync || !dk || !dv || !dkn || !dvn || !dq || !dout || !dlse)
         return 2;
 
     CHECK_OSCAR(oscar_prefill_quantize(&g, &c, 0, dk, dv, n, dtype, NULL));

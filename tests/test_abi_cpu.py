@@ -35,6 +35,7 @@ def test_cache_layout_sizes():
     assert s.res_norm == 2 * 128 * 2
     assert s.block_table == 2 * 100 * 4
     assert s.seq_state == 2 * 2 * 4
+    assert s.error_flag == 4 and s.append_sync == 2 * 4
 
 
 @pytest.mark.parametrize("bad", [
@@ -111,6 +112,18 @@ def test_dense_calls_validate_before_touching_memory():
     assert _dense_call("oscar_dense_write_kv", gr, A, A, A, 1, 0, A, A, 8, A, None) == ok.EINVAL
     assert _dense_call("oscar_dense_write_kv", gr, A, A, A, 0, 120, A, A, 9, A, None) == ok.EINVAL
     assert _dense_call("oscar_dense_write_kv", gr, A, A, A, 0, 0, odd, A, 8, A, None) == ok.EINVAL
+
+
+def test_absorb_value_rotation_validates_before_launch():
+    """Shapes the transform cannot take are refused on the host (the fake
+    addresses are never dereferenced)."""
+    L = ok.lib()
+    A = ctypes.c_void_p(0x100000)
+    for w, o, rows, cols, axis in [(None, A, 128, 4, 0), (A, None, 128, 4, 0),
+                                   (A, A, 100, 4, 0), (A, A, 4, 100, 1), (A, A, 128, 128, 2),
+                                   (A, A, -128, 4, 0), (A, A, 128, -1, 0),
+                                   (A, A, 1 << 40, 1 << 40, 1)]:
+        assert L.oscar_absorb_value_rotation(w, o, rows, cols, axis, None) == ok.EINVAL
 
 
 def test_status_strings():

@@ -521,3 +521,30 @@ def test_zero_key_tokens_through_prefill_and_append():
     want, wlse = pr.orc.decode_attn(oracle.rotate_query(q, wl.cfg.dtype))
     assert float(np.abs(got - want).max()) <= ATOL
     assert np.allclose(glse, wlse, rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("scope,flush,hkv,batch", [
+    (0, 32, 16, 3), (1, 32, 16, 2), (0, 128, 5, 4), (1, 128, 3, 2), (0, 32, 1, 5)])
+def test_append_workgroup_per_head(scope, flush, hkv, batch):
+    """append_kv runs one workgroup per (sequence, KV head): every head count
+    (1, odd, 16 = four heads per wave), both norm scopes and both flush sizes
+    give the oracle's bytes over appends that cross flushes in ragged
+    sequences, and the per-sequence arrival counters are zero after every
+    call."""
+    base = synth.workload(2, ctx=600)
+    cfg = synth.Config("appendw", batch, 2 * hkv, hkv, None, synth.BF16, 0.4, (4, 8), 1)
+    wl = synth.Workload(cfg, 61 + hkv, [300 + 57 * b for b in range(batch)],
+                        (base.outlier_idx * 2)[:hkv])
+    pr = Pair(wl, max_ctx=max(wl.ctx_lens) + 150, norm_scope=scope, flush_tokens=flush)
+    for b in range(batch):
+        k, v = wl.prefill(b)
+        pr.prefill(b, k, v)
+    for i, (kn, vn, q) in enumerate(wl.steps(140)):
+        pr.append(kn, vn)
+        if i % 35 == 34:
+            pr.compare_state()
+            assert not pr.gpu.append_sync.any().item()
+    pr.compare_state()
+    want, _ = pr.orc.decode_attn(oracle.rotate_query(q, wl.cfg.dtype))
+    got, _ = pr.attend(q)
+    assert np.abs(got - want).max() <= ATOL
