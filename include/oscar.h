@@ -19,7 +19,8 @@
  *     current device; "host" pointers are ordinary host memory.
  *   - The caller owns and allocates every buffer (sizes from
  *     oscar_cache_layout / oscar_decode_workspace_bytes).  The library never
- *     allocates, frees or synchronizes.
+ *     allocates, frees or synchronizes; its only memory of its own is the
+ *     fixed per-GPU workspace of oscar_decode_attn_noalloc.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL is the default stream).  Results are visible after the
  *     caller synchronizes that stream.
@@ -304,6 +305,26 @@ OSCAR_API oscar_status oscar_decode_attn(const oscar_cache_geom *geom, const osc
                                const void *q, oscar_dtype q_dtype, float *out, float *lse,
                                void *workspace, size_t ws_bytes, int32_t num_splits,
                                int32_t max_ctx, oscar_attn_variant variant, void *stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation:
+ * oscar_decode_attn with its workspace taken from a library-owned device
+ * array (one per GPU, OSCAR_STATIC_WORKSPACE_BYTES = 8 MiB, held until the
+ * process ends) instead of an argument.  Same arguments (less the
+ * workspace), kernels and results as oscar_decode_attn.  Allocates nothing.
+ * The array's merge counters are cleared by a fill kernel enqueued on
+ * `stream` by the first call on each GPU, and every call leaves them zero.
+ * Calls on one GPU share its array: calls that overlap in time on one GPU
+ * (different streams, or one graph replayed on two streams) race.
+ * Errors: as oscar_decode_attn, and OSCAR_EWORKSPACE when the workspace the
+ * geometry and split count need (oscar_decode_workspace_bytes) exceeds
+ * OSCAR_STATIC_WORKSPACE_BYTES (e.g. 48 sequences with 1024 splits). */
+#define OSCAR_STATIC_WORKSPACE_BYTES ((size_t)8 << 20)
+OSCAR_API oscar_status oscar_decode_attn_noalloc(const oscar_cache_geom *geom,
+                                                 const oscar_cache *cache, const void *q,
+                                                 oscar_dtype q_dtype, float *out, float *lse,
+                                                 int32_t num_splits, int32_t max_ctx,
+                                                 oscar_attn_variant variant, void *stream);
 
 /* ---------------------------------------------------------------------------
  * The BF16 baseline: decode attention over an unquantized bf16 cache, the

@@ -29,7 +29,7 @@ HEAD_DIM, BLOCK_TOKENS, RESIDUAL_TOKENS, V_GROUP, RECORD_BYTES = 128, 32, 128, 3
 API = ("oscar_cache_layout", "oscar_rotate_scale", "oscar_quant_pack", "oscar_append_kv",
        "oscar_prefill_quantize", "oscar_decode_workspace_bytes", "oscar_decode_attn",
        "oscar_dense_write_kv", "oscar_dense_workspace_bytes", "oscar_dense_decode_attn",
-       "oscar_absorb_value_rotation", "oscar_status_str")
+       "oscar_absorb_value_rotation", "oscar_decode_attn_noalloc", "oscar_status_str")
 
 
 class OscarError(RuntimeError):
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
                                                   P(ctypes.c_size_t)]
         L.oscar_dense_decode_attn.argtypes = [P(Geom), vp, vp, vp, vp, vp, vp, vp, vp,
                                               ctypes.c_size_t, i32, i32, vp, vp]
+        L.oscar_decode_attn_noalloc.argtypes = [P(Geom), P(CacheBufs), vp, st, vp, vp, i32, i32,
+                                                st, vp]
         L.oscar_absorb_value_rotation.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, i32,
                                                   vp]
         for name in API:
@@ -232,6 +234,18 @@ def decode_attn(cache: DeviceCache, q, q_dtype: int, out, lse, workspace, max_ct
     _check("oscar_decode_attn", lib().oscar_decode_attn(
         ctypes.byref(cache.geom), ctypes.byref(cache.bufs), _ptr(q), q_dtype, _ptr(out),
         _ptr(lse), _ptr(workspace), nbytes, num_splits, max_ctx, variant, _stream(stream)))
+
+
+STATIC_WORKSPACE_BYTES = 8 << 20   # OSCAR_STATIC_WORKSPACE_BYTES
+
+
+def decode_attn_noalloc(cache: DeviceCache, q, q_dtype: int, out, lse, max_ctx: int,
+                        num_splits: int = 0, variant: int = ATTN_AUTO, stream=None):
+    """oscar_decode_attn_noalloc: decode attention with the library's own
+    per-GPU workspace, for callers that cannot allocate."""
+    _check("oscar_decode_attn_noalloc", lib().oscar_decode_attn_noalloc(
+        ctypes.byref(cache.geom), ctypes.byref(cache.bufs), _ptr(q), q_dtype, _ptr(out),
+        _ptr(lse), num_splits, max_ctx, variant, _stream(stream)))
 
 
 # ---------------------------------------------------------------- prepared calls

@@ -126,6 +126,19 @@ def test_absorb_value_rotation_validates_before_launch():
         assert L.oscar_absorb_value_rotation(w, o, rows, cols, axis, None) == ok.EINVAL
 
 
+def test_noalloc_refuses_a_workspace_beyond_its_array():
+    """Host-only: a call whose partials need more than the 8 MiB static
+    workspace returns OSCAR_EWORKSPACE before touching the device (the fake
+    addresses are never dereferenced)."""
+    g = ok.make_geom(48, 32, 8, 1100, 48 * 1100)
+    assert ok.decode_workspace_bytes(g, 35000, 1024)[1] > ok.STATIC_WORKSPACE_BYTES
+    A = ctypes.c_void_p(0x100000)
+    bufs = ok.CacheBufs(*([0x100000] * len(ok.CacheBufs._fields_)))
+    st = ok.lib().oscar_decode_attn_noalloc(ctypes.byref(g), ctypes.byref(bufs), A, ok.BF16, A,
+                                            None, 1024, 35000, ok.ATTN_AUTO, None)
+    assert st == ok.EWORKSPACE
+
+
 def test_status_strings():
     assert ok.status_str(ok.OK) == "ok"
     assert "workspace" in ok.status_str(ok.EWORKSPACE)
