@@ -144,9 +144,9 @@ typedef struct {
  *   block_table [B][max_blocks_per_seq] int32 physical block ids (caller fills)
  *   seq_state   [B][2] int32 = {n tokens, Q quantized tokens}; zero = empty
  *   error_flag  [1] int32 sticky bits (OSCAR_FLAG_*); caller zeroes it
- *   append_sync [B] int32, library-private (oscar_append_kv's per-sequence
- *               arrival counters); caller zeroes it once, every call leaves
- *               it zero
+ *   append_sync [B] int32, library-private (the per-sequence arrival
+ *               counters of oscar_append_kv's and oscar_prefill_quantize's
+ *               workgroups); caller zeroes it once, every call leaves it zero
  *   rope        NULL when geom->rope_max_pos == 0; else read-only
  *               [rope_max_pos][64][2] fp32 (cos, sin): the rotary position
  *               embedding of the model.  The popular-science article (五)

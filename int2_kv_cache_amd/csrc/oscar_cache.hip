@@ -42,11 +42,15 @@ __device__ __forceinline__ Range range32(const float* x) {
 // The 32 codes of a range's own values, packed two bits each: channel or
 // token i at bits 2 (i & 15) of w[i >> 4].  q1 = (x - zero) * (1/delta) is
 // within 2^-20 of the correctly rounded quotient (which lies in [0, 3]), so
-// rint(q1) is the code unless q1 lies within 2^-18 of a half integer; if any
-// of the 32 does, all 32 are recomputed with the exact quotient.  Codes
-// accumulate eight at a time as sum c * 4^k in fp32 (exact: below 2^16).
+// rint(q1) is the code unless q1 lies within 2^-18 of a half integer.  Such
+// values (exact ties among fp16 inputs make them common enough that most
+// waves hold one) are recomputed one at a time with the exact quotient, each
+// under its own branch, so a wave pays for the values some lane needs and
+// not for all 32.  Codes accumulate eight at a time as sum c * 4^k in fp32
+// (exact: below 2^16); a recomputed code adds its difference.
 __device__ __forceinline__ void codes32(const float* x, const Range& r, uint32_t w[2]) {
 #pragma clang fp contract(off)
+  constexpr float kNear = 0.5f - 0x1p-18f;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float far = 0.0f;
 #pragma unroll
@@ -56,14 +60,16 @@ __device__ __forceinline__ void codes32(const float* x, const Range& r, uint32_t
     far = fmaxf(far, fabsf(q1 - c));
     acc[i >> 3] = __builtin_fmaf(c, static_cast<float>(1u << (2 * (i & 7))), acc[i >> 3]);
   }
-  if (far >= 0.5f - 0x1p-18f) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc[k] = 0.0f;
+  if (far >= kNear) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const float q = rintf(__fdiv_rn(x[i] - r.zero, r.delta));
-      const float c = r.delta > 0.0f ? fminf(fmaxf(q, 0.0f), 3.0f) : 0.0f;
-      acc[i >> 3] = __builtin_fmaf(c, static_cast<float>(1u << (2 * (i & 7))), acc[i >> 3]);
+      const float q1 = (x[i] - r.zero) * r.rdelta;
+      const float c = rintf(q1);
+      if (fabsf(q1 - c) >= kNear) {
+        const float q = rintf(__fdiv_rn(x[i] - r.zero, r.delta));
+        const float ce = r.delta > 0.0f ? fminf(fmaxf(q, 0.0f), 3.0f) : 0.0f;
+        acc[i >> 3] = __builtin_fmaf(ce - c, static_cast<float>(1u << (2 * (i & 7))), acc[i >> 3]);
+      }
     }
   }
   w[0] = static_cast<uint32_t>(acc[0]) | (static_cast<uint32_t>(acc[1]) << 16);
@@ -176,6 +182,78 @@ template <int X>
 __device__ __forceinline__ float quad_xor(float x) {
   constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xF, 0xF, true));
+}
+
+// RoPE of the 128-vector a lane quad holds (lane tq: elements 32 tq ..
+// 32 tq + 31) at position pos: element j of lane tq pairs with element j of
+// lane tq ^ 2 (channels i and i + 64).  Four elements at a time: both lanes
+// of a pair read each other's elements of the chunk before either
+// overwrites them.  An invalid lane (no token) uses (1, 0).
+__device__ __forceinline__ void rope_quad(float* x, int tq, const float* rope, int pos,
+                                          bool valid) {
+  const float2* cs = reinterpret_cast<const float2*>(rope) +
+                     static_cast<size_t>(valid ? pos : 0) * 64 + 32 * (tq & 1);
+  const bool lower = tq < 2;
+#pragma unroll
+  for (int j0 = 0; j0 < 32; j0 += 4) {
+    float mate[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mate[j] = quad_xor<2>(x[j0 + j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float2 r = valid ? cs[j0 + j] : make_float2(1.0f, 0.0f);
+      float lo = lower ? x[j0 + j] : mate[j], hi = lower ? mate[j] : x[j0 + j];
+      rope_pair(lo, hi, r.x, r.y);
+      x[j0 + j] = lower ? lo : hi;
+    }
+  }
+}
+
+// FHT of the 128-vector a lane quad holds, then x 1/sqrt(128): butterflies
+// with strides 1..16 in registers, strides 32 and 64 across the quad (the
+// partner is lane tq ^ 1, then tq ^ 2; the upper lane of a pair takes
+// partner - own as one exactly rounded fma with -1) -- the oracle's stages
+// in the oracle's order.  Returns the vector's sum of squares by the same
+// pairwise tree (strides 1..16 in registers, 32 and 64 across the quad), the
+// same value in all four lanes.
+__device__ __forceinline__ float fht_quad(float* x, int tq) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int hs = 1; hs < 32; hs <<= 1)
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if ((j & hs) == 0) {
+        const float a = x[j], b = x[j + hs];
+        x[j] = a + b;
+        x[j + hs] = a - b;
+      }
+  const float sg1 = (tq & 1) ? -1.0f : 1.0f, sg2 = (tq & 2) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) x[j] = __builtin_fmaf(sg1, x[j], quad_xor<1>(x[j]));
+#pragma unroll
+  for (int j = 0; j < 32; ++j) x[j] = __builtin_fmaf(sg2, x[j], quad_xor<2>(x[j]));
+#pragma unroll
+  for (int j = 0; j < 32; ++j) x[j] = x[j] * kFhtScale;
+  // levels 1, 2, 4 within each run of 8 (the same additions as level by
+  // level over all 32), then levels 8 and 16
+  float s8[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float sq[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sq[j] = x[8 * c + j] * x[8 * c + j];
+#pragma unroll
+    for (int hs = 1; hs < 8; hs <<= 1)
+#pragma unroll
+      for (int j = 0; j < 8; j += 2 * hs) sq[j] = sq[j] + sq[j + hs];
+    s8[c] = sq[0];
+  }
+  s8[0] = s8[0] + s8[1];
+  s8[2] = s8[2] + s8[3];
+  float ssum = s8[0] + s8[2];
+  ssum = ssum + quad_xor<1>(ssum);
+  ssum = ssum + quad_xor<2>(ssum);
+  return ssum;
 }
 
 // ---------------------------------------------------------------- append
@@ -375,7 +453,9 @@ __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_
 // ---------------------------------------------------------------- prefill
 // grid nb + nr, NT threads: workgroup j < nb turns tokens 32j..32j+31 (all
 // KV heads) into block j; workgroup nb + c writes window chunk c (tokens
-// Q + 32c ..) without quantizing.
+// Q + 32c ..) without quantizing.  The last workgroup to finish (arrival
+// counter append_sync[seq]) writes {n, Q}.  Barriers order LDS only, so the
+// Value loads issued before the Key ranges stay in flight across them.
 //
 // Rotation: four lanes per (token, head) vector, lane tq holding elements
 // 32 tq .. 32 tq + 31; butterflies with strides 1..16 are in registers,
@@ -402,9 +482,10 @@ size_t prefill_lds_bytes(int hkv) {
 // BF16: the input type (bf16 or fp16) as a compile-time choice; ROPE: the
 // Keys are rotated by position before the FHT (ca.rope non-null).
 template <int NT, int BF16, int ROPE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
-                    const uint16_t* __restrict__ v, int n_tokens, int Qn) {
+__device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
+                                             const uint16_t* __restrict__ k,
+                                             const uint16_t* __restrict__ v, int n_tokens,
+                                             int Qn) {
   constexpr int is_bf16 = BF16;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int hkv = ca.hkv;
@@ -415,11 +496,6 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
   float* part = reinterpret_cast<float*>(prm);                          // rotation phase: [32][hkv]
   float* tok_r = part + 32 * hkv;                          // [32] or [32][hkv] (HEAD)
 
-  if (ca.seq_state[2 * seq] != 0) {
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-      atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_NONEMPTY));
-    return;
-  }
   const int nb = Qn / kG;
   const bool ring = static_cast<int>(blockIdx.x) >= nb;
   const int t0 = ring ? Qn + 32 * (blockIdx.x - nb) : 32 * blockIdx.x;
@@ -459,63 +535,11 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
 #pragma unroll
       for (int j = 0; j < 32; ++j) x[j] = 0.0f;
     }
-    if constexpr (ROPE != 0) {
-      // token t0 + t at its position; element 32 tq + j pairs with element
-      // 32 (tq ^ 2) + j of the lane quad (channels i and i + 64)
-      const float2* cs = reinterpret_cast<const float2*>(ca.rope) +
-                         static_cast<size_t>(valid ? t0 + t : 0) * 64 + 32 * (tq & 1);
-      // eight elements at a time: both lanes of a pair read each other's
-      // elements of the chunk before either overwrites them
-      const bool lower = tq < 2;
-#pragma unroll
-      for (int j0 = 0; j0 < 32; j0 += 8) {
-        float mate[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mate[j] = quad_xor<2>(x[j0 + j]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float2 r = valid ? cs[j0 + j] : make_float2(1.0f, 0.0f);
-          float lo = lower ? x[j0 + j] : mate[j], hi = lower ? mate[j] : x[j0 + j];
-          rope_pair(lo, hi, r.x, r.y);
-          x[j0 + j] = lower ? lo : hi;
-        }
-      }
-    }
-    {
-#pragma clang fp contract(off)
-#pragma unroll
-      for (int hs = 1; hs < 32; hs <<= 1)
-#pragma unroll
-        for (int j = 0; j < 32; ++j)
-          if ((j & hs) == 0) {
-            const float a = x[j], b = x[j + hs];
-            x[j] = a + b;
-            x[j + hs] = a - b;
-          }
-      // strides 32 and 64: the partner is lane tq ^ 1, then tq ^ 2; the
-      // upper lane of a pair takes partner - own, as one exactly rounded
-      // fma with -1
-      const float sg1 = (tq & 1) ? -1.0f : 1.0f, sg2 = (tq & 2) ? -1.0f : 1.0f;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) x[j] = __builtin_fmaf(sg1, x[j], quad_xor<1>(x[j]));
-#pragma unroll
-      for (int j = 0; j < 32; ++j) x[j] = __builtin_fmaf(sg2, x[j], quad_xor<2>(x[j]));
-#pragma unroll
-      for (int j = 0; j < 32; ++j) x[j] = x[j] * kFhtScale;
-      float sq[32];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) sq[j] = x[j] * x[j];
-#pragma unroll
-      for (int hs = 1; hs < 32; hs <<= 1)
-#pragma unroll
-        for (int j = 0; j < 32; j += 2 * hs) sq[j] = sq[j] + sq[j + hs];
-      float ssum = sq[0];
-      ssum = ssum + quad_xor<1>(ssum);
-      ssum = ssum + quad_xor<2>(ssum);
-      if (tq == 0 && vtx < nvec) part[t * hkv + h] = ssum;
-    }
+    if constexpr (ROPE != 0) rope_quad(x, tq, ca.rope, t0 + t, valid);
+    const float ssum = fht_quad(x, tq);
+    if (tq == 0 && vtx < nvec) part[t * hkv + h] = ssum;
   }
-  __syncthreads();
+  barrier_lds();
   // one factor per token (TOKEN: tree over the heads) or per (token, head)
   // (HEAD: the head's own tree); NT >= 32 * 16
   if (tid < 32 * (ca.head_norm ? hkv : 1)) {
@@ -531,7 +555,7 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
         ca.pool_norm[pool_norm_at(ca, p, h, tl)] = f32_to_f16_sat(nrm);
     }
   }
-  __syncthreads();
+  barrier_lds();
   // ---- scaled Keys (and, for a window chunk, fp16 Values) to LDS or the ring
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
@@ -564,21 +588,7 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
     }
   }
   if (ring) return;
-  __syncthreads();
-
-  // The Value inputs of this thread's Value units (at most two: 32 Hkv 4
-  // units over NT threads) are requested now and land during the Key phase.
-  uint4 vraw[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int u = tid + NT * i;
-    if (u < 32 * hkv * 4) {
-      const int t = u / (hkv * 4), h = (u >> 2) % hkv, g = u & 3;
-      const uint4* src = reinterpret_cast<const uint4*>(v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * g);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) vraw[i][q] = src[q];
-    }
-  }
+  barrier_lds();
 
   // ---- Key ranges and codes: unit (head, channel) over the 32 tokens
   for (int u = tid; u < hkv * kD; u += NT) {
@@ -595,7 +605,21 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
     img_k[(2 * h) * kD + c] = w[0];      // tokens 0..15
     img_k[(2 * h + 1) * kD + c] = w[1];  // tokens 16..31
   }
-  __syncthreads();  // k_hat is dead: its space takes the Value image
+  // The Value inputs of this thread's Value units (at most two: 32 Hkv 4
+  // units over NT threads) are requested now.
+  uint4 vraw[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = tid + NT * i;
+    if (u < 32 * hkv * 4) {
+      const int t = u / (hkv * 4), h = (u >> 2) % hkv, g = u & 3;
+      const uint4* src = reinterpret_cast<const uint4*>(v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * g);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) vraw[i][q] = src[q];
+    }
+  }
+
+  barrier_lds();  // k_hat is dead: its space takes the Value image
 
   // ---- Value ranges and codes: unit (token, head, group) over 32 channels
   static_assert(32 * 16 * 4 <= 2 * 1024 && 32 * 8 * 4 <= 2 * 512, "two Value units per thread");
@@ -622,7 +646,7 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
     codes32(x, r, w);
     *reinterpret_cast<uint2*>(img_v + (h * 4 + g) * kVImgRow + 2 * t) = uint2{w[0], w[1]};
   }
-  __syncthreads();
+  barrier_lds();
 
   // ---- code words.  Key word (head, token, j): channels 16 j .. 16 j + 15
   // of the token row.  Value word (head, octet, group d, quarter, i): tokens
@@ -641,10 +665,32 @@ void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
   }
 }
 
-__global__ void prefill_finish_kernel(int32_t* seq_state, int seq, int n_tokens, int Qn) {
-  if (threadIdx.x == 0 && seq_state[2 * seq] == 0) {
-    seq_state[2 * seq] = n_tokens;
-    seq_state[2 * seq + 1] = Qn;
+template <int NT, int BF16, int ROPE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void prefill_kernel(CacheArgs ca, int seq, const uint16_t* __restrict__ k,
+                    const uint16_t* __restrict__ v, int n_tokens, int Qn) {
+  // every workgroup reads {n} before any of them arrives below
+  const bool nonempty = ca.seq_state[2 * seq] != 0;
+  if (!nonempty)
+    prefill_unit<NT, BF16, ROPE>(ca, seq, k, v, n_tokens, Qn);
+  else if (blockIdx.x == 0 && threadIdx.x == 0)
+    atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_NONEMPTY));
+  // the last workgroup to finish writes {n, Q} (not if the sequence was not
+  // empty) and leaves the arrival counter zero.  Every wave has used its
+  // read of {n} (a branch) before the barrier, so no read can see the new
+  // state; the writes need no ordering within the launch (they are read by
+  // later launches), hence a relaxed counter and no cache write-back.
+  barrier_lds();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(ca.append_sync + seq, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    if (old == static_cast<int>(gridDim.x) - 1) {
+      __hip_atomic_store(ca.append_sync + seq, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!nonempty) {
+        ca.seq_state[2 * seq] = n_tokens;
+        ca.seq_state[2 * seq + 1] = Qn;
+      }
+    }
   }
 }
 
@@ -753,9 +799,5 @@ extern "C" oscar_status oscar_prefill_quantize(const oscar_cache_geom* geom,
     else
       bf16 ? launch(&prefill_kernel<1024, 1, 0>, 1024) : launch(&prefill_kernel<1024, 0, 0>, 1024);
   }
-  st = launch_status();
-  if (st != OSCAR_OK) return st;
-  hipLaunchKernelGGL(prefill_finish_kernel, dim3(1), dim3(64), 0, as_stream(stream),
-                     cache->seq_state, static_cast<int>(seq), static_cast<int>(n_tokens), Q);
   return launch_status();
 }

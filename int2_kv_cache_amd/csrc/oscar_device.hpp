@@ -81,6 +81,15 @@ __device__ __forceinline__ float lane_xor(float x) {
   }
 }
 
+// Workgroup barrier that orders LDS accesses only: loads and stores to
+// global memory in flight (prefetched inputs, results) stay in flight across
+// it, where __syncthreads would wait for every one of them.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void fht128_wave(float& a, float& b) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
