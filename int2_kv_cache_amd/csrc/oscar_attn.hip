@@ -1120,9 +1120,44 @@ void attn_mfma_kernel(AttnArgs A) {
   // (PUB 0: the counter's acquire, on this workgroup's CU, precedes the
   // barrier that every thread passed before reading the partials)
   if (!lds_last) return;
-  // all of a thread's partials are requested at once (one round trip for
-  // up to 32 splits at one output per thread)
-  constexpr int kChunk = NI == 1 ? 32 : 16;
+  if (S <= 32) {
+    // Lane j < S of each wave reads split j's (m, l) of the wave's head and
+    // every lane reads its channel of all S partial outputs, all at once; the
+    // weights come from wave reductions (the same values in every lane) and
+    // the outputs fold in split order, weight j read from lane j.
+    const int lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int idx = tid + NT * i, hh = idx >> 7, c = idx & 127;
+      if (idx >= GRP * kD) break;  // whole waves: GRP * 128 is a multiple of 64
+      const size_t base = pbase + static_cast<size_t>(hh) * S;
+      float mj = -INFINITY, lj = 0.0f, oc[32];
+      if (lane < S) {
+        mj = load_dev(ml + 2 * (base + lane));
+        lj = load_dev(ml + 2 * (base + lane) + 1);
+      }
+#pragma unroll
+      for (int j = 0; j < 32; ++j) oc[j] = j < S ? load_dev(A.ws_o + (base + j) * kD + c) : 0.0f;
+      float M = mj;
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
+      const float wj = mj == -INFINITY ? 0.0f : exp2f(mj - M);
+      float Lw = wj * lj;
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) Lw += __shfl_xor(Lw, sh);
+      float Ow = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (j < S)
+          Ow += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j)) *
+                oc[j];
+      finish(idx, M, Lw, Ow);
+    }
+    if (tid == 0) __hip_atomic_store(A.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  // more splits: a thread's partials are requested 16 at a time
+  constexpr int kChunk = 16;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int idx = tid + NT * i, hh = idx >> 7, c = idx & 127;

@@ -115,6 +115,27 @@ __device__ __forceinline__ uint32_t value_word(const uint32_t* img, int oct, int
   return word;
 }
 
+// Transpose of a 16 x 16 matrix of 2-bit fields: on return r[f] field i is
+// what r[i] field f was (field i of a word at bits 2i).  Recursive block
+// swap: at block size s the fields of rows r (bit s of r clear) whose index
+// has bit s set trade places with the fields of row r + s whose index has it
+// clear, two bitfield inserts per pair of rows.
+__device__ __forceinline__ void transpose16x2(uint32_t* r) {
+  constexpr uint32_t kMask[4] = {0x33333333u, 0x0F0F0F0Fu, 0x00FF00FFu, 0x0000FFFFu};
+#pragma unroll
+  for (int k = 3; k >= 0; --k) {
+    const int s = 1 << k, sh = 2 * s;
+    const uint32_t m = kMask[k];  // fields whose index has bit s clear
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & s) continue;
+      const uint32_t a = r[i], b = r[i + s];
+      r[i] = (a & m) | ((b << sh) & ~m);
+      r[i + s] = ((a >> sh) & m) | (b & ~m);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- quant_pack
 // grid (n_blocks, Hkv), 256 threads: one (block, KV head) record.  Thread
 // tg < 128 takes Key channel tg over the 32 tokens, thread tg >= 128 the
@@ -605,33 +626,25 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
     img_k[(2 * h) * kD + c] = w[0];      // tokens 0..15
     img_k[(2 * h + 1) * kD + c] = w[1];  // tokens 16..31
   }
-  // The Value inputs of this thread's Value units (at most two: 32 Hkv 4
-  // units over NT threads) are requested now.
-  uint4 vraw[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int u = tid + NT * i;
-    if (u < 32 * hkv * 4) {
-      const int t = u / (hkv * 4), h = (u >> 2) % hkv, g = u & 3;
-      const uint4* src = reinterpret_cast<const uint4*>(v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * g);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) vraw[i][q] = src[q];
-    }
-  }
-
   barrier_lds();  // k_hat is dead: its space takes the Value image
 
   // ---- Value ranges and codes: unit (token, head, group) over 32 channels
+  // (at most two per thread: 32 Hkv 4 units over NT threads).  A unit's
+  // inputs are requested just before it is processed.
   static_assert(32 * 16 * 4 <= 2 * 1024 && 32 * 8 * 4 <= 2 * 512, "two Value units per thread");
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int u = tid + NT * i;
     if (u >= 32 * hkv * 4) break;
     const int t = u / (hkv * 4), h = (u >> 2) % hkv, g = u & 3;
+    const uint4* src = reinterpret_cast<const uint4*>(v + static_cast<size_t>(t0 + t) * row + h * kD + 32 * g);
+    uint4 vraw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vraw[q] = src[q];
     float x[32];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint4 w8 = vraw[i][q];
+      const uint4 w8 = vraw[q];
       const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -648,19 +661,47 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
   }
   barrier_lds();
 
-  // ---- code words.  Key word (head, token, j): channels 16 j .. 16 j + 15
-  // of the token row.  Value word (head, octet, group d, quarter, i): tokens
-  // 8 octet .. + 7 at channels 32 d + 16 e + 4 quarter + i, e = 0, 1.
-  const int nkw = hkv * 32 * 8;
-  for (int u = tid; u < 2 * nkw; u += NT) {
-    if (u < nkw) {
-      const int h = u >> 8, t = (u >> 3) & 31, j = u & 7;
-      *reinterpret_cast<uint32_t*>(rec_of(h) + kRecKCodes + 32 * t + 4 * j) =
-          key_word(img_k + 2 * h * kD, t, j);
+  // ---- code words, sixteen per thread by one 16 x 16 transpose of 2-bit
+  // fields.  Key word (head, token t, j): channels 16 j .. 16 j + 15 of token
+  // t, i.e. field (t & 15) of the image words of those 16 channels (token
+  // half t >> 4).  Value word (head, octet, m, group d): field m of the
+  // image words (w_e of token 8 octet + kk) for the 8 tokens and e = 0, 1,
+  // at field 8 e + s(kk) (s: the record's token order within an octet).
+  if (tid < hkv * 32) {
+    uint32_t r[16];
+    if (tid < hkv * 16) {
+      const int h = tid >> 4, half = (tid >> 3) & 1, j = tid & 7;
+      const uint4* src = reinterpret_cast<const uint4*>(img_k + (2 * h + half) * kD + 16 * j);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 w4 = src[q];
+        r[4 * q] = w4.x;
+        r[4 * q + 1] = w4.y;
+        r[4 * q + 2] = w4.z;
+        r[4 * q + 3] = w4.w;
+      }
+      transpose16x2(r);
+      uint8_t* dst = rec_of(h) + kRecKCodes + 32 * (16 * half) + 4 * j;
+#pragma unroll
+      for (int f = 0; f < 16; ++f) *reinterpret_cast<uint32_t*>(dst + 32 * f) = r[f];
     } else {
-      const int w = u - nkw, h = w >> 8, oct = (w >> 6) & 3, m = (w >> 2) & 15, d = w & 3;
-      *reinterpret_cast<uint32_t*>(rec_of(h) + kRecVCodes + 16 * (16 * oct + m) + 4 * d) =
-          value_word(img_v + 4 * h * kVImgRow, oct, m, d);
+      const int w = tid - hkv * 16, h = w >> 4, d = (w >> 2) & 3, oct = w & 3;
+      const uint4* src = reinterpret_cast<const uint4*>(img_v + (h * 4 + d) * kVImgRow + 16 * oct);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 w4 = src[q];  // tokens 2q, 2q + 1 of the octet, words e = 0, 1
+        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int kk = 2 * q + (f >> 1), e = f & 1;
+          const int sk = (kk & 4) | ((kk & 1) << 1) | ((kk >> 1) & 1);
+          r[8 * e + sk] = ww[f];
+        }
+      }
+      transpose16x2(r);
+      uint8_t* dst = rec_of(h) + kRecVCodes + 16 * (16 * oct) + 4 * d;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) *reinterpret_cast<uint32_t*>(dst + 16 * m) = r[m];
     }
   }
 }
