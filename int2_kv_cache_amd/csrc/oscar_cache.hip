@@ -316,9 +316,10 @@ __device__ __forceinline__ bool state_ok(int n, int Q, int max_blocks) {
 // token (and, when the window is full, quantizes head h's share of the
 // flushed block); 512 threads, so that each of up to 8 heads of the new
 // token rotates in a wave of its own (two per wave for 9..16 heads).  Every workgroup of a sequence reads {n, Q}
-// first; the last of them to finish (counted in append_sync[b]) writes the
-// new state and resets the counter, so no workgroup can see a half-updated
-// state.  In TOKEN scope every workgroup rotates all heads of the new token
+// first and counts itself in (append_sync[b]) once it knows the append goes
+// ahead; the last to count itself in writes the new state at its end and
+// resets the counter, so no workgroup can see a half-updated state.  The
+// barriers order LDS only, so the counter's round trip overlaps the work.  In TOKEN scope every workgroup rotates all heads of the new token
 // (2 KB) so that it has the norm over all heads without talking to the
 // others; the same tree order as a single workgroup gives the same bits.
 __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_t* __restrict__ k_new,
@@ -362,7 +363,8 @@ __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_
     return;
   }
   const size_t bh = static_cast<size_t>(b) * hkv + h;
-  if (n - Q == kR) {
+  const bool flush = n - Q == kR;
+  if (flush) {
     const int nfb = ca.flush_blocks, j0 = Q / kG;
     if (j0 + nfb > ca.max_blocks) {
       if (tid == 0 && h == 0) atomicOr(ca.error_flag, static_cast<int32_t>(OSCAR_FLAG_CAPACITY));
@@ -375,6 +377,18 @@ __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_
         return;
       }
     }
+  }
+  // The append will happen (every check above is the same for all of the
+  // sequence's workgroups): count this workgroup in now, while its work
+  // proceeds.  The counter only orders the reads of {n, Q} -- each
+  // workgroup has read them by now -- before the last arrival's write of
+  // the new state, which later launches read.
+  int prev = 0;
+  if (tid == 0)
+    prev = __hip_atomic_fetch_add(ca.append_sync + b, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  if (flush) {
+    const int nfb = ca.flush_blocks, j0 = Q / kG;
     for (int fi = 0; fi < nfb; ++fi) {
       const int p = ca.block_table[static_cast<size_t>(b) * ca.max_blocks + j0 + fi];
       const int s0 = (Q + kG * fi) % kR;
@@ -387,7 +401,7 @@ __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_
           reinterpret_cast<const uint4*>(ca.res_k + (bh * kR + s0) * kD)[tid];
       reinterpret_cast<uint4*>(fv)[tid] = reinterpret_cast<const uint4*>(
           ca.res_v + (bh * kD + (tid >> 2)) * kR + s0)[tid & 3];
-      __syncthreads();
+      barrier_lds();
       float x[32];
       uint32_t cw[2];
       if (tid < kD) {
@@ -411,7 +425,7 @@ __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_
         codes32(x, r, cw);
         *reinterpret_cast<uint2*>(img_v + g * kVImgRow + 2 * t) = uint2{cw[0], cw[1]};
       }
-      __syncthreads();
+      barrier_lds();
       if (tid < 256) {
         const int t = tid >> 3, j = tid & 7;  // Key word j of token t
         *reinterpret_cast<uint32_t*>(rec + kRecKCodes + 32 * t + 4 * j) = key_word(img_k, t, j);
@@ -420,7 +434,7 @@ __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_
         *reinterpret_cast<uint32_t*>(rec + kRecVCodes + 16 * (16 * oct + m) + 4 * d) =
             value_word(img_v, oct, m, d);
       }
-      __syncthreads();  // the next block reuses the images
+      barrier_lds();  // the next block reuses the images
     }
     Q += kG * nfb;
   }
@@ -444,7 +458,7 @@ __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_
       if (lane == 0) part[hh] = hs;
     }
   }
-  __syncthreads();
+  barrier_lds();
   if (wave == (h & 7)) {
     // head h's rotated values: register set h / 8 of this wave
     const float ya = h >= 8 ? a[1] : a[0], yb = h >= 8 ? bb[1] : bb[0];
@@ -457,17 +471,12 @@ __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_
     if (lane == 0 && (ca.head_norm || h == 0)) ca.res_norm[res_norm_at(ca, b, h, slot)] = f32_to_f16_sat(nrm);
   }
   if (tid < kD) ca.res_v[(bh * kD + tid) * kR + slot] = f32_to_f16_sat(in_to_f32(vin, is_bf16));
-  // every thread has read {n, Q} before the workgroup counts itself in; the
-  // last of the sequence's workgroups writes the new state
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(ca.append_sync + b, 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == hkv - 1) {
-      st[0] = n + 1;
-      st[1] = Q;
-      __hip_atomic_store(ca.append_sync + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+  // the last of the sequence's workgroups to count itself in writes the new
+  // state and resets the counter
+  if (tid == 0 && prev == hkv - 1) {
+    st[0] = n + 1;
+    st[1] = Q;
+    __hip_atomic_store(ca.append_sync + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
