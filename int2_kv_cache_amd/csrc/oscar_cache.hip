@@ -19,6 +19,8 @@ namespace oscar {
 // canonicalised (+0) extremes; 1/delta (0 when delta == 0).
 struct Range {
   float zero, delta, rdelta;
+  float c0;     // -zero * rdelta, rounded: the fast quotient is x * rdelta + c0
+  float near;   // a fast quotient this close to a half integer is recomputed
   uint32_t zm;  // fp16 bits of min | max << 16 (both fp16 values)
 };
 __device__ __forceinline__ Range range32(const float* x) {
@@ -35,40 +37,51 @@ __device__ __forceinline__ Range range32(const float* x) {
   r.zero = mn;
   r.delta = __fdiv_rn(mx - mn, 3.0f);
   r.rdelta = r.delta > 0.0f ? __fdiv_rn(1.0f, r.delta) : 0.0f;
+  r.c0 = -mn * r.rdelta;
+  // q1 = fl(x * rdelta + c0) (one fma) against q = fl(fl(x - min) / delta):
+  // rdelta and c0 carry relative errors below 2^-24 each, x * rdelta + c0 =
+  // (x - min) / delta + e with |e| <= 2^-24 (|q| + |c0|) (1 + 2^-23), q1
+  // adds one rounding (|q1| <= 3.5) and q two, so |q1 - q| <= 2^-24 (14 +
+  // 1.01 |c0|).  Codes can differ only if a half integer lies within that
+  // distance of q1.
+  r.near = 0.5f - 0x1p-24f * (16.0f + 1.01f * fabsf(r.c0));
   r.zm = static_cast<uint32_t>(f32_to_f16(mn)) | (static_cast<uint32_t>(f32_to_f16(mx)) << 16);
   return r;
 }
 
 // The 32 codes of a range's own values, packed two bits each: channel or
-// token i at bits 2 (i & 15) of w[i >> 4].  q1 = (x - zero) * (1/delta) is
-// within 2^-20 of the correctly rounded quotient (which lies in [0, 3]), so
-// rint(q1) is the code unless q1 lies within 2^-18 of a half integer.  Such
-// values (exact ties among fp16 inputs make them common enough that most
-// waves hold one) are recomputed one at a time with the exact quotient, each
-// under its own branch, so a wave pays for the values some lane needs and
-// not for all 32.  Codes accumulate eight at a time as sum c * 4^k in fp32
-// (exact: below 2^16); a recomputed code adds its difference.
+// token i at bits 2 (i & 15) of w[i >> 4].  The fast quotient q1 = x *
+// (1/delta) - min/delta (one fma) is close enough to the correctly rounded
+// quotient of (x - min) by delta (bound at range32) that rint(q1) is the code
+// unless q1 lies near a half integer.  Such values (exact ties among fp16
+// inputs make them common enough that most waves hold one) are recomputed
+// one at a time with the exact quotient: a wave-wide mask per value records
+// which lanes need it, so a wave pays only for the values some lane needs.
+// Codes accumulate eight at a time as sum c * 4^k in fp32 (exact: below
+// 2^16); a recomputed code adds its difference.
 __device__ __forceinline__ void codes32(const float* x, const Range& r, uint32_t w[2]) {
 #pragma clang fp contract(off)
-  constexpr float kNear = 0.5f - 0x1p-18f;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float far = 0.0f;
+  // near[i]: the lanes whose value i lies near a half integer (a wave-wide
+  // mask, so that finding them later costs no vector instructions)
+  uint64_t near[32], any = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const float q1 = (x[i] - r.zero) * r.rdelta;
-    const float c = rintf(q1);
-    far = fmaxf(far, fabsf(q1 - c));
+    const float c = rintf(__builtin_fmaf(x[i], r.rdelta, r.c0));
+    near[i] = __ballot(fabsf(__builtin_fmaf(x[i], r.rdelta, r.c0) - c) >= r.near);
+    any |= near[i];
     acc[i >> 3] = __builtin_fmaf(c, static_cast<float>(1u << (2 * (i & 7))), acc[i >> 3]);
   }
-  if (far >= kNear) {
+  if (any) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const float q1 = (x[i] - r.zero) * r.rdelta;
-      const float c = rintf(q1);
-      if (fabsf(q1 - c) >= kNear) {
+      if (near[i]) {  // uniform: some lane needs value i; the wave recomputes it
+        const float c = rintf(__builtin_fmaf(x[i], r.rdelta, r.c0));
         const float q = rintf(__fdiv_rn(x[i] - r.zero, r.delta));
         const float ce = r.delta > 0.0f ? fminf(fmaxf(q, 0.0f), 3.0f) : 0.0f;
-        acc[i >> 3] = __builtin_fmaf(ce - c, static_cast<float>(1u << (2 * (i & 7))), acc[i >> 3]);
+        // the correction applies in the lanes of the mask only
+        const float corr = __builtin_amdgcn_inverse_ballot_w64(near[i]) ? ce - c : 0.0f;
+        acc[i >> 3] = __builtin_fmaf(corr, static_cast<float>(1u << (2 * (i & 7))), acc[i >> 3]);
       }
     }
   }
