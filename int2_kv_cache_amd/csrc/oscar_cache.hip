@@ -49,6 +49,36 @@ __device__ __forceinline__ Range range32(const float* x) {
   return r;
 }
 
+// Range of a Value unit from its 32 inputs as fp32 (bf16 or fp16 values,
+// exact), before their rounding to the stored fp16 values.  That rounding
+// (clamp to +-65504, then round to nearest even) is monotone, so the stored
+// extremes are the rounded input extremes: only those two are converted.
+// Below 2^-14 the rounding moves a value by at most 2^-25 (fp16's subnormal
+// spacing is 2^-24; bf16 values from 2^-14 to 65504 are fp16 values
+// already), so the fast quotient of an unrounded input lies within a further
+// 2^-25 rdelta of the stored value's, and the near margin widens by that.
+// Returns false when an input is NaN or beyond +-65504 (the min / max
+// propagate NaN): such a unit takes the plain path on its stored values.
+__device__ __forceinline__ bool range32_row(const float* x, Range& r) {
+#pragma clang fp contract(off)
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    mn = __builtin_elementwise_minimum(mn, x[i]);
+    mx = __builtin_elementwise_maximum(mx, x[i]);
+  }
+  if (!(mn >= -65504.0f && mx <= 65504.0f)) return false;
+  mn = f16_to_f32(f32_to_f16(mn)) + 0.0f;
+  mx = f16_to_f32(f32_to_f16(mx)) + 0.0f;
+  r.zero = mn;
+  r.delta = __fdiv_rn(mx - mn, 3.0f);
+  r.rdelta = r.delta > 0.0f ? __fdiv_rn(1.0f, r.delta) : 0.0f;
+  r.c0 = -mn * r.rdelta;
+  r.near = 0.5f - 0x1p-24f * (16.0f + 1.01f * fabsf(r.c0) + 0.51f * r.rdelta);
+  r.zm = static_cast<uint32_t>(f32_to_f16(mn)) | (static_cast<uint32_t>(f32_to_f16(mx)) << 16);
+  return true;
+}
+
 // The 32 codes of a range's own values, packed two bits each: channel or
 // token i at bits 2 (i & 15) of w[i >> 4].  The fast quotient q1 = x *
 // (1/delta) - min/delta (one fma) is close enough to the correctly rounded
@@ -59,7 +89,11 @@ __device__ __forceinline__ Range range32(const float* x) {
 // which lanes need it, so a wave pays only for the values some lane needs.
 // Codes accumulate eight at a time as sum c * 4^k in fp32 (exact: below
 // 2^16); a recomputed code adds its difference.
-__device__ __forceinline__ void codes32(const float* x, const Range& r, uint32_t w[2]) {
+// ROW: x holds a Value unit's unrounded inputs and r comes from range32_row;
+// a value recomputed exactly is first rounded to its stored fp16 value, and
+// a NaN input (it always counts as near) makes the call return false.
+template <bool ROW = false>
+__device__ __forceinline__ bool codes32(const float* x, const Range& r, uint32_t w[2]) {
 #pragma clang fp contract(off)
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   // near[i]: the lanes whose value i lies near a half integer (a wave-wide
@@ -68,16 +102,20 @@ __device__ __forceinline__ void codes32(const float* x, const Range& r, uint32_t
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const float c = rintf(__builtin_fmaf(x[i], r.rdelta, r.c0));
-    near[i] = __ballot(fabsf(__builtin_fmaf(x[i], r.rdelta, r.c0) - c) >= r.near);
+    const float d = fabsf(__builtin_fmaf(x[i], r.rdelta, r.c0) - c);
+    near[i] = __ballot(ROW ? !(d < r.near) : d >= r.near);
     any |= near[i];
     acc[i >> 3] = __builtin_fmaf(c, static_cast<float>(1u << (2 * (i & 7))), acc[i >> 3]);
   }
+  bool ok = true;
   if (any) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       if (near[i]) {  // uniform: some lane needs value i; the wave recomputes it
         const float c = rintf(__builtin_fmaf(x[i], r.rdelta, r.c0));
-        const float q = rintf(__fdiv_rn(x[i] - r.zero, r.delta));
+        const float xs = ROW ? f16_to_f32(f32_to_f16(x[i])) : x[i];
+        if (ROW && x[i] != x[i]) ok = false;
+        const float q = rintf(__fdiv_rn(xs - r.zero, r.delta));
         const float ce = r.delta > 0.0f ? fminf(fmaxf(q, 0.0f), 3.0f) : 0.0f;
         // the correction applies in the lanes of the mask only
         const float corr = __builtin_amdgcn_inverse_ballot_w64(near[i]) ? ce - c : 0.0f;
@@ -87,6 +125,7 @@ __device__ __forceinline__ void codes32(const float* x, const Range& r, uint32_t
   }
   w[0] = static_cast<uint32_t>(acc[0]) | (static_cast<uint32_t>(acc[1]) << 16);
   w[1] = static_cast<uint32_t>(acc[2]) | (static_cast<uint32_t>(acc[3]) << 16);
+  return ok;
 }
 
 // Value image: per (head, group) a row of 32 tokens x 2 words (channels
@@ -663,22 +702,28 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
     uint4 vraw[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) vraw[q] = src[q];
-    float x[32];
+    float x[32];  // the inputs as fp32 (exact)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint4 w8 = vraw[q];
       const uint32_t ww[4] = {w8.x, w8.y, w8.z, w8.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t xh = static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1)));
-        x[8 * q + e] = f16_to_f32(f32_to_f16_sat(in_to_f32(xh, is_bf16)));
+      for (int e = 0; e < 8; ++e)
+        x[8 * q + e] = in_to_f32(static_cast<uint16_t>(ww[e >> 1] >> (16 * (e & 1))), is_bf16);
+    }
+    Range r;
+    uint32_t w[2];
+    const bool fast = range32_row(x, r) && codes32<true>(x, r, w);
+    if (__ballot(!fast)) {  // uniform: a NaN or out-of-range input in some lane
+      if (!fast) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) x[j] = f16_to_f32(f32_to_f16_sat(x[j]));
+        r = range32(x);
+        codes32(x, r, w);
       }
     }
-    const Range r = range32(x);
     reinterpret_cast<uint32_t*>(rec_of(h) + kRecVParam)[32 * g + t] =
         static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
-    uint32_t w[2];
-    codes32(x, r, w);
     *reinterpret_cast<uint2*>(img_v + (h * 4 + g) * kVImgRow + 2 * t) = uint2{w[0], w[1]};
   }
   barrier_lds();

@@ -133,6 +133,39 @@ def test_prefill_and_flush_value_ties():
     pr.compare_state()
 
 
+def _tiny_values(rng, shape, dtype):
+    """Values whose 32-channel groups run from ordinary to far below fp16's
+    smallest normal (2^-14): bf16 inputs there round to fp16's subnormal grid
+    (2^-24) when stored.  Some groups hold one repeated tiny value, some
+    exact zeros of either sign."""
+    x = rng.standard_normal(shape).astype(np.float32)
+    g = x.reshape(-1, 32)
+    scale = np.float32([1.0, 1e-3, 2e-5, 3e-6, 4e-7, 6e-8, 2e-8])
+    g *= scale[rng.integers(0, scale.size, size=(g.shape[0], 1))]
+    rep = rng.random(g.shape[0]) < 0.05
+    g[rep] = g[rep, :1] * np.float32(1e-6)
+    g.ravel()[rng.integers(0, g.size, size=g.size // 50)] = 0.0
+    g.ravel()[rng.integers(0, g.size, size=g.size // 50)] = -0.0
+    return synth.cast_bits(x, dtype)
+
+
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_prefill_tiny_values(cfg):
+    """Values below fp16's normal range through bulk prefill and appends that
+    flush: bit-exact with the oracle, which rounds every Value to fp16 before
+    its range and codes."""
+    rng = np.random.default_rng(41 + cfg)
+    n0 = 32 * 7 + 133
+    wl = synth.workload(cfg, ctx=n0 + 50)
+    pr = Pair(wl)
+    k, _ = wl.prefill(0, n0)
+    pr.prefill(0, k, _tiny_values(rng, (n0, wl.cfg.hkv, 128), wl.cfg.dtype))
+    pr.compare_state()
+    for kn, _, _ in wl.steps(50):
+        pr.append(kn, _tiny_values(rng, (1, wl.cfg.hkv, 128), wl.cfg.dtype))
+    pr.compare_state()
+
+
 @pytest.mark.parametrize("cfg,batch,steps", [(0, 1, 300), (1, 2, 200)])
 def test_append_sequence_bit_exact(cfg, batch, steps):
     """Appends from an empty cache cross several window flushes."""
