@@ -23,14 +23,11 @@ struct Range {
   float near;   // a fast quotient this close to a half integer is recomputed
   uint32_t zm;  // fp16 bits of min | max << 16 (both fp16 values)
 };
-__device__ __forceinline__ Range range32(const float* x) {
+// From the extremes (fp16 values as fp32): both canonicalised to +0 if
+// zero, delta, 1/delta and the fast-quotient constants.  `wide` widens the
+// near margin for inputs that are not yet the quantized values (below).
+__device__ __forceinline__ Range range_of(float mn, float mx, float wide) {
 #pragma clang fp contract(off)
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int i = 1; i < 32; ++i) {
-    mn = fminf(mn, x[i]);
-    mx = fmaxf(mx, x[i]);
-  }
   mn = mn + 0.0f;
   mx = mx + 0.0f;
   Range r;
@@ -44,9 +41,31 @@ __device__ __forceinline__ Range range32(const float* x) {
   // adds one rounding (|q1| <= 3.5) and q two, so |q1 - q| <= 2^-24 (14 +
   // 1.01 |c0|).  Codes can differ only if a half integer lies within that
   // distance of q1.
-  r.near = 0.5f - 0x1p-24f * (16.0f + 1.01f * fabsf(r.c0));
+  r.near = 0.5f - 0x1p-24f * (16.0f + 1.01f * fabsf(r.c0) + wide * r.rdelta);
   r.zm = static_cast<uint32_t>(f32_to_f16(mn)) | (static_cast<uint32_t>(f32_to_f16(mx)) << 16);
   return r;
+}
+__device__ __forceinline__ Range range32(const float* x) {
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+  return range_of(mn, mx, 0.0f);
+}
+
+// Range of 32 fp16 values held as 16 packed pairs: two values per
+// instruction, in fp16 (the extremes are exact there).
+__device__ __forceinline__ Range range32_pk(const half2_t* xp) {
+  half2_t mn = xp[0], mx = xp[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    mn = __builtin_elementwise_minimum(mn, xp[i]);
+    mx = __builtin_elementwise_maximum(mx, xp[i]);
+  }
+  return range_of(static_cast<float>(__builtin_elementwise_minimum(mn.x, mn.y)),
+                  static_cast<float>(__builtin_elementwise_maximum(mx.x, mx.y)), 0.0f);
 }
 
 // Range of a Value unit from its 32 inputs as fp32 (bf16 or fp16 values,
@@ -68,14 +87,7 @@ __device__ __forceinline__ bool range32_row(const float* x, Range& r) {
     mx = __builtin_elementwise_maximum(mx, x[i]);
   }
   if (!(mn >= -65504.0f && mx <= 65504.0f)) return false;
-  mn = f16_to_f32(f32_to_f16(mn)) + 0.0f;
-  mx = f16_to_f32(f32_to_f16(mx)) + 0.0f;
-  r.zero = mn;
-  r.delta = __fdiv_rn(mx - mn, 3.0f);
-  r.rdelta = r.delta > 0.0f ? __fdiv_rn(1.0f, r.delta) : 0.0f;
-  r.c0 = -mn * r.rdelta;
-  r.near = 0.5f - 0x1p-24f * (16.0f + 1.01f * fabsf(r.c0) + 0.51f * r.rdelta);
-  r.zm = static_cast<uint32_t>(f32_to_f16(mn)) | (static_cast<uint32_t>(f32_to_f16(mx)) << 16);
+  r = range_of(f16_to_f32(f32_to_f16(mn)), f16_to_f32(f32_to_f16(mx)), 0.51f);
   return true;
 }
 
@@ -92,8 +104,9 @@ __device__ __forceinline__ bool range32_row(const float* x, Range& r) {
 // ROW: x holds a Value unit's unrounded inputs and r comes from range32_row;
 // a value recomputed exactly is first rounded to its stored fp16 value, and
 // a NaN input (it always counts as near) makes the call return false.
-template <bool ROW = false>
-__device__ __forceinline__ bool codes32(const float* x, const Range& r, uint32_t w[2]) {
+// xv(i): value i as fp32.
+template <bool ROW = false, class XV>
+__device__ __forceinline__ bool codes32_of(XV xv, const Range& r, uint32_t w[2]) {
 #pragma clang fp contract(off)
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   // near[i]: the lanes whose value i lies near a half integer (a wave-wide
@@ -101,8 +114,8 @@ __device__ __forceinline__ bool codes32(const float* x, const Range& r, uint32_t
   uint64_t near[32], any = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const float c = rintf(__builtin_fmaf(x[i], r.rdelta, r.c0));
-    const float d = fabsf(__builtin_fmaf(x[i], r.rdelta, r.c0) - c);
+    const float c = rintf(__builtin_fmaf(xv(i), r.rdelta, r.c0));
+    const float d = fabsf(__builtin_fmaf(xv(i), r.rdelta, r.c0) - c);
     near[i] = __ballot(ROW ? !(d < r.near) : d >= r.near);
     any |= near[i];
     acc[i >> 3] = __builtin_fmaf(c, static_cast<float>(1u << (2 * (i & 7))), acc[i >> 3]);
@@ -112,9 +125,9 @@ __device__ __forceinline__ bool codes32(const float* x, const Range& r, uint32_t
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       if (near[i]) {  // uniform: some lane needs value i; the wave recomputes it
-        const float c = rintf(__builtin_fmaf(x[i], r.rdelta, r.c0));
-        const float xs = ROW ? f16_to_f32(f32_to_f16(x[i])) : x[i];
-        if (ROW && x[i] != x[i]) ok = false;
+        const float c = rintf(__builtin_fmaf(xv(i), r.rdelta, r.c0));
+        const float xs = ROW ? f16_to_f32(f32_to_f16(xv(i))) : xv(i);
+        if (ROW && xv(i) != xv(i)) ok = false;
         const float q = rintf(__fdiv_rn(xs - r.zero, r.delta));
         const float ce = r.delta > 0.0f ? fminf(fmaxf(q, 0.0f), 3.0f) : 0.0f;
         // the correction applies in the lanes of the mask only
@@ -126,6 +139,10 @@ __device__ __forceinline__ bool codes32(const float* x, const Range& r, uint32_t
   w[0] = static_cast<uint32_t>(acc[0]) | (static_cast<uint32_t>(acc[1]) << 16);
   w[1] = static_cast<uint32_t>(acc[2]) | (static_cast<uint32_t>(acc[3]) << 16);
   return ok;
+}
+template <bool ROW = false>
+__device__ __forceinline__ bool codes32(const float* x, const Range& r, uint32_t w[2]) {
+  return codes32_of<ROW>([x](int i) { return x[i]; }, r, w);
 }
 
 // Value image: per (head, group) a row of 32 tokens x 2 words (channels
@@ -550,7 +567,7 @@ __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_
 // words of 16 codes; whole code words of the record are then assembled from
 // that image (Key: one word = 16 channels of one token; Value: one word = 8
 // tokens x 2 channels).
-// Dynamic LDS: k_hat [32][Hkv][128] fp16 (the Value image reuses it once the
+// Dynamic LDS: k_hat [Hkv][32][128] fp16 (the Value image reuses it once the
 // Key ranges are done), then the Key image [Hkv][2][128] words (the rotation
 // phase borrows it for the per-head sums and per-token factors).
 size_t prefill_lds_bytes(int hkv) {
@@ -571,7 +588,7 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
   constexpr int is_bf16 = BF16;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int hkv = ca.hkv;
-  uint16_t* khs = reinterpret_cast<uint16_t*>(dyn);                      // [32][hkv][128]
+  uint16_t* khs = reinterpret_cast<uint16_t*>(dyn);                      // [hkv][32][128]
   uint32_t* img_v = reinterpret_cast<uint32_t*>(dyn);                    // [hkv][4][kVImgRow]
   uint8_t* prm = dyn + static_cast<size_t>(32) * hkv * kD * 2;
   uint32_t* img_k = reinterpret_cast<uint32_t*>(prm);                    // [hkv][2][128]
@@ -590,7 +607,8 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
   }
   auto rec_of = [&](int h) { return ca.pool + (static_cast<size_t>(p) * hkv + h) * kRec; };
 
-  // ---- rotation and sums of squares (1 round for Hkv <= 8, 2 for Hkv <= 16)
+  // ---- rotation and sums of squares (32 Hkv vectors, four lanes each: one
+  // or two rounds of NT threads).  Vector (head h, token t) is 32 h + t.
   const int nvec = 32 * hkv;
   float y[2][32];
 #pragma unroll
@@ -598,7 +616,7 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
     const int task = rr * NT + tid;
     const int vtx = task >> 2, tq = task & 3;
     if (rr * NT >= nvec * 4) break;  // uniform
-    const int t = vtx / hkv, h = vtx % hkv;
+    const int t = vtx & 31, h = vtx >> 5;
     const bool valid = vtx < nvec && t0 + t < n_tokens;
     float* x = y[rr];
     if (valid) {
@@ -644,14 +662,12 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
     const int task = rr * NT + tid;
     const int vtx = task >> 2, tq = task & 3;
     if (rr * NT >= nvec * 4) break;
-    const int t = vtx / hkv, h = vtx % hkv;
+    const int t = vtx & 31, h = vtx >> 5;
     if (vtx < nvec && t0 + t < n_tokens) {
       const float r = tok_r[ca.head_norm ? t * hkv + h : t];
       uint32_t kw[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        kw[e] = static_cast<uint32_t>(f32_to_f16(mul_rn(y[rr][2 * e], r))) |
-                (static_cast<uint32_t>(f32_to_f16(mul_rn(y[rr][2 * e + 1], r))) << 16);
+      for (int e = 0; e < 16; ++e) kw[e] = f32x2_to_f16x2(mul_rn(y[rr][2 * e], r), mul_rn(y[rr][2 * e + 1], r));
       uint4* dst;
       if (ring) {
         const int slot = (t0 + t) % kR;
@@ -663,7 +679,7 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
         for (int j = 0; j < 32; ++j)
           rv[static_cast<size_t>(32 * tq + j) * kR] = f32_to_f16_sat(in_to_f32(vs[j], is_bf16));
       } else {
-        dst = reinterpret_cast<uint4*>(khs + (t * hkv + h) * kD + 32 * tq);
+        dst = reinterpret_cast<uint4*>(khs + (h * 32 + t) * kD + 32 * tq);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) dst[q] = uint4{kw[4 * q], kw[4 * q + 1], kw[4 * q + 2], kw[4 * q + 3]};
@@ -675,15 +691,19 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
   // ---- Key ranges and codes: unit (head, channel) over the 32 tokens
   for (int u = tid; u < hkv * kD; u += NT) {
     const int h = u >> 7, c = u & 127;
-    float x[32];
+    const _Float16* kc = reinterpret_cast<const _Float16*>(khs) + h * 32 * kD + c;
+    half2_t xp[16];  // tokens 2i, 2i + 1
 #pragma unroll
-    for (int t = 0; t < 32; ++t) x[t] = f16_to_f32(khs[(t * hkv + h) * kD + c]);
-    const Range r = range32(x);
+    for (int i = 0; i < 16; ++i) {
+      xp[i].x = kc[(2 * i) * kD];
+      xp[i].y = kc[(2 * i + 1) * kD];
+    }
+    const Range r = range32_pk(xp);
     uint8_t* rec = rec_of(h);
     reinterpret_cast<uint16_t*>(rec + kRecKDelta)[c] = f32_to_f16(r.delta);
     reinterpret_cast<uint16_t*>(rec + kRecKZero)[c] = static_cast<uint16_t>(r.zm);
     uint32_t w[2];
-    codes32(x, r, w);
+    codes32_of([&xp](int i) { return static_cast<float>(i & 1 ? xp[i >> 1].y : xp[i >> 1].x); }, r, w);
     img_k[(2 * h) * kD + c] = w[0];      // tokens 0..15
     img_k[(2 * h + 1) * kD + c] = w[1];  // tokens 16..31
   }
