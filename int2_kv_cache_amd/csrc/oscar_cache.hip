@@ -149,6 +149,10 @@ __device__ __forceinline__ bool codes32(const float* x, const Range& r, uint32_t
 // 0..15 and 16..31 of the group), padded to 80 words so that the four groups
 // a wave reads fall in different banks.
 constexpr int kVImgRow = 80;
+// Prefill: the heads' Value images one after another, 4 words apart beyond
+// their 4 rows, so that a wave's image writes (all heads, four groups, two
+// tokens) spread over the banks.
+constexpr int kVImgHead = 4 * kVImgRow + 4;
 
 // Key code word j of token t (channels 16 j .. 16 j + 15) from a head's Key
 // image [2][128] (word s of channel c holds tokens 16 s .. 16 s + 15).
@@ -567,7 +571,10 @@ __global__ __launch_bounds__(512) void append_kernel(CacheArgs ca, const uint16_
 // words of 16 codes; whole code words of the record are then assembled from
 // that image (Key: one word = 16 channels of one token; Value: one word = 8
 // tokens x 2 channels).
-// Dynamic LDS: k_hat [Hkv][32][128] fp16 (the Value image reuses it once the
+// Dynamic LDS: k_hat [Hkv][32][128] fp16, the 16-byte chunks of token t's
+// row permuted by chunk ^ (t & 3) so that a wave's chunk writes (four lanes
+// per row, 16 consecutive rows) fall in distinct banks; channel c of token t
+// sits at element c ^ 8 (t & 3).  (The Value image reuses it once the
 // Key ranges are done), then the Key image [Hkv][2][128] words (the rotation
 // phase borrows it for the per-head sums and per-token factors).
 size_t prefill_lds_bytes(int hkv) {
@@ -589,7 +596,7 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int hkv = ca.hkv;
   uint16_t* khs = reinterpret_cast<uint16_t*>(dyn);                      // [hkv][32][128]
-  uint32_t* img_v = reinterpret_cast<uint32_t*>(dyn);                    // [hkv][4][kVImgRow]
+  uint32_t* img_v = reinterpret_cast<uint32_t*>(dyn);                    // [hkv][kVImgHead]
   uint8_t* prm = dyn + static_cast<size_t>(32) * hkv * kD * 2;
   uint32_t* img_k = reinterpret_cast<uint32_t*>(prm);                    // [hkv][2][128]
   float* part = reinterpret_cast<float*>(prm);                          // rotation phase: [32][hkv]
@@ -681,8 +688,9 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
       } else {
         dst = reinterpret_cast<uint4*>(khs + (h * 32 + t) * kD + 32 * tq);
       }
+      const int sw = ring ? 0 : (t & 3);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dst[q] = uint4{kw[4 * q], kw[4 * q + 1], kw[4 * q + 2], kw[4 * q + 3]};
+      for (int q = 0; q < 4; ++q) dst[q ^ sw] = uint4{kw[4 * q], kw[4 * q + 1], kw[4 * q + 2], kw[4 * q + 3]};
     }
   }
   if (ring) return;
@@ -691,12 +699,13 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
   // ---- Key ranges and codes: unit (head, channel) over the 32 tokens
   for (int u = tid; u < hkv * kD; u += NT) {
     const int h = u >> 7, c = u & 127;
-    const _Float16* kc = reinterpret_cast<const _Float16*>(khs) + h * 32 * kD + c;
+    const _Float16* kh = reinterpret_cast<const _Float16*>(khs) + h * 32 * kD;
+    const _Float16* kc[4] = {kh + c, kh + (c ^ 8), kh + (c ^ 16), kh + (c ^ 24)};  // by t & 3
     half2_t xp[16];  // tokens 2i, 2i + 1
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      xp[i].x = kc[(2 * i) * kD];
-      xp[i].y = kc[(2 * i + 1) * kD];
+      xp[i].x = kc[(2 * i) & 3][(2 * i) * kD];
+      xp[i].y = kc[(2 * i + 1) & 3][(2 * i + 1) * kD];
     }
     const Range r = range32_pk(xp);
     uint8_t* rec = rec_of(h);
@@ -744,7 +753,7 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
     }
     reinterpret_cast<uint32_t*>(rec_of(h) + kRecVParam)[32 * g + t] =
         static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
-    *reinterpret_cast<uint2*>(img_v + (h * 4 + g) * kVImgRow + 2 * t) = uint2{w[0], w[1]};
+    *reinterpret_cast<uint2*>(img_v + h * kVImgHead + g * kVImgRow + 2 * t) = uint2{w[0], w[1]};
   }
   barrier_lds();
 
@@ -773,7 +782,7 @@ __device__ __forceinline__ void prefill_unit(const CacheArgs& ca, int seq,
       for (int f = 0; f < 16; ++f) *reinterpret_cast<uint32_t*>(dst + 32 * f) = r[f];
     } else {
       const int w = tid - hkv * 16, h = w >> 4, d = (w >> 2) & 3, oct = w & 3;
-      const uint4* src = reinterpret_cast<const uint4*>(img_v + (h * 4 + d) * kVImgRow + 16 * oct);
+      const uint4* src = reinterpret_cast<const uint4*>(img_v + h * kVImgHead + d * kVImgRow + 16 * oct);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint4 w4 = src[q];  // tokens 2q, 2q + 1 of the octet, words e = 0, 1
