@@ -11,6 +11,14 @@
 
 namespace oscar {
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+// Two fp32 -> two fp16, round to nearest even, packed a | b << 16 (one
+// v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){a, b}, half2_t));
+}
+
 // INT2 min-max quantizer over 32 fp16-valued numbers: delta = (max - min)/3,
 // zero = min, code = clamp(rint((x - zero)/delta), 0, 3) with ties to even,
 // delta == 0 -> code 0 ([SUM] 前置知识 on per-channel quantization and

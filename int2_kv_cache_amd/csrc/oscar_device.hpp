@@ -41,13 +41,6 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 __device__ __forceinline__ uint16_t f32_to_f16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-// Two fp32 -> two fp16, round to nearest even, packed a | b << 16 (one
-// v_cvt_pk_f16_f32).
-__device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){a, b}, half2_t));
-}
 // fp32 -> fp16 bits of a stored value (a Value row entry, a token norm):
 // clamped to the finite fp16 range first, so nothing stored is infinite; the
 // max returns its other operand for a NaN, which is therefore stored as
