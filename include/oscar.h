@@ -306,6 +306,31 @@ OSCAR_API oscar_status oscar_decode_attn(const oscar_cache_geom *geom, const osc
                                void *workspace, size_t ws_bytes, int32_t num_splits,
                                int32_t max_ctx, oscar_attn_variant variant, void *stream);
 
+/* One whole decode step in one launch: the same result as oscar_append_kv
+ * (k_new, v_new) followed by oscar_decode_attn (q) on the same stream -- the
+ * cache left byte for byte as the append leaves it, the same flags, and the
+ * same out and lse -- for the steps the pages describe (popular-science
+ * article, 三: the newest token joins the fp16 residual cache, a full window
+ * is quantized a block at a time; summary "OScaR：…", 方法步骤详情 ③: fused
+ * attention over the INT2 blocks and the window).  Inside the launch each
+ * sequence's attention covers the state the append leaves: the workgroup
+ * whose window chunk holds the new token rotates and scales it itself, a
+ * block that a full window flushes is quantized by the workgroup whose
+ * split holds it (and written to the pool before its copy), and the stores
+ * that overwrite slots other workgroups read (the new token's window rows
+ * and norm, {n, Q}) are made by the last of the sequence's workgroups to
+ * finish those reads (counted in append_sync[b]).
+ *   k_new, v_new, kv_dtype  as oscar_append_kv;
+ *   q, q_dtype, out, lse, workspace, ws_bytes, num_splits, max_ctx, variant
+ *            as oscar_decode_attn (max_ctx bounds n after the append).
+ *            VALU: the append and then attention, two launches.
+ * Errors: as oscar_append_kv and oscar_decode_attn. */
+OSCAR_API oscar_status oscar_decode_step(const oscar_cache_geom *geom, const oscar_cache *cache,
+                               const void *k_new, const void *v_new, oscar_dtype kv_dtype,
+                               const void *q, oscar_dtype q_dtype, float *out, float *lse,
+                               void *workspace, size_t ws_bytes, int32_t num_splits,
+                               int32_t max_ctx, oscar_attn_variant variant, void *stream);
+
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation:
  * oscar_decode_attn with its workspace taken from a library-owned device

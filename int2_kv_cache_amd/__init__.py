@@ -29,7 +29,8 @@ HEAD_DIM, BLOCK_TOKENS, RESIDUAL_TOKENS, V_GROUP, RECORD_BYTES = 128, 32, 128, 3
 API = ("oscar_cache_layout", "oscar_rotate_scale", "oscar_quant_pack", "oscar_append_kv",
        "oscar_prefill_quantize", "oscar_decode_workspace_bytes", "oscar_decode_attn",
        "oscar_dense_write_kv", "oscar_dense_workspace_bytes", "oscar_dense_decode_attn",
-       "oscar_absorb_value_rotation", "oscar_decode_attn_noalloc", "oscar_status_str")
+       "oscar_absorb_value_rotation", "oscar_decode_attn_noalloc", "oscar_decode_step",
+       "oscar_status_str")
 
 
 class OscarError(RuntimeError):
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.oscar_decode_workspace_bytes.argtypes = [P(Geom), i32, i32, P(ctypes.c_int32),
                                                    P(ctypes.c_size_t)]
         L.oscar_decode_attn.argtypes = [P(Geom), P(CacheBufs), vp, st, vp, vp, vp,
+                                        ctypes.c_size_t, i32, i32, st, vp]
+        L.oscar_decode_step.argtypes = [P(Geom), P(CacheBufs), vp, vp, st, vp, st, vp, vp, vp,
                                         ctypes.c_size_t, i32, i32, st, vp]
         L.oscar_dense_write_kv.argtypes = [P(Geom), vp, vp, vp, i32, i32, vp, vp, i32, vp, vp]
         L.oscar_dense_workspace_bytes.argtypes = [P(Geom), i32, i32, P(ctypes.c_int32),
@@ -236,6 +239,18 @@ def decode_attn(cache: DeviceCache, q, q_dtype: int, out, lse, workspace, max_ct
         _ptr(lse), _ptr(workspace), nbytes, num_splits, max_ctx, variant, _stream(stream)))
 
 
+def decode_step(cache: DeviceCache, k_new, v_new, kv_dtype: int, q, q_dtype: int, out, lse,
+                workspace, max_ctx: int, num_splits: int = 0, variant: int = ATTN_AUTO,
+                stream=None):
+    """oscar_decode_step: append_kv(k_new, v_new) then decode_attn(q), in one
+    launch (two with ATTN_VALU)."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("oscar_decode_step", lib().oscar_decode_step(
+        ctypes.byref(cache.geom), ctypes.byref(cache.bufs), _ptr(k_new), _ptr(v_new), kv_dtype,
+        _ptr(q), q_dtype, _ptr(out), _ptr(lse), _ptr(workspace), nbytes, num_splits, max_ctx,
+        variant, _stream(stream)))
+
+
 STATIC_WORKSPACE_BYTES = 8 << 20   # OSCAR_STATIC_WORKSPACE_BYTES
 
 
@@ -282,6 +297,16 @@ def prepare_decode_attn(cache: DeviceCache, q, q_dtype: int, out, lse, workspace
         ctypes.byref(cache.geom), ctypes.byref(cache.bufs), _ptr(q), q_dtype, _ptr(out),
         _ptr(lse), _ptr(workspace), ctypes.c_size_t(nbytes), num_splits, max_ctx, variant,
         _stream(stream)))
+
+
+def prepare_decode_step(cache: DeviceCache, k_new, v_new, kv_dtype: int, q, q_dtype: int, out,
+                        lse, workspace, max_ctx: int, num_splits: int = 0,
+                        variant: int = ATTN_AUTO, stream=None) -> PreparedCall:
+    nbytes = workspace.numel() * workspace.element_size()
+    return PreparedCall("oscar_decode_step", (
+        ctypes.byref(cache.geom), ctypes.byref(cache.bufs), _ptr(k_new), _ptr(v_new), kv_dtype,
+        _ptr(q), q_dtype, _ptr(out), _ptr(lse), _ptr(workspace), ctypes.c_size_t(nbytes),
+        num_splits, max_ctx, variant, _stream(stream)))
 
 
 # ---------------------------------------------------------------- bf16 baseline

@@ -16,6 +16,7 @@
 
 #include "oscar_device.hpp"
 #include "oscar_host.hpp"
+#include "oscar_quant.hpp"
 
 namespace oscar {
 
@@ -47,7 +48,31 @@ struct AttnArgs {
   // rotated by position n - 1, the step's own token, before its FHT
   const float* rope;
   int rope_max_pos;
+  // Decode step (STEP kernels): each sequence's new token, appended by the
+  // same launch, and the cache buffers the append writes (the same buffers
+  // as above)
+  const uint16_t* k_new;  // [B][Hkv][128], bf16 or fp16 (kv_bf16)
+  const uint16_t* v_new;
+  int kv_bf16;
+  int flush_blocks;       // blocks quantized when the window is full: 1 or 4
+  int hw_rsq;             // 1: Key scaling factor from the hardware rsqrt
+  uint8_t* pool_w;
+  uint16_t* pool_norm_w;
+  uint16_t* res_k_w;
+  uint16_t* res_v_w;
+  uint16_t* res_norm_w;
+  int32_t* seq_state_w;
+  int32_t* append_sync;   // [B] arrival counters: zero before and after a launch
 };
+
+// A stored fp16 value from fp32, as the append stores Values and norms:
+// clamped to +-65504 first, a NaN stored as -65504 (the clamp's result in
+// IEEE max/min order).  Integer tests, so that the result does not depend on
+// how this file's floating-point options treat NaN.
+__device__ __forceinline__ uint16_t f16_sat_bits(float f) {
+  if ((__float_as_uint(f) & 0x7fffffffu) > 0x7f800000u) return 0xFBFFu;
+  return f32_to_f16(__builtin_amdgcn_fmed3f(f, -65504.0f, 65504.0f));
+}
 
 // The (cos, sin) of the decode query's position n - 1 for lane L (channel
 // pair L, L + 64), or (1, 0) when no RoPE applies; a position past the
@@ -553,7 +578,7 @@ __device__ __forceinline__ float load_dev(const float* p) {
 // agent-scope atomic stores and loads (coherent at the device level by
 // themselves), each wave waiting for its stores to complete before the
 // workgroup counts itself in.
-template <int GRP, int NW, int PUB>
+template <int GRP, int NW, int PUB, int STEP>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void attn_mfma_kernel(AttnArgs A) {
   static_assert(GRP == 1 || GRP == 2 || GRP == 4 || GRP == 8, "group size");
@@ -584,6 +609,12 @@ void attn_mfma_kernel(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) uint8_t stage0[NW][kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[NW][kStage];
   __shared__ int lds_last;
+  // decode step: the new token's per-head sums of squares, its rotated Key
+  // row and stored Value row for this head; whether this workgroup appends
+  __shared__ float step_part[STEP ? 16 : 1];
+  __shared__ float step_y[STEP ? kD : 1];
+  __shared__ uint16_t step_v[STEP ? kD : 2];
+  __shared__ int lds_app;
 
   const int wid = static_cast<int>(blockIdx.x);
   const int pair = wid / A.splits, s = wid - pair * A.splits;
@@ -603,9 +634,45 @@ void attn_mfma_kernel(AttnArgs A) {
   // priority: the main loop lowers it as a wave progresses
   __builtin_amdgcn_s_setprio(3);
   int n = A.seq_state[2 * b], Q = A.seq_state[2 * b + 1];
-  if (!(Q >= 0 && (Q & 31) == 0 && n >= Q && n - Q <= kR && Q / kG <= A.max_blocks)) {
+  const bool state_good = Q >= 0 && (Q & 31) == 0 && n >= Q && n - Q <= kR && Q / kG <= A.max_blocks;
+  if (!state_good) {
     if (tid == 0 && s == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
     n = Q = 0;
+  }
+  // Decode step: the append's own checks, the same in every workgroup of the
+  // sequence.  When the append goes ahead, attention covers the state it
+  // leaves -- n + 1 tokens, with the block(s) a full window flushes quantized
+  // by this launch -- so the step equals an append followed by attention.
+  const int n_old = n, Q_old = Q;
+  bool app = false;
+  if constexpr (STEP != 0) {
+    if (state_good) {
+      app = true;
+      int32_t why = 0;
+      if (A.rope && n >= A.rope_max_pos) {
+        app = false;  // no (cos, sin) for position n
+        why = OSCAR_FLAG_POSITION;
+      } else if (n - Q == kR) {
+        const int j0 = Q / kG;
+        if (j0 + A.flush_blocks > A.max_blocks) {
+          app = false;
+          why = OSCAR_FLAG_CAPACITY;
+        } else {
+          for (int i = 0; i < A.flush_blocks; ++i) {
+            const int pi = A.block_table[static_cast<size_t>(b) * A.max_blocks + j0 + i];
+            if (pi < 0 || pi >= A.nphys) {
+              app = false;
+              why = OSCAR_FLAG_BADSTATE;
+            }
+          }
+        }
+      }
+      if (!app && tid == 0 && s == 0 && h == 0) atomicOr(A.error_flag, why);
+    }
+    if (app) {
+      if (n - Q == kR) Q += kG * A.flush_blocks;
+      n += 1;
+    }
   }
   // Splits partition the units by weight: an INT2 block weighs 1, a window
   // chunk (16 KB of fp16 data against a 3 KB record) kRingWeight.
@@ -628,6 +695,14 @@ void attn_mfma_kernel(AttnArgs A) {
   const int n_units = u1 > first ? (u1 - first + NW - 1) / NW : 0;
   const int cnt = nb > first ? min(n_units, (nb - first + NW - 1) / NW) : 0;
   const bool has_ring = n_units > cnt;
+  // Decode step: this split's share of the blocks the append flushes
+  // (units f0 .. f1 - 1, quantized here from the window before any record
+  // copy), and whether its window chunk holds the new token (unit_new).
+  const int f0 = app ? max(u0, Q_old / kG) : 0, f1 = app ? min(u1, nb) : 0;
+  const bool wg_fresh = STEP != 0 && f1 > f0;
+  const int unit_new = nb + (n_old - Q) / kG;
+  const bool wg_new = STEP != 0 && app && unit_new >= u0 && unit_new < u1;
+  const bool wave_new = wg_new && has_ring && first + NW * cnt == unit_new;
 
   // Physical block ids of the wave's INT2 blocks, 64 at a time: lane j holds
   // block k0 + j; a block is then taken out with readlane (no scalar memory
@@ -686,7 +761,7 @@ void attn_mfma_kernel(AttnArgs A) {
   const int ring_valid = has_ring ? min(32, n - ring_tb) : 0;
   u32x4 rk[2][4], rv[8];
   float rnt[TPL];
-  if (has_ring) {
+  auto load_ring = [&]() {
     const int slot0 = ring_tb % kR;  // a multiple of 32: the chunk is 32 consecutive slots
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
@@ -700,7 +775,10 @@ void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
     for (int j = 0; j < TPL; ++j)
       rnt[j] = f16_to_f32(window_norms(A, b, h)[slot0 + ((sm_t0 + j) & 31)]);
-  }
+  };
+  // (a workgroup that quantizes a flushed block first loads its window
+  // chunks after that, so that their registers are free meanwhile)
+  if (has_ring && !wg_fresh) load_ring();
 
   // Block j of the wave goes through stage j % 2.  Its DMA is issued two
   // blocks ahead (unconditionally: past the end it re-reads the last block)
@@ -712,8 +790,84 @@ void attn_mfma_kernel(AttnArgs A) {
     const int p = __builtin_amdgcn_readlane(idv, j & 63);
     dma_unit(unit_rec(p), unit_nrm(p), st, L);
   };
-  if (cnt > 0) dma_block(0, st0);
-  if (cnt > 1) dma_block(1, st1);
+  if (!wg_fresh) {
+    if (cnt > 0) dma_block(0, st0);
+    if (cnt > 1) dma_block(1, st1);
+  }
+  if constexpr (STEP != 0) {
+    if (wg_fresh) {
+      // The flushed block(s) of this split: head h's 32 window tokens of
+      // each, quantized to the bytes the append writes (the streaming form
+      // of its range and code functions), written to the pool, and then
+      // copied like any record.  The
+      // stages are free until the copies start: Key rows [32][128] and the
+      // Key image in stage0, Value columns [128][32] and the Value image in
+      // stage1.
+      uint16_t* fk = reinterpret_cast<uint16_t*>(&stage0[0][0]);
+      uint32_t* fimg_k = reinterpret_cast<uint32_t*>(&stage0[0][0] + 32 * kD * 2);
+      uint16_t* fv = reinterpret_cast<uint16_t*>(&stage1[0][0]);
+      uint32_t* fimg_v = reinterpret_cast<uint32_t*>(&stage1[0][0] + 32 * kD * 2);
+      static_assert(32 * kD * 2 + 2 * kD * 4 <= 4 * kStage && 32 * kD * 2 + 4 * kVImgRow * 4 <= 4 * kStage,
+                    "the flush staging fits the stages");
+      for (int fu = f0; fu < f1; ++fu) {
+        const int s0 = (Q_old + kG * (fu - Q_old / kG)) % kR;
+        const int p = A.block_table[static_cast<size_t>(b) * A.max_blocks + fu];
+        uint8_t* rec = A.pool_w + (static_cast<size_t>(p) * A.hkv + h) * kRec;
+        for (int i = tid; i < 32 * kD / 8; i += NT) {
+          reinterpret_cast<uint4*>(fk)[i] =
+              reinterpret_cast<const uint4*>(A.res_k + (bh * kR + s0) * kD)[i];
+          reinterpret_cast<uint4*>(fv)[i] = reinterpret_cast<const uint4*>(
+              A.res_v + (bh * kD + (i >> 2)) * kR + s0)[i & 3];
+        }
+        // TOKEN scope: every head writes the same 32 norms
+        if (tid < 32) {
+          const uint16_t nv = window_norms(A, b, h)[s0 + tid];
+          A.pool_norm_w[A.head_norm ? (static_cast<size_t>(p) * A.hkv + h) * 32 + tid
+                                    : static_cast<size_t>(p) * 32 + tid] = nv;
+        }
+        __syncthreads();
+        uint32_t cw[2];
+        if (tid < kD) {
+          // Key channel tid over the block's 32 window tokens
+          auto xk = [&](int t) { return f16_to_f32(fk[t * kD + tid]); };
+          const Range r = range32_stream(xk);
+          reinterpret_cast<uint16_t*>(rec + kRecKDelta)[tid] = f32_to_f16(r.delta);
+          reinterpret_cast<uint16_t*>(rec + kRecKZero)[tid] = static_cast<uint16_t>(r.zm);
+          codes32_stream(xk, r, cw);
+          fimg_k[tid] = cw[0];
+          fimg_k[kD + tid] = cw[1];
+        } else if (tid < 2 * kD) {
+          // Value (token t, group g) over 32 channels
+          const int u = tid - kD, t = u & 31, g = u >> 5;
+          auto xv = [&](int i) { return f16_to_f32(fv[(32 * g + i) * 32 + t]); };
+          const Range r = range32_stream(xv);
+          reinterpret_cast<uint32_t*>(rec + kRecVParam)[32 * g + t] =
+              static_cast<uint32_t>(f32_to_f16(r.delta)) | (r.zm << 16);
+          codes32_stream(xv, r, cw);
+          *reinterpret_cast<uint2*>(fimg_v + g * kVImgRow + 2 * t) = uint2{cw[0], cw[1]};
+        }
+        __syncthreads();
+        for (int i = tid; i < 512; i += NT) {
+          if (i < 256) {
+            const int t = i >> 3, j = i & 7;  // Key word j of token t
+            *reinterpret_cast<uint32_t*>(rec + kRecKCodes + 32 * t + 4 * j) = key_word(fimg_k, t, j);
+          } else {
+            const int w = i - 256, oct = (w >> 6) & 3, m = (w >> 2) & 15, d = w & 3;
+            *reinterpret_cast<uint32_t*>(rec + kRecVCodes + 16 * (16 * oct + m) + 4 * d) =
+                value_word(fimg_v, oct, m, d);
+          }
+        }
+        __syncthreads();  // the next block reuses the staging
+      }
+      // the records are in memory (this workgroup's stores have completed)
+      // before its copies of them start
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      __syncthreads();
+      if (has_ring) load_ring();
+      if (cnt > 0) dma_block(0, st0);
+      if (cnt > 1) dma_block(1, st1);
+    }
+  }
 
   const float2 qcs = query_rope(A, n, L);
 #pragma unroll
@@ -730,7 +884,96 @@ void attn_mfma_kernel(AttnArgs A) {
       qs[i * kD + L + 64] = qy[j] * kScale;
     }
   }
+  // Decode step: the new token's rotated Key rows (every head: the TOKEN
+  // norm spans them) and this head's stored Value row, for the wave whose
+  // window chunk holds it -- the append's arithmetic, in the append's order.
+  auto new_token_row = [&](int hh, float& ya, float& yb) {
+    const size_t base = (static_cast<size_t>(b) * A.hkv + hh) * kD;
+    ya = in_to_f32(A.k_new[base + L], A.kv_bf16);
+    yb = in_to_f32(A.k_new[base + L + 64], A.kv_bf16);
+    if (A.rope) {  // the new token sits at position n_old
+      const float2 cs = reinterpret_cast<const float2*>(A.rope)[static_cast<size_t>(n_old) * 64 + L];
+      rope_pair(ya, yb, cs.x, cs.y);
+    }
+    fht128_wave(ya, yb);
+  };
+  int prev_app = -1;
+  if constexpr (STEP != 0) {
+    if (wg_new) {
+      for (int hh = wave; hh < A.hkv; hh += NW) {
+        float ya, yb;
+        new_token_row(hh, ya, yb);
+        const float ss = wave_tree_sumsq(ya, yb);
+        if (L == 0) step_part[hh] = ss;
+        if (hh == h) {
+          step_y[L] = ya;
+          step_y[L + 64] = yb;
+        }
+      }
+      if (tid < kD)
+        step_v[tid] = f16_sat_bits(in_to_f32(A.v_new[bh * kD + tid], A.kv_bf16));
+    }
+    // A wave's window reads have landed before its workgroup counts itself
+    // in (vector loads complete in order; at most the four newest copies of
+    // each of its first two records may still run).
+    if (app && has_ring) {
+      if (cnt >= 2)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (cnt == 1)
+        vmcnt_le4();
+      else
+        vmcnt_0();
+    }
+  }
   __syncthreads();
+  // Decode step: every workgroup of the sequence counts itself in once it
+  // has read {n, Q} and its window slots; the last to do so writes the new
+  // token and state (at its end), when no slot it overwrites is still read.
+  if constexpr (STEP != 0) {
+    if (app && tid == 0)
+      prev_app = __hip_atomic_fetch_add(A.append_sync + b, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    if (wave_new) {
+      // the token's Key row and norm as the append stores them, put in place
+      // of what the window loads read at its slot
+      const float ss = A.head_norm ? step_part[h] : tree16(step_part, A.hkv);
+      float nrm, r;
+      scale_from_ss(ss, nrm, r, A.hw_rsq != 0);
+      const int tau = n_old - ring_tb;  // its place in the chunk
+      if (col == (tau & 15)) {
+        // lane (col, g4): token 16 tau' + col, channels 32 g4 + 8 kk + 0..7
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          u32x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = 32 * g4 + 8 * kk + 2 * i;
+            w[i] = static_cast<uint32_t>(f32_to_f16(mul_rn(step_y[c], r))) |
+                   (static_cast<uint32_t>(f32_to_f16(mul_rn(step_y[c + 1], r))) << 16);
+          }
+          if (tau < 16)
+            rk[0][kk] = w;
+          else
+            rk[1][kk] = w;
+        }
+      }
+      if (g4 == (tau >> 3)) {
+        // lane (col, g4): channel 16 ct + col, tokens 8 g4 .. 8 g4 + 7
+        const int e = tau & 7;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          const uint32_t hv = step_v[16 * ct + col];
+#pragma unroll
+          for (int wi = 0; wi < 4; ++wi)
+            if ((e >> 1) == wi)
+              rv[ct][wi] = (e & 1) ? ((rv[ct][wi] & 0xFFFFu) | (hv << 16)) : ((rv[ct][wi] & 0xFFFF0000u) | hv);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TPL; ++j)
+        if (sm_t0 + j == tau) rnt[j] = f16_to_f32(f16_sat_bits(nrm));
+    }
+  }
   float m_run = -INFINITY, l_part = 0.0f;
   float zacc[NR];
 #pragma unroll
@@ -1021,6 +1264,52 @@ void attn_mfma_kernel(AttnArgs A) {
   auto wo_at = [&](int w, int hh) {
     return reinterpret_cast<float*>((hh < 4 ? stage0[w] : stage1[w]) + 512 * (hh & 3));
   };
+  // Decode step, in the workgroup that counted itself in last: the new
+  // token's window rows and norm for every head, then the new state -- the
+  // append's stores, made once every read of what they overwrite is done.
+  auto append_tail = [&]() {
+    constexpr int HPW = (16 + NW - 1) / NW;  // heads per wave (Hkv <= 16)
+    const int slot = n_old % kR;
+    float ya[HPW], yb[HPW];
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const int hh = wave + NW * j;
+      ya[j] = yb[j] = 0.0f;
+      if (hh < A.hkv) {
+        new_token_row(hh, ya[j], yb[j]);
+        const float ss = wave_tree_sumsq(ya[j], yb[j]);
+        if (L == 0) step_part[hh] = ss;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const int hh = wave + NW * j;
+      if (hh < A.hkv) {
+        float nrm, r;
+        scale_from_ss(A.head_norm ? step_part[hh] : tree16(step_part, A.hkv), nrm, r, A.hw_rsq != 0);
+        uint16_t* rkw = A.res_k_w + ((static_cast<size_t>(b) * A.hkv + hh) * kR + slot) * kD;
+        rkw[L] = f32_to_f16(mul_rn(ya[j], r));
+        rkw[L + 64] = f32_to_f16(mul_rn(yb[j], r));
+        if (L == 0 && (A.head_norm || hh == 0))
+          A.res_norm_w[A.head_norm ? (static_cast<size_t>(b) * A.hkv + hh) * kR + slot
+                                   : static_cast<size_t>(b) * kR + slot] = f16_sat_bits(nrm);
+      }
+    }
+    // Value rows [B][Hkv][128][slots]; v_new [B][Hkv][128]
+    for (int i = tid; i < A.hkv * kD; i += NT) {
+      const size_t row = static_cast<size_t>(b) * A.hkv * kD + i;
+      A.res_v_w[row * kR + slot] = f16_sat_bits(in_to_f32(A.v_new[row], A.kv_bf16));
+    }
+    if (tid == 0) {
+      A.seq_state_w[2 * b] = n_old + 1;
+      A.seq_state_w[2 * b + 1] = Q;
+      __hip_atomic_store(A.append_sync + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  if constexpr (STEP != 0) {
+    if (tid == 0) lds_app = app && prev_app == A.hkv * A.splits - 1;
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (sm_on && (L % LPH) == 0) {
@@ -1079,6 +1368,8 @@ void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       if (tid + NT * i < GRP * kD) finish(tid + NT * i, Mi[i], Li[i], Oi[i]);
+    if constexpr (STEP != 0)
+      if (lds_app) append_tail();
     return;
   }
 
@@ -1103,7 +1394,11 @@ void attn_mfma_kernel(AttnArgs A) {
       if (c == 0) A.ws_ml[part] = make_float2(Mi[i], Li[i]);
     }
   }
-  if (!A.merge_in_kernel) return;
+  if (!A.merge_in_kernel) {
+    if constexpr (STEP != 0)
+      if (lds_app) append_tail();
+    return;
+  }
   // every wave's stores have completed (reached the L2, or with PUB 1 the
   // device's coherence point) before the workgroup counts itself in
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
@@ -1119,7 +1414,11 @@ void attn_mfma_kernel(AttnArgs A) {
   __syncthreads();
   // (PUB 0: the counter's acquire, on this workgroup's CU, precedes the
   // barrier that every thread passed before reading the partials)
-  if (!lds_last) return;
+  if (!lds_last) {
+    if constexpr (STEP != 0)
+      if (lds_app) append_tail();
+    return;
+  }
   if (S <= 32) {
     // Lane j < S of each wave reads split j's (m, l) of the wave's head and
     // every lane reads its channel of all S partial outputs, all at once; the
@@ -1154,6 +1453,8 @@ void attn_mfma_kernel(AttnArgs A) {
       finish(idx, M, Lw, Ow);
     }
     if (tid == 0) __hip_atomic_store(A.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (STEP != 0)
+      if (lds_app) append_tail();
     return;
   }
   // more splits: a thread's partials are requested 16 at a time
@@ -1202,6 +1503,8 @@ void attn_mfma_kernel(AttnArgs A) {
     finish(idx, M, Lw, Ow);
   }
   if (tid == 0) __hip_atomic_store(A.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (STEP != 0)
+    if (lds_app) append_tail();
 }
 
 // ---------------------------------------------------------------- reduce
@@ -1353,15 +1656,15 @@ void launch_lse_reduce(const float2* ws_ml, const float* ws_o, int hq, int batch
                      out, lse);
 }
 
-template <int GRP>
+template <int GRP, int STEP>
 void launch_mfma(const AttnArgs& A, int nwg, int nw, hipStream_t st) {
   constexpr int P = OSCAR_ATTN_PUB;
   if (nw == 12)
-    hipLaunchKernelGGL((attn_mfma_kernel<GRP, 12, P>), dim3(nwg), dim3(768), 0, st, A);
+    hipLaunchKernelGGL((attn_mfma_kernel<GRP, 12, P, STEP>), dim3(nwg), dim3(768), 0, st, A);
   else if (nw == 6)
-    hipLaunchKernelGGL((attn_mfma_kernel<GRP, 6, P>), dim3(nwg), dim3(384), 0, st, A);
+    hipLaunchKernelGGL((attn_mfma_kernel<GRP, 6, P, STEP>), dim3(nwg), dim3(384), 0, st, A);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<GRP, 4, P>), dim3(nwg), dim3(256), 0, st, A);
+    hipLaunchKernelGGL((attn_mfma_kernel<GRP, 4, P, STEP>), dim3(nwg), dim3(256), 0, st, A);
 }
 
 }  // namespace oscar
@@ -1380,11 +1683,14 @@ extern "C" oscar_status oscar_decode_workspace_bytes(const oscar_cache_geom* geo
   return OSCAR_OK;
 }
 
-extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const oscar_cache* cache,
-                                          const void* q, oscar_dtype q_dtype, float* out,
-                                          float* lse, void* workspace, size_t ws_bytes,
-                                          int32_t num_splits, int32_t max_ctx,
-                                          oscar_attn_variant variant, void* stream) {
+// One decode call: attention alone (step == null) or, with the new tokens,
+// the fused decode step.
+static oscar_status decode_call(const oscar_cache_geom* geom, const oscar_cache* cache,
+                                const void* q, oscar_dtype q_dtype, float* out, float* lse,
+                                void* workspace, size_t ws_bytes, int32_t num_splits,
+                                int32_t max_ctx, oscar_attn_variant variant, void* stream,
+                                const void* k_new, const void* v_new, oscar_dtype kv_dtype) {
+  const bool step = k_new != nullptr;
   oscar_status st = check_cache(geom, cache);
   if (st != OSCAR_OK) return st;
   if (!q || !out || !workspace || max_ctx < 0 || num_splits < 0 || num_splits > 1024)
@@ -1393,13 +1699,20 @@ extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const os
   if (!aligned(workspace, 256) || !aligned(q, 4) || !aligned(out, 16)) return OSCAR_EINVAL;
   if (variant != OSCAR_ATTN_AUTO && variant != OSCAR_ATTN_VALU && variant != OSCAR_ATTN_MFMA)
     return OSCAR_EINVAL;
+  if (step && (!v_new || (kv_dtype != OSCAR_FP16 && kv_dtype != OSCAR_BF16))) return OSCAR_EINVAL;
   if (static_cast<long long>(geom->batch) * geom->num_kv_heads > kMaxPairs) return OSCAR_EINVAL;
   const AttnShape shape = attn_shape(geom, max_ctx, num_splits);
   const int S = shape.splits;
   if (ws_bytes < attn_workspace_bytes(geom, S)) return OSCAR_EWORKSPACE;
   st = check_device();
   if (st != OSCAR_OK) return st;
-
+  if (step && variant == OSCAR_ATTN_VALU) {
+    // the vector-ALU variant has no fused form: the append, then attention
+    st = oscar_append_kv(geom, cache, k_new, v_new, kv_dtype, stream);
+    if (st != OSCAR_OK) return st;
+    return decode_call(geom, cache, q, q_dtype, out, lse, workspace, ws_bytes, num_splits, max_ctx,
+                       variant, stream, nullptr, nullptr, kv_dtype);
+  }
   AttnArgs A;
   A.pool = static_cast<const uint8_t*>(cache->pool);
   A.pool_norm = static_cast<const uint16_t*>(cache->pool_norm);
@@ -1426,6 +1739,18 @@ extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const os
   A.lse = lse;
   A.rope = geom->rope_max_pos > 0 ? cache->rope : nullptr;
   A.rope_max_pos = geom->rope_max_pos;
+  A.k_new = static_cast<const uint16_t*>(k_new);
+  A.v_new = static_cast<const uint16_t*>(v_new);
+  A.kv_bf16 = kv_dtype == OSCAR_BF16 ? 1 : 0;
+  A.flush_blocks = geom->flush_tokens == 128 ? 4 : 1;
+  A.hw_rsq = geom->key_scale == OSCAR_SCALE_HW_RSQ ? 1 : 0;
+  A.pool_w = static_cast<uint8_t*>(cache->pool);
+  A.pool_norm_w = static_cast<uint16_t*>(cache->pool_norm);
+  A.res_k_w = static_cast<uint16_t*>(cache->res_k);
+  A.res_v_w = static_cast<uint16_t*>(cache->res_v);
+  A.res_norm_w = static_cast<uint16_t*>(cache->res_norm);
+  A.seq_state_w = cache->seq_state;
+  A.append_sync = cache->append_sync;
   hipStream_t hs = as_stream(stream);
   const int grp = geom->num_q_heads / geom->num_kv_heads;
   if (variant == OSCAR_ATTN_VALU) {
@@ -1447,14 +1772,44 @@ extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const os
   // spreads the merging over the chip
   A.merge_in_kernel = shape.merge_in_kernel;
   const int nwg = geom->batch * geom->num_kv_heads * S;
-  switch (grp) {
-    case 1: launch_mfma<1>(A, nwg, shape.nw, hs); break;
-    case 2: launch_mfma<2>(A, nwg, shape.nw, hs); break;
-    case 4: launch_mfma<4>(A, nwg, shape.nw, hs); break;
-    default: launch_mfma<8>(A, nwg, shape.nw, hs); break;
+  if (step) {
+    switch (grp) {
+      case 1: launch_mfma<1, 1>(A, nwg, shape.nw, hs); break;
+      case 2: launch_mfma<2, 1>(A, nwg, shape.nw, hs); break;
+      case 4: launch_mfma<4, 1>(A, nwg, shape.nw, hs); break;
+      default: launch_mfma<8, 1>(A, nwg, shape.nw, hs); break;
+    }
+  } else {
+    switch (grp) {
+      case 1: launch_mfma<1, 0>(A, nwg, shape.nw, hs); break;
+      case 2: launch_mfma<2, 0>(A, nwg, shape.nw, hs); break;
+      case 4: launch_mfma<4, 0>(A, nwg, shape.nw, hs); break;
+      default: launch_mfma<8, 0>(A, nwg, shape.nw, hs); break;
+    }
   }
   st = launch_status();
   if (st != OSCAR_OK || A.merge_in_kernel || S == 1) return st;
   launch_lse_reduce(A.ws_ml, A.ws_o, geom->num_q_heads, geom->batch, S, out, lse, hs);
   return launch_status();
+}
+
+extern "C" oscar_status oscar_decode_attn(const oscar_cache_geom* geom, const oscar_cache* cache,
+                                          const void* q, oscar_dtype q_dtype, float* out,
+                                          float* lse, void* workspace, size_t ws_bytes,
+                                          int32_t num_splits, int32_t max_ctx,
+                                          oscar_attn_variant variant, void* stream) {
+  return decode_call(geom, cache, q, q_dtype, out, lse, workspace, ws_bytes, num_splits, max_ctx,
+                     variant, stream, nullptr, nullptr, OSCAR_FP16);
+}
+
+extern "C" oscar_status oscar_decode_step(const oscar_cache_geom* geom, const oscar_cache* cache,
+                                          const void* k_new, const void* v_new,
+                                          oscar_dtype kv_dtype, const void* q,
+                                          oscar_dtype q_dtype, float* out, float* lse,
+                                          void* workspace, size_t ws_bytes, int32_t num_splits,
+                                          int32_t max_ctx, oscar_attn_variant variant,
+                                          void* stream) {
+  if (!k_new) return OSCAR_EINVAL;
+  return decode_call(geom, cache, q, q_dtype, out, lse, workspace, ws_bytes, num_splits, max_ctx,
+                     variant, stream, k_new, v_new, kv_dtype);
 }

@@ -21,7 +21,8 @@ struct Range {
 };
 // From the extremes (fp16 values as fp32): both canonicalised to +0 if
 // zero, delta, 1/delta and the fast-quotient constants.  `wide` widens the
-// near margin for inputs that are not yet the quantized values (below).
+// near margin for inputs that are not yet the quantized values (the
+// prefill's Value ranges, taken before the rounding to fp16).
 __device__ __forceinline__ Range range_of(float mn, float mx, float wide) {
 #pragma clang fp contract(off)
   mn = mn + 0.0f;
@@ -103,6 +104,44 @@ __device__ __forceinline__ bool codes32_of(XV xv, const Range& r, uint32_t w[2])
 template <bool ROW = false>
 __device__ __forceinline__ bool codes32(const float* x, const Range& r, uint32_t w[2]) {
   return codes32_of<ROW>([x](int i) { return x[i]; }, r, w);
+}
+
+// range32 and codes32 for values read one at a time (xv(i) may load from
+// LDS each time): no value array and no per-value masks, a near value is
+// corrected on the spot.  The same extremes in the same order, the same
+// quotients and the same exact sums of c 4^k, hence the same bits; for rare
+// paths inside kernels whose registers are spoken for.
+template <class XV>
+__device__ __forceinline__ Range range32_stream(XV xv) {
+  float mn = xv(0), mx = mn;
+#pragma unroll 1
+  for (int i = 1; i < 32; ++i) {
+    const float x = xv(i);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+  return range_of(mn, mx, 0.0f);
+}
+template <class XV>
+__device__ __forceinline__ void codes32_stream(XV xv, const Range& r, uint32_t w[2]) {
+#pragma clang fp contract(off)
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll 1
+    for (int i = 8 * k; i < 8 * k + 8; ++i) {
+      const float x = xv(i);
+      const float q1 = __builtin_fmaf(x, r.rdelta, r.c0);
+      float c = rintf(q1);
+      if (fabsf(q1 - c) >= r.near) {
+        const float q = rintf(__fdiv_rn(x - r.zero, r.delta));
+        c = r.delta > 0.0f ? fminf(fmaxf(q, 0.0f), 3.0f) : 0.0f;
+      }
+      acc[k] = __builtin_fmaf(c, static_cast<float>(1u << (2 * (i & 7))), acc[k]);
+    }
+  }
+  w[0] = static_cast<uint32_t>(acc[0]) | (static_cast<uint32_t>(acc[1]) << 16);
+  w[1] = static_cast<uint32_t>(acc[2]) | (static_cast<uint32_t>(acc[3]) << 16);
 }
 
 // Value image: per (head, group) a row of 32 tokens x 2 words (channels

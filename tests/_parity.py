@@ -69,6 +69,30 @@ def shuffled_table(batch: int, max_blocks: int, seed: int = 99) -> np.ndarray:
     return rng.permutation(batch * max_blocks).astype(np.int32).reshape(batch, max_blocks)
 
 
+def compare_cache(g: "ok.DeviceCache", o: "oracle.OracleCache", table: np.ndarray):
+    """Bit-exact comparison of a GPU cache's valid region (state, flags,
+    the records and norms of its quantized blocks, its window slots) with the
+    oracle's."""
+    torch.cuda.synchronize()
+    st = g.seq_state.cpu().numpy()
+    assert np.array_equal(st, o.seq_state), (st, o.seq_state)
+    assert int(g.error_flag.cpu()[0]) == int(o.error_flag[0])
+    pool = g.pool.cpu().numpy()
+    pnorm = host_u16(g.pool_norm)
+    rk, rv, rn = host_u16(g.res_k), host_u16(g.res_v), host_u16(g.res_norm)
+    for b in range(g.geom.batch):
+        n, Q = o.n(b), o.q(b)
+        phys = table[b, :Q // 32]
+        for j, p in enumerate(phys):
+            assert_same_bits(pool[p], o.pool[p], "seq %d block %d record" % (b, j))
+            assert_same_bits(pnorm[p], o.pool_norm[p], "seq %d block %d norms" % (b, j))
+        slots = np.array([t % 128 for t in range(Q, n)], dtype=np.int64)
+        if len(slots):
+            assert_same_bits(rk[b][:, slots, :], o.res_k[b][:, slots, :], "res_k seq %d" % b)
+            assert_same_bits(rv[b][:, :, slots], o.res_v[b][:, :, slots], "res_v seq %d" % b)
+            assert_same_bits(rn[b][..., slots], o.res_norm[b][..., slots], "res_norm seq %d" % b)
+
+
 class Pair:
     """The same cache on the GPU and in the oracle."""
 
@@ -86,6 +110,7 @@ class Pair:
                                  rope_max_pos=0 if rope_table is None else len(rope_table))
         self.gpu = ok.DeviceCache(self.geom, block_table=torch.from_numpy(self.table),
                                   rope_table=rope_table)
+        self.rope_table = rope_table
         self.orc = oracle.OracleCache(cfg.batch, cfg.hq, cfg.hkv, self.max_blocks, nphys,
                                       block_table=self.table, norm_scope=norm_scope,
                                       flush_tokens=flush_tokens, rope_table=rope_table)
@@ -104,28 +129,10 @@ class Pair:
         self.orc.append(kn, vn, self.dtype)
         ok.append_kv(self.gpu, dev_u16(kn), dev_u16(vn), self.dtype)
 
-    def compare_state(self):
-        """Bit-exact comparison of the valid cache region."""
-        torch.cuda.synchronize()
-        g = self.gpu
-        st = g.seq_state.cpu().numpy()
-        assert np.array_equal(st, self.orc.seq_state), (st, self.orc.seq_state)
-        assert int(g.error_flag.cpu()[0]) == int(self.orc.error_flag[0])
-        pool = g.pool.cpu().numpy()
-        pnorm = host_u16(g.pool_norm)
-        rk, rv, rn = host_u16(g.res_k), host_u16(g.res_v), host_u16(g.res_norm)
-        o = self.orc
-        for b in range(self.geom.batch):
-            n, Q = o.n(b), o.q(b)
-            phys = self.table[b, :Q // 32]
-            for j, p in enumerate(phys):
-                assert_same_bits(pool[p], o.pool[p], "seq %d block %d record" % (b, j))
-                assert_same_bits(pnorm[p], o.pool_norm[p], "seq %d block %d norms" % (b, j))
-            slots = np.array([t % 128 for t in range(Q, n)], dtype=np.int64)
-            if len(slots):
-                assert_same_bits(rk[b][:, slots, :], o.res_k[b][:, slots, :], "res_k seq %d" % b)
-                assert_same_bits(rv[b][:, :, slots], o.res_v[b][:, :, slots], "res_v seq %d" % b)
-                assert_same_bits(rn[b][..., slots], o.res_norm[b][..., slots], "res_norm seq %d" % b)
+    def compare_state(self, gpu=None):
+        """Bit-exact comparison of the valid cache region of `gpu` (default:
+        this pair's own GPU cache) with the oracle's."""
+        compare_cache(self.gpu if gpu is None else gpu, self.orc, self.table)
 
     def attend(self, q: np.ndarray, variant=ok.ATTN_AUTO, splits=0, max_ctx=None,
                q_dtype=None, ws=None):
