@@ -53,7 +53,7 @@ WORKLOADS = {
 BATCH48_PROFILE = "decode_attn_qwen3-8b-batch48.md"
 # the decode-attention kernel and the headers it compiles from
 ATTN_SRC = [os.path.join(ROOT, "int2_kv_cache_amd", "csrc", f)
-            for f in ("oscar_attn.hip", "oscar_device.hpp", "oscar_host.hpp")]
+            for f in ("oscar_attn.hip", "oscar_device.hpp", "oscar_host.hpp", "oscar_quant.hpp")]
 
 
 def attn_src_hash() -> str:
@@ -102,6 +102,23 @@ def quantized(n: int, flush128: bool = False) -> int:
     return 32 * ((max(0, n - 128) + 31) // 32)
 
 
+def append_bytes(batch: int, hkv: int, head_norm: bool) -> int:
+    """Algorithmic bytes of one append per sequence: the new token's Keys and
+    Values in (bf16), its window rows out (fp16 Key row and Value column
+    entries), its norm(s) and the state."""
+    return batch * (hkv * 128 * 2 * 2 + hkv * 128 * 2 * 2 + (hkv if head_norm else 1) * 2 + 8)
+
+
+def kernel_desc(args) -> str:
+    if args.variant == 1:
+        return ("decode_attn (VALU attention + LSE reduce)" if args.unfused else
+                "append_kv + decode_attn (VALU attention + LSE reduce)")
+    if args.unfused:
+        return "decode_attn (one launch: split-K attention and the cross-split merge)"
+    return ("decode_step (one launch: the append, split-K attention and the cross-split "
+            "merge)")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +149,9 @@ def parse():
     ap.add_argument("--q-standalone", action="store_true",
                     help="rotate the query with its own oscar_rotate_scale launch and pass "
                          "q' as fp32, instead of the rotation inside decode attention")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run each layer's step as two launches (oscar_append_kv, then "
+                         "oscar_decode_attn) instead of one oscar_decode_step")
     ap.add_argument("--batch48", action="store_true",
                     help="only the batched workload (48 ragged sequences of 8K..32K tokens, "
                          "36 resident layer caches), on a JSON line of its own")
@@ -436,27 +456,46 @@ def decode_workload(ok, torch, synth, args, wname: str, steps: int, warmup: int,
     # the timed steps' calls, marshalled once (a call through the binding's
     # convenience wrappers costs several microseconds of host time, which at
     # short contexts is more than the GPU spends on a layer)
+    def fused_standalone(c, i):
+        ok.rotate_scale(q_d[i], cfg.dtype, ok.ROT_QUERY, q_out=qrot)
+        ok.decode_step(c, kn_d[i], vn_d[i], cfg.dtype, qrot, ok.FP32, out, lse, ws, max_ctx, S,
+                       args.variant)
+
     stream = torch.cuda.current_stream()
     calls = []
     for i in range(n_steps_total):
         row = []
         for c in caches:
-            app = ok.prepare_append_kv(c, kn_d[i], vn_d[i], cfg.dtype, stream=stream)
-            if args.q_standalone:
-                att = (lambda c=c, i=i: attend(c, i))
+            if args.unfused:
+                app = ok.prepare_append_kv(c, kn_d[i], vn_d[i], cfg.dtype, stream=stream)
+                if args.q_standalone:
+                    att = (lambda c=c, i=i: attend(c, i))
+                else:
+                    att = ok.prepare_decode_attn(c, q_d[i], cfg.dtype, out, lse, ws, max_ctx, S,
+                                                 args.variant, stream=stream)
             else:
-                att = ok.prepare_decode_attn(c, q_d[i], cfg.dtype, out, lse, ws, max_ctx, S,
-                                             args.variant, stream=stream)
+                # one launch: the append and attention (oscar_decode_step)
+                app = None
+                if args.q_standalone:
+                    att = (lambda c=c, i=i: fused_standalone(c, i))
+                else:
+                    att = ok.prepare_decode_step(c, kn_d[i], vn_d[i], cfg.dtype, q_d[i],
+                                                 cfg.dtype, out, lse, ws, max_ctx, S,
+                                                 args.variant, stream=stream)
             row.append((app, att))
         calls.append(row)
+    # attention alone on the last layer's cache, for the Infinity-Cache probe
+    hot_call = ok.prepare_decode_attn(caches[-1], q_d[-1], cfg.dtype, out, lse, ws, max_ctx, S,
+                                      args.variant, stream=stream)
 
     def step(i, ev=None, ev_layer=-1, ap=None, ap_layer=-1):
         for li, (app, att) in enumerate(calls[i]):
-            if li == ap_layer:
-                ap[0].record()
-            app()
-            if li == ap_layer:
-                ap[1].record()
+            if app is not None:
+                if li == ap_layer:
+                    ap[0].record()
+                app()
+                if li == ap_layer:
+                    ap[1].record()
             if li == ev_layer:
                 ev[0].record()
             att()
@@ -485,8 +524,8 @@ def decode_workload(ok, torch, synth, args, wname: str, steps: int, warmup: int,
     assert flag == 0, "cache error flag %d" % flag
     n1, Q1 = int(st[0]), int(st[1])
     attn_us = event_us(attn_ev)
-    append_us = event_us(app_ev)
-    hot_us = hot_attn_us(torch, calls[n_steps_total - 1][0][1])
+    append_us = event_us(app_ev) if args.unfused else None
+    hot_us = hot_attn_us(torch, hot_call)
 
     ms_per_step = total_ms / steps
     us_per_layer = ms_per_step * 1000.0 / L
@@ -494,9 +533,11 @@ def decode_workload(ok, torch, synth, args, wname: str, steps: int, warmup: int,
     n_mid = n0 + 1 + steps // 2
     bytes_attn = algorithmic_bytes(n_mid, quantized(n_mid, args.flush128), cfg.hq, cfg.hkv,
                                    args.head_norm)
+    if not args.unfused:
+        bytes_attn += append_bytes(1, cfg.hkv, args.head_norm)
     achieved = bytes_attn / (attn_us * 1e-6) / 1e9
     plain = not (args.head_norm or args.flush128 or args.q_standalone or args.hw_rsqrt
-                 or args.variant == 1 or args.splits)
+                 or args.variant == 1 or args.splits or args.unfused)
     res = {
         "workload": wdesc,
         "value": ctx_tokens / (total_ms / 1000.0),
@@ -510,15 +551,16 @@ def decode_workload(ok, torch, synth, args, wname: str, steps: int, warmup: int,
                    "query_rotation": "standalone" if args.q_standalone else "fused",
                    "key_scale": "hw_rsq" if args.hw_rsqrt else "ieee"},
         "us_per_layer_step": us_per_layer,
+        "step_launches": 2 if args.unfused or args.variant == 1 else 1,
         "attn_us": attn_us,
+        "attn_us_is": ("decode_attn between events" if args.unfused else
+                       "decode_step between events (append + attention, one launch)"),
         "attn_us_hot_mall_resident": hot_us,
         "append_us": append_us,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counter_traffic(profile) if plain else None,
-                     "kernel": "decode_attn (one launch: split-K attention and the "
-                               "cross-split merge)" if args.variant != 1 else
-                               "decode_attn (VALU attention + LSE reduce)",
+                     "kernel": kernel_desc(args),
                      "algorithmic_bytes": bytes_attn},
         "prefill_ms_per_layer": float(np.median(pre_ms)),
         "prefill_tokens_per_s": (n_ctx - 1) / (float(np.median(pre_ms)) / 1000.0),
@@ -599,18 +641,25 @@ def batch48_workload(ok, torch, synth, args, steps: int, warmup: int, bf16: bool
     setup_s = time.perf_counter() - t0
 
     stream = torch.cuda.current_stream()
-    calls = [[(ok.prepare_append_kv(c, kn_d[i], vn_d[i], cfg.dtype, stream=stream),
-               ok.prepare_decode_attn(c, q_d[i], cfg.dtype, out, lse, ws, max_ctx, S,
-                                      args.variant, stream=stream))
-              for c in caches] for i in range(n_total)]
+    if args.unfused:
+        calls = [[(ok.prepare_append_kv(c, kn_d[i], vn_d[i], cfg.dtype, stream=stream),
+                   ok.prepare_decode_attn(c, q_d[i], cfg.dtype, out, lse, ws, max_ctx, S,
+                                          args.variant, stream=stream))
+                  for c in caches] for i in range(n_total)]
+    else:
+        calls = [[(None, ok.prepare_decode_step(c, kn_d[i], vn_d[i], cfg.dtype, q_d[i],
+                                                 cfg.dtype, out, lse, ws, max_ctx, S,
+                                                 args.variant, stream=stream))
+                  for c in caches] for i in range(n_total)]
 
     def step(i, ev=None, ev_layer=-1, ap=None, ap_layer=-1):
         for li, (app, att) in enumerate(calls[i]):
-            if li == ap_layer:
-                ap[0].record()
-            app()
-            if li == ap_layer:
-                ap[1].record()
+            if app is not None:
+                if li == ap_layer:
+                    ap[0].record()
+                app()
+                if li == ap_layer:
+                    ap[1].record()
             if li == ev_layer:
                 ev[0].record()
             att()
@@ -632,10 +681,12 @@ def batch48_workload(ok, torch, synth, args, steps: int, warmup: int, bf16: bool
     torch.cuda.synchronize()
     total_ms = t_beg.elapsed_time(t_end)
     attn_us = event_us(attn_ev)
-    append_us = event_us(app_ev)
+    append_us = event_us(app_ev) if args.unfused else None
     assert int(caches[0].error_flag.item()) == 0
     n_mid = n0 + 1 + steps // 2
     bytes_attn = sum(algorithmic_bytes(int(n), quantized(int(n)), cfg.hq, cfg.hkv) for n in n_mid)
+    if not args.unfused:
+        bytes_attn += append_bytes(B, cfg.hkv, False)
     achieved = bytes_attn / (attn_us * 1e-6) / 1e9
     int2_bytes = sum(int(n) // 32 * (cfg.hkv * 3072 + 64) + 128 * (cfg.hkv * 512 + 2)
                      for n in n0) * L
@@ -651,14 +702,17 @@ def batch48_workload(ok, torch, synth, args, steps: int, warmup: int, bf16: bool
                    "layers": L, "splits": S},
         "ctx_tokens_per_s": float(np.sum(n0 + 1 + (steps - 1) / 2.0)) * L / (total_ms / 1000.0),
         "us_per_layer_step": total_ms * 1000.0 / (steps * L),
+        "step_launches": 2 if args.unfused or args.variant == 1 else 1,
         "attn_us_per_layer": attn_us,
+        "attn_us_is": ("decode_attn between events" if args.unfused else
+                       "decode_step between events (append + attention, one launch)"),
         "append_us_per_layer": append_us,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (counter_traffic(BATCH48_PROFILE)
-                                 if args.variant != 1 and not args.splits else None),
-                     "kernel": "decode_attn (one launch: split-K attention and the "
-                               "cross-split merge)",
+                                 if args.variant != 1 and not args.splits and not args.unfused
+                                 else None),
+                     "kernel": kernel_desc(args),
                      "algorithmic_bytes": bytes_attn},
         "cache_bytes_int2_36_layers": int2_bytes,
         "cache_bytes_bf16_36_layers": bf16_bytes,

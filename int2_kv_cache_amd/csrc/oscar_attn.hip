@@ -673,6 +673,10 @@ void attn_mfma_kernel(AttnArgs A) {
       if (n - Q == kR) Q += kG * A.flush_blocks;
       n += 1;
     }
+    // the same in every lane: kept in scalar registers, so that the unit
+    // bounds derived from them (and the main loop's branches) stay uniform
+    n = __builtin_amdgcn_readfirstlane(n);
+    Q = __builtin_amdgcn_readfirstlane(Q);
   }
   // Splits partition the units by weight: an INT2 block weighs 1, a window
   // chunk (16 KB of fp16 data against a 3 KB record) kRingWeight.
@@ -734,6 +738,21 @@ void attn_mfma_kernel(AttnArgs A) {
         qy[j] = in_to_f32(q16[base + L + 64], A.q_mode);
       }
     }
+  }
+  // Decode step: the new token's Keys for the heads this wave rotates (wave,
+  // wave + NW, ..), requested with the query when the split's window chunk
+  // holds the token
+  constexpr int HPW = (16 + NW - 1) / NW;  // heads per wave (Hkv <= 16)
+  uint16_t knx[HPW], kny[HPW];
+  auto load_new = [&](int hh, uint16_t& kx, uint16_t& ky) {
+    const size_t base = (static_cast<size_t>(b) * A.hkv + hh) * kD;
+    kx = A.k_new[base + L];
+    ky = A.k_new[base + L + 64];
+  };
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    knx[j] = kny[j] = 0;
+    if (STEP != 0 && wg_new && wave + NW * j < A.hkv) load_new(wave + NW * j, knx[j], kny[j]);
   }
   int idv = cnt > 0 ? load_ids(0) : 0;
 
@@ -887,52 +906,38 @@ void attn_mfma_kernel(AttnArgs A) {
   // Decode step: the new token's rotated Key rows (every head: the TOKEN
   // norm spans them) and this head's stored Value row, for the wave whose
   // window chunk holds it -- the append's arithmetic, in the append's order.
-  auto new_token_row = [&](int hh, float& ya, float& yb) {
-    const size_t base = (static_cast<size_t>(b) * A.hkv + hh) * kD;
-    ya = in_to_f32(A.k_new[base + L], A.kv_bf16);
-    yb = in_to_f32(A.k_new[base + L + 64], A.kv_bf16);
+  auto rotate_new = [&](uint16_t kx, uint16_t ky, float& ya, float& yb) {
+    ya = in_to_f32(kx, A.kv_bf16);
+    yb = in_to_f32(ky, A.kv_bf16);
     if (A.rope) {  // the new token sits at position n_old
       const float2 cs = reinterpret_cast<const float2*>(A.rope)[static_cast<size_t>(n_old) * 64 + L];
       rope_pair(ya, yb, cs.x, cs.y);
     }
     fht128_wave(ya, yb);
   };
-  int prev_app = -1;
+  const bool flush_step = app && n_old - Q_old == kR;
   if constexpr (STEP != 0) {
     if (wg_new) {
-      for (int hh = wave; hh < A.hkv; hh += NW) {
-        float ya, yb;
-        new_token_row(hh, ya, yb);
-        const float ss = wave_tree_sumsq(ya, yb);
-        if (L == 0) step_part[hh] = ss;
-        if (hh == h) {
-          step_y[L] = ya;
-          step_y[L + 64] = yb;
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        const int hh = wave + NW * j;
+        if (hh < A.hkv) {
+          float ya, yb;
+          rotate_new(knx[j], kny[j], ya, yb);
+          const float ss = wave_tree_sumsq(ya, yb);
+          if (L == 0) step_part[hh] = ss;
+          if (hh == h) {
+            step_y[L] = ya;
+            step_y[L + 64] = yb;
+          }
         }
       }
       if (tid < kD)
         step_v[tid] = f16_sat_bits(in_to_f32(A.v_new[bh * kD + tid], A.kv_bf16));
     }
-    // A wave's window reads have landed before its workgroup counts itself
-    // in (vector loads complete in order; at most the four newest copies of
-    // each of its first two records may still run).
-    if (app && has_ring) {
-      if (cnt >= 2)
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if (cnt == 1)
-        vmcnt_le4();
-      else
-        vmcnt_0();
-    }
   }
   __syncthreads();
-  // Decode step: every workgroup of the sequence counts itself in once it
-  // has read {n, Q} and its window slots; the last to do so writes the new
-  // token and state (at its end), when no slot it overwrites is still read.
   if constexpr (STEP != 0) {
-    if (app && tid == 0)
-      prev_app = __hip_atomic_fetch_add(A.append_sync + b, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
     if (wave_new) {
       // the token's Key row and norm as the append stores them, put in place
       // of what the window loads read at its slot
@@ -969,9 +974,24 @@ void attn_mfma_kernel(AttnArgs A) {
               rv[ct][wi] = (e & 1) ? ((rv[ct][wi] & 0xFFFFu) | (hv << 16)) : ((rv[ct][wi] & 0xFFFF0000u) | hv);
         }
       }
+      const uint16_t nrm16 = f16_sat_bits(nrm);
 #pragma unroll
       for (int j = 0; j < TPL; ++j)
-        if (sm_t0 + j == tau) rnt[j] = f16_to_f32(f16_sat_bits(nrm));
+        if (sm_t0 + j == tau) rnt[j] = f16_to_f32(nrm16);
+      if (!flush_step) {
+        // Without a flush no other wave reads the token's slot in this
+        // launch (the window holds at most 128 tokens, each slot in one
+        // chunk, and this wave has read its own): the append's window rows
+        // of this head, and the norm, are stored now.
+        const int slot = n_old % kR;
+        uint16_t* rkw = A.res_k_w + (bh * kR + slot) * kD;
+        rkw[L] = f32_to_f16(mul_rn(step_y[L], r));
+        rkw[L + 64] = f32_to_f16(mul_rn(step_y[L + 64], r));
+        A.res_v_w[(bh * kD + L) * kR + slot] = step_v[L];
+        A.res_v_w[(bh * kD + L + 64) * kR + slot] = step_v[L + 64];
+        if (L == 0 && (A.head_norm || h == 0))
+          A.res_norm_w[A.head_norm ? bh * kR + slot : static_cast<size_t>(b) * kR + slot] = nrm16;
+      }
     }
   }
   float m_run = -INFINITY, l_part = 0.0f;
@@ -1264,42 +1284,46 @@ void attn_mfma_kernel(AttnArgs A) {
   auto wo_at = [&](int w, int hh) {
     return reinterpret_cast<float*>((hh < 4 ? stage0[w] : stage1[w]) + 512 * (hh & 3));
   };
-  // Decode step, in the workgroup that counted itself in last: the new
-  // token's window rows and norm for every head, then the new state -- the
-  // append's stores, made once every read of what they overwrite is done.
+  // Decode step, in the workgroup that counted itself in last (every other
+  // workgroup of the sequence has finished reading {n, Q} and the window):
+  // on a flush step the new token's window rows and norm for every head
+  // (their slot held a flushed token that others read), then the new state.
   auto append_tail = [&]() {
-    constexpr int HPW = (16 + NW - 1) / NW;  // heads per wave (Hkv <= 16)
-    const int slot = n_old % kR;
-    float ya[HPW], yb[HPW];
+    if (flush_step) {
+      const int slot = n_old % kR;
+      float ya[HPW], yb[HPW];
 #pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-      const int hh = wave + NW * j;
-      ya[j] = yb[j] = 0.0f;
-      if (hh < A.hkv) {
-        new_token_row(hh, ya[j], yb[j]);
-        const float ss = wave_tree_sumsq(ya[j], yb[j]);
-        if (L == 0) step_part[hh] = ss;
+      for (int j = 0; j < HPW; ++j) {
+        const int hh = wave + NW * j;
+        ya[j] = yb[j] = 0.0f;
+        if (hh < A.hkv) {
+          uint16_t kx, ky;
+          load_new(hh, kx, ky);
+          rotate_new(kx, ky, ya[j], yb[j]);
+          const float ss = wave_tree_sumsq(ya[j], yb[j]);
+          if (L == 0) step_part[hh] = ss;
+        }
       }
-    }
-    __syncthreads();
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-      const int hh = wave + NW * j;
-      if (hh < A.hkv) {
-        float nrm, r;
-        scale_from_ss(A.head_norm ? step_part[hh] : tree16(step_part, A.hkv), nrm, r, A.hw_rsq != 0);
-        uint16_t* rkw = A.res_k_w + ((static_cast<size_t>(b) * A.hkv + hh) * kR + slot) * kD;
-        rkw[L] = f32_to_f16(mul_rn(ya[j], r));
-        rkw[L + 64] = f32_to_f16(mul_rn(yb[j], r));
-        if (L == 0 && (A.head_norm || hh == 0))
-          A.res_norm_w[A.head_norm ? (static_cast<size_t>(b) * A.hkv + hh) * kR + slot
-                                   : static_cast<size_t>(b) * kR + slot] = f16_sat_bits(nrm);
+      for (int j = 0; j < HPW; ++j) {
+        const int hh = wave + NW * j;
+        if (hh < A.hkv) {
+          float nrm, r;
+          scale_from_ss(A.head_norm ? step_part[hh] : tree16(step_part, A.hkv), nrm, r, A.hw_rsq != 0);
+          uint16_t* rkw = A.res_k_w + ((static_cast<size_t>(b) * A.hkv + hh) * kR + slot) * kD;
+          rkw[L] = f32_to_f16(mul_rn(ya[j], r));
+          rkw[L + 64] = f32_to_f16(mul_rn(yb[j], r));
+          if (L == 0 && (A.head_norm || hh == 0))
+            A.res_norm_w[A.head_norm ? (static_cast<size_t>(b) * A.hkv + hh) * kR + slot
+                                     : static_cast<size_t>(b) * kR + slot] = f16_sat_bits(nrm);
+        }
       }
-    }
-    // Value rows [B][Hkv][128][slots]; v_new [B][Hkv][128]
-    for (int i = tid; i < A.hkv * kD; i += NT) {
-      const size_t row = static_cast<size_t>(b) * A.hkv * kD + i;
-      A.res_v_w[row * kR + slot] = f16_sat_bits(in_to_f32(A.v_new[row], A.kv_bf16));
+      // Value rows [B][Hkv][128][slots]; v_new [B][Hkv][128]
+      for (int i = tid; i < A.hkv * kD; i += NT) {
+        const size_t row = static_cast<size_t>(b) * A.hkv * kD + i;
+        A.res_v_w[row * kR + slot] = f16_sat_bits(in_to_f32(A.v_new[row], A.kv_bf16));
+      }
     }
     if (tid == 0) {
       A.seq_state_w[2 * b] = n_old + 1;
@@ -1307,9 +1331,18 @@ void attn_mfma_kernel(AttnArgs A) {
       __hip_atomic_store(A.append_sync + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
-  if constexpr (STEP != 0) {
-    if (tid == 0) lds_app = app && prev_app == A.hkv * A.splits - 1;
-  }
+  // Decode step: this workgroup counts itself in (all of its reads are done)
+  // and learns whether it is the sequence's last; where no merge counter is
+  // taken below, on its own.
+  auto count_in_alone = [&]() {
+    if constexpr (STEP != 0) {
+      // (lds_app is written in every case: LDS keeps an earlier launch's bytes)
+      if (tid == 0)
+        lds_app = app && __hip_atomic_fetch_add(A.append_sync + b, 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) == A.hkv * A.splits - 1;
+      __syncthreads();
+    }
+  };
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (sm_on && (L % LPH) == 0) {
@@ -1364,12 +1397,14 @@ void attn_mfma_kernel(AttnArgs A) {
     A.out[row * kD + c] = empty ? 0.0f : Ow * (1.0f / Lw);
     if (c == 0 && A.lse) A.lse[row] = empty ? -INFINITY : (M + log2f(Lw)) * 0.6931471805599453f;
   };
+  // the merge of the splits and the outputs; returns where this workgroup's
+  // part ends
+  auto merge_out = [&]() {
   if (S == 1) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       if (tid + NT * i < GRP * kD) finish(tid + NT * i, Mi[i], Li[i], Oi[i]);
-    if constexpr (STEP != 0)
-      if (lds_app) append_tail();
+    count_in_alone();
     return;
   }
 
@@ -1395,8 +1430,7 @@ void attn_mfma_kernel(AttnArgs A) {
     }
   }
   if (!A.merge_in_kernel) {
-    if constexpr (STEP != 0)
-      if (lds_app) append_tail();
+    count_in_alone();
     return;
   }
   // every wave's stores have completed (reached the L2, or with PUB 1 the
@@ -1409,16 +1443,19 @@ void attn_mfma_kernel(AttnArgs A) {
       prev = __hip_atomic_fetch_add(A.counters + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
       prev = __hip_atomic_fetch_add(A.counters + pair, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (STEP != 0) {
+      // decode step: the sequence's count, in flight together with the merge's
+      const int pa = app ? __hip_atomic_fetch_add(A.append_sync + b, 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                         : -1;
+      lds_app = app && pa == A.hkv * S - 1;
+    }
     lds_last = prev == S - 1;
   }
   __syncthreads();
   // (PUB 0: the counter's acquire, on this workgroup's CU, precedes the
   // barrier that every thread passed before reading the partials)
-  if (!lds_last) {
-    if constexpr (STEP != 0)
-      if (lds_app) append_tail();
-    return;
-  }
+  if (!lds_last) return;
   if (S <= 32) {
     // Lane j < S of each wave reads split j's (m, l) of the wave's head and
     // every lane reads its channel of all S partial outputs, all at once; the
@@ -1453,8 +1490,6 @@ void attn_mfma_kernel(AttnArgs A) {
       finish(idx, M, Lw, Ow);
     }
     if (tid == 0) __hip_atomic_store(A.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if constexpr (STEP != 0)
-      if (lds_app) append_tail();
     return;
   }
   // more splits: a thread's partials are requested 16 at a time
@@ -1503,6 +1538,10 @@ void attn_mfma_kernel(AttnArgs A) {
     finish(idx, M, Lw, Ow);
   }
   if (tid == 0) __hip_atomic_store(A.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  merge_out();
+  // decode step: the sequence's last workgroup makes the append's remaining
+  // stores (one place, after whatever merging this workgroup did)
   if constexpr (STEP != 0)
     if (lds_app) append_tail();
 }
