@@ -754,6 +754,9 @@ void attn_mfma_kernel(AttnArgs A) {
     knx[j] = kny[j] = 0;
     if (STEP != 0 && wg_new && wave + NW * j < A.hkv) load_new(wave + NW * j, knx[j], kny[j]);
   }
+  // and this head's Value row (threads 0..127)
+  uint16_t vnew = 0;
+  if (STEP != 0 && wg_new && tid < kD) vnew = A.v_new[bh * kD + tid];
   int idv = cnt > 0 ? load_ids(0) : 0;
 
   UnitOffs<NR> off;
@@ -932,8 +935,7 @@ void attn_mfma_kernel(AttnArgs A) {
           }
         }
       }
-      if (tid < kD)
-        step_v[tid] = f16_sat_bits(in_to_f32(A.v_new[bh * kD + tid], A.kv_bf16));
+      if (tid < kD) step_v[tid] = f16_sat_bits(in_to_f32(vnew, A.kv_bf16));
     }
   }
   __syncthreads();
@@ -978,20 +980,6 @@ void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
       for (int j = 0; j < TPL; ++j)
         if (sm_t0 + j == tau) rnt[j] = f16_to_f32(nrm16);
-      if (!flush_step) {
-        // Without a flush no other wave reads the token's slot in this
-        // launch (the window holds at most 128 tokens, each slot in one
-        // chunk, and this wave has read its own): the append's window rows
-        // of this head, and the norm, are stored now.
-        const int slot = n_old % kR;
-        uint16_t* rkw = A.res_k_w + (bh * kR + slot) * kD;
-        rkw[L] = f32_to_f16(mul_rn(step_y[L], r));
-        rkw[L + 64] = f32_to_f16(mul_rn(step_y[L + 64], r));
-        A.res_v_w[(bh * kD + L) * kR + slot] = step_v[L];
-        A.res_v_w[(bh * kD + L + 64) * kR + slot] = step_v[L + 64];
-        if (L == 0 && (A.head_norm || h == 0))
-          A.res_norm_w[A.head_norm ? bh * kR + slot : static_cast<size_t>(b) * kR + slot] = nrm16;
-      }
     }
   }
   float m_run = -INFINITY, l_part = 0.0f;
@@ -1443,19 +1431,29 @@ void attn_mfma_kernel(AttnArgs A) {
       prev = __hip_atomic_fetch_add(A.counters + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
       prev = __hip_atomic_fetch_add(A.counters + pair, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if constexpr (STEP != 0) {
-      // decode step: the sequence's count, in flight together with the merge's
-      const int pa = app ? __hip_atomic_fetch_add(A.append_sync + b, 1, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT)
-                         : -1;
-      lds_app = app && pa == A.hkv * S - 1;
-    }
+    if constexpr (STEP != 0) lds_app = 0;
     lds_last = prev == S - 1;
   }
   __syncthreads();
   // (PUB 0: the counter's acquire, on this workgroup's CU, precedes the
   // barrier that every thread passed before reading the partials)
   if (!lds_last) return;
+  // Decode step: the last split of each (sequence, KV head) counts the head
+  // in for the sequence once all S splits have read what they read (one
+  // counter increment per head, not per split); the answer comes back
+  // while the splits are merged.
+  // It is issued by a wave that reads no partials when there is one (its
+  // loads then need not wait for the counter's round trip: a wave's vector
+  // memory results return in order).
+  constexpr int kCountTid = NT > GRP * kD ? NT - 64 : 0;
+  int pa = -1;
+  if constexpr (STEP != 0)
+    if (app && tid == kCountTid)
+      pa = __hip_atomic_fetch_add(A.append_sync + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto counted = [&]() {
+    if constexpr (STEP != 0)
+      if (tid == kCountTid) lds_app = app && pa == A.hkv - 1;
+  };
   if (S <= 32) {
     // Lane j < S of each wave reads split j's (m, l) of the wave's head and
     // every lane reads its channel of all S partial outputs, all at once; the
@@ -1490,6 +1488,7 @@ void attn_mfma_kernel(AttnArgs A) {
       finish(idx, M, Lw, Ow);
     }
     if (tid == 0) __hip_atomic_store(A.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    counted();
     return;
   }
   // more splits: a thread's partials are requested 16 at a time
@@ -1538,12 +1537,34 @@ void attn_mfma_kernel(AttnArgs A) {
     finish(idx, M, Lw, Ow);
   }
   if (tid == 0) __hip_atomic_store(A.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  counted();
   };
   merge_out();
-  // decode step: the sequence's last workgroup makes the append's remaining
-  // stores (one place, after whatever merging this workgroup did)
-  if constexpr (STEP != 0)
+  if constexpr (STEP != 0) {
+    // Without a flush no other wave reads the new token's slot in this
+    // launch (the window holds at most 128 tokens, each slot in one chunk,
+    // and the wave that holds it has read it): that wave stores the
+    // append's window rows of this head, and the norm, at its very end,
+    // where no wait of its own depends on them.
+    if (wave_new && !flush_step) {
+      const float ss = A.head_norm ? step_part[h] : tree16(step_part, A.hkv);
+      float nrm, r;
+      scale_from_ss(ss, nrm, r, A.hw_rsq != 0);
+      const int slot = n_old % kR;
+      uint16_t* rkw = A.res_k_w + (bh * kR + slot) * kD;
+      rkw[L] = f32_to_f16(mul_rn(step_y[L], r));
+      rkw[L + 64] = f32_to_f16(mul_rn(step_y[L + 64], r));
+      A.res_v_w[(bh * kD + L) * kR + slot] = step_v[L];
+      A.res_v_w[(bh * kD + L + 64) * kR + slot] = step_v[L + 64];
+      if (L == 0 && (A.head_norm || h == 0))
+        A.res_norm_w[A.head_norm ? bh * kR + slot : static_cast<size_t>(b) * kR + slot] =
+            f16_sat_bits(nrm);
+    }
+    // the sequence's last workgroup makes the append's remaining stores
+    // (one place, after whatever merging this workgroup did)
+    __syncthreads();
     if (lds_app) append_tail();
+  }
 }
 
 // ---------------------------------------------------------------- reduce
