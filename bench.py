@@ -41,16 +41,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak
 # batch-1 decode workloads: option name -> (synthetic workload id, description,
 # layer caches cycled so that they exceed 3x the 256 MB Infinity Cache,
-# profile summary holding the attention kernel's byte counters)
+# profile summary holding the decode-step kernel's byte counters)
 WORKLOADS = {
     "llama-32k": (1, "llama-3.1-8b-shape decode, 32K ctx, batch 1", 32,
-                  "decode_attn_llama-3.1-8b-32k.md"),
+                  "decode_step_llama-3.1-8b-32k.md"),
     "qwen3-128k": (2, "qwen3-8b-shape decode, 128K ctx, batch 1", 8,
-                   "decode_attn_qwen3-8b-128k.md"),
+                   "decode_step_qwen3-8b-128k.md"),
     "multimodal-64k": (4, "qwen3-vl-8b-shape multimodal prefill + decode, 64K ctx, batch 1", 16,
-                       "decode_attn_multimodal-64k.md"),
+                       "decode_step_multimodal-64k.md"),
 }
-BATCH48_PROFILE = "decode_attn_qwen3-8b-batch48.md"
+BATCH48_PROFILE = "decode_step_qwen3-8b-batch48.md"
 # the decode-attention kernel and the headers it compiles from
 ATTN_SRC = [os.path.join(ROOT, "int2_kv_cache_amd", "csrc", f)
             for f in ("oscar_attn.hip", "oscar_device.hpp", "oscar_host.hpp", "oscar_quant.hpp")]
