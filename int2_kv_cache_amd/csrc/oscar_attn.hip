@@ -681,11 +681,15 @@ void attn_mfma_kernel(AttnArgs A) {
   // Splits partition the units by weight: an INT2 block weighs 1, a window
   // chunk (16 KB of fp16 data against a 3 KB record) kRingWeight.
   const int nb = Q / kG, nr = (n - Q + kG - 1) / kG;
-  const long long wt = nb + static_cast<long long>(kRingWeight) * nr;
-  auto unit_at = [&](long long w) {
-    return w <= nb ? static_cast<int>(w) : nb + static_cast<int>((w - nb + kRingWeight - 1) / kRingWeight);
+  const unsigned wt = nb + kRingWeight * nr, S_u = A.splits;
+  auto unit_at = [&](unsigned w) {
+    return w <= static_cast<unsigned>(nb) ? static_cast<int>(w)
+                                          : nb + static_cast<int>((w - nb + kRingWeight - 1) / kRingWeight);
   };
-  const int u0 = unit_at(s * wt / A.splits), u1 = unit_at((s + 1) * wt / A.splits);
+  // floor(s wt / S) in 32-bit arithmetic: with wt = qw S + rw it is
+  // s qw + floor(s rw / S), and s rw < S^2 <= 2^20
+  const unsigned qw = wt / S_u, rw = wt - qw * S_u;
+  const int u0 = unit_at(s * qw + s * rw / S_u), u1 = unit_at((s + 1) * qw + (s + 1) * rw / S_u);
   const size_t bh = static_cast<size_t>(b) * A.hkv + h;
   const int col = L & 15, g4 = L >> 4;
   const int sm_head = L / LPH, sm_t0 = TPL * (L % LPH), sm_c0 = CPL * (L % LPH);
@@ -720,25 +724,39 @@ void attn_mfma_kernel(AttnArgs A) {
     return bad ? 0 : id;
   };
   // The query heads of this wave (wave, wave + NW) load first: their latency
-  // overlaps the block-table read and the first record's.
+  // overlaps the block-table read and the first record's.  They stay raw
+  // bits (fp32, or the 16-bit value) until the record copies are issued: a
+  // conversion here would wait for them before the block ids are requested.
   constexpr int QPW = (GRP + NW - 1) / NW;
-  float qx[QPW], qy[QPW];
+  uint32_t qbx[QPW], qby[QPW];
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
     const int i = wave + NW * j;
-    qx[j] = qy[j] = 0.0f;
+    qbx[j] = qby[j] = 0u;
     if (i < GRP) {
       const size_t base = (static_cast<size_t>(b) * A.hq + h * GRP + i) * kD;
       if (A.q_mode == 2) {
-        qx[j] = static_cast<const float*>(A.q)[base + L];
-        qy[j] = static_cast<const float*>(A.q)[base + L + 64];
+        qbx[j] = static_cast<const uint32_t*>(A.q)[base + L];
+        qby[j] = static_cast<const uint32_t*>(A.q)[base + L + 64];
       } else {
         const uint16_t* q16 = static_cast<const uint16_t*>(A.q);
-        qx[j] = in_to_f32(q16[base + L], A.q_mode);
-        qy[j] = in_to_f32(q16[base + L + 64], A.q_mode);
+        qbx[j] = q16[base + L];
+        qby[j] = q16[base + L + 64];
       }
     }
   }
+  // and their RoPE (cos, sin) at the step's own position, n - 1.  The load is
+  // made in every case, from the state's first word when no RoPE applies:
+  // with a branch around it, the path that sets (1, 0) instead would write
+  // its registers while the load may still be in flight, and must first
+  // wait for every earlier load.  A position past the table flags the call
+  // and leaves the query unrotated.
+  const bool q_rope = A.rope && A.q_mode != 2 && n >= 1;
+  if (q_rope && n - 1 >= A.rope_max_pos && wave == 0 && L == 0)
+    atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_POSITION));
+  const bool q_rope_on = q_rope && n - 1 < A.rope_max_pos;
+  const float2 qcs_ld = *(q_rope_on ? reinterpret_cast<const float2*>(A.rope) + static_cast<size_t>(n - 1) * 64 + L
+                                    : reinterpret_cast<const float2*>(A.seq_state));
   // Decode step: the new token's Keys for the heads this wave rotates (wave,
   // wave + NW, ..), requested with the query when the split's window chunk
   // holds the token
@@ -757,7 +775,6 @@ void attn_mfma_kernel(AttnArgs A) {
   // and this head's Value row (threads 0..127)
   uint16_t vnew = 0;
   if (STEP != 0 && wg_new && tid < kD) vnew = A.v_new[bh * kD + tid];
-  int idv = cnt > 0 ? load_ids(0) : 0;
 
   UnitOffs<NR> off;
   off.kc0 = kRecKCodes + 32 * col + 8 * g4;
@@ -782,7 +799,11 @@ void attn_mfma_kernel(AttnArgs A) {
   const int ring_tb = Q + kG * (first + NW * cnt - nb);
   const int ring_valid = has_ring ? min(32, n - ring_tb) : 0;
   u32x4 rk[2][4], rv[8];
-  float rnt[TPL];
+  // the softmax lane's token norms of the chunk (tokens sm_t0 .. sm_t0 + TPL
+  // - 1, consecutive and 4-byte aligned when TPL > 1), fp16 bits kept in
+  // whole words until they are used
+  constexpr int RNW = (TPL + 1) / 2;
+  uint32_t rnw[RNW];
   auto load_ring = [&]() {
     const int slot0 = ring_tb % kR;  // a multiple of 32: the chunk is 32 consecutive slots
 #pragma unroll
@@ -794,13 +815,19 @@ void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
       rv[ct] = *reinterpret_cast<const u32x4*>(A.res_v + (bh * kD + 16 * ct + col) * kR + slot0 + 8 * g4);
+    const uint16_t* wn = window_norms(A, b, h) + slot0 + sm_t0;
+    if constexpr (TPL == 1) {
+      rnw[0] = wn[0];
+    } else {
 #pragma unroll
-    for (int j = 0; j < TPL; ++j)
-      rnt[j] = f16_to_f32(window_norms(A, b, h)[slot0 + ((sm_t0 + j) & 31)]);
+      for (int i = 0; i < RNW; ++i) rnw[i] = reinterpret_cast<const uint32_t*>(wn)[i];
+    }
   };
   // (a workgroup that quantizes a flushed block first loads its window
   // chunks after that, so that their registers are free meanwhile)
   if (has_ring && !wg_fresh) load_ring();
+  // the block ids, requested after every load that does not depend on them
+  int idv = cnt > 0 ? load_ids(0) : 0;
 
   // Block j of the wave goes through stage j % 2.  Its DMA is issued two
   // blocks ahead (unconditionally: past the end it re-reads the last block)
@@ -891,19 +918,25 @@ void attn_mfma_kernel(AttnArgs A) {
     }
   }
 
-  const float2 qcs = query_rope(A, n, L);
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
     const int i = wave + NW * j;
     if (i < GRP) {
-      if (A.q_mode != 2) {
-        rope_pair(qx[j], qy[j], qcs.x, qcs.y);
-        fht128_wave(qx[j], qy[j]);
+      float qx, qy;
+      if (A.q_mode == 2) {
+        qx = __uint_as_float(qbx[j]);
+        qy = __uint_as_float(qby[j]);
+      } else {
+        qx = in_to_f32(static_cast<uint16_t>(qbx[j]), A.q_mode);
+        qy = in_to_f32(static_cast<uint16_t>(qby[j]), A.q_mode);
+        const float2 qcs = q_rope_on ? qcs_ld : make_float2(1.0f, 0.0f);
+        rope_pair(qx, qy, qcs.x, qcs.y);
+        fht128_wave(qx, qy);
       }
       // q' carries the score scale 1/sqrt(128) * log2(e): every score
       // comes out in the log2 domain of the softmax
-      qs[i * kD + L] = qx[j] * kScale;
-      qs[i * kD + L + 64] = qy[j] * kScale;
+      qs[i * kD + L] = qx * kScale;
+      qs[i * kD + L + 64] = qy * kScale;
     }
   }
   // Decode step: the new token's rotated Key rows (every head: the TOKEN
@@ -979,7 +1012,11 @@ void attn_mfma_kernel(AttnArgs A) {
       const uint16_t nrm16 = f16_sat_bits(nrm);
 #pragma unroll
       for (int j = 0; j < TPL; ++j)
-        if (sm_t0 + j == tau) rnt[j] = f16_to_f32(nrm16);
+        if (sm_t0 + j == tau) {
+          uint32_t& w = rnw[j >> 1];
+          w = TPL == 1 ? nrm16
+              : (j & 1) ? ((w & 0xFFFFu) | (static_cast<uint32_t>(nrm16) << 16)) : ((w & 0xFFFF0000u) | nrm16);
+        }
     }
   }
   float m_run = -INFINITY, l_part = 0.0f;
@@ -1185,6 +1222,13 @@ void attn_mfma_kernel(AttnArgs A) {
       cs[tau] = acc;
     }
     store_scores(cs);
+    // converted here, not where they were loaded: the empty statement keeps
+    // the compiler from moving the conversion (and its wait) up there
+#pragma unroll
+    for (int i = 0; i < RNW; ++i) asm volatile("" : "+v"(rnw[i]));
+    float rnt[TPL];
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) rnt[j] = f16_to_f32(static_cast<uint16_t>(rnw[j >> 1] >> (16 * (j & 1))));
     softmax_block(rnt, 0.0f, ring_valid, true);
     pv_tiles(nullptr);
     const u32x4 b0 = Wbv[0][vrow];
