@@ -463,20 +463,24 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Written as inline assembly so that the compiler does not track these LDS
 // writes (its tracking waits for every copy in flight before any LDS access
 // it cannot prove disjoint); the stage readers wait with vmcnt_le4 instead.
-// M0 holds the stage's LDS address.
+// M0 holds the stage's LDS address.  The copies are non-temporal (nt): each
+// record is read once per call, and streaming it through the caches as
+// normal lines would evict what the call does reuse (its partials, the state,
+// the block table, its own code) -- measured 1.2 to 1.5 us less per call at
+// batch 1.
 __device__ __forceinline__ void dma_unit(__amdgpu_buffer_rsrc_t rec, __amdgpu_buffer_rsrc_t nrm,
                                          const uint8_t* st, int L) {
   const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)st));
   const uint32_t v0 = 16 * L, v1 = 16 * L + 1024, v2 = 16 * L + 2048, vn = 4 * L;
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen nt lds\n\t"
       "s_add_u32 m0, %0, 0x400\n\t"
-      "buffer_load_dwordx4 %2, %5, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %5, 0 offen nt lds\n\t"
       "s_add_u32 m0, %0, 0x800\n\t"
-      "buffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen nt lds\n\t"
       "s_add_u32 m0, %0, 0xc00\n\t"
-      "buffer_load_dword %4, %6, 0 offen lds"
+      "buffer_load_dword %4, %6, 0 offen nt lds"
       :
       : "s"(base), "v"(v0), "v"(v1), "v"(v2), "v"(vn), "s"(rec), "s"(nrm)
       : "memory", "m0", "scc");
@@ -1258,11 +1262,15 @@ void attn_mfma_kernel(AttnArgs A) {
   // Q.K^T has been issued.  Copies of blocks k + 1 and k + 2 are in flight
   // during most of block k.
   UnitRegs<NR, CPL> ru;
-  // Every load issued so far has landed (blocks 0 and 1 included): a wait
-  // the compiler sees on every path into the loop, so that it keeps no stale
-  // wait for earlier register loads inside the loop, where a full wait would
-  // also stall on the copies in flight.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  // Block 0 has landed, and so has every load issued before the copies:
+  // only block 1's four copies, the newest operations, may still run.  A
+  // wait the compiler sees on every path into the loop, so that it keeps no
+  // stale wait for earlier register loads inside the loop, where a full wait
+  // would also stall on the copies in flight.
+  if (cnt > 1)
+    __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   if (cnt > 0) {
     read_kpart<GRP, NR, TPL, CPL>(ru, off, st0, L);
     read_vpart<GRP, NR, TPL, CPL>(ru, off, st0, L);
@@ -1304,12 +1312,17 @@ void attn_mfma_kernel(AttnArgs A) {
     if (c < NCOMBO && (c & 3) == 0) Wzs[c / (4 * GRP)][(c >> 2) % GRP] = z;
   }
   lds_order();
+  // (the four sums of the lane's head, read by every lane: col % GRP is a
+  // head of the wave)
+  float zs[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) zs[d] = Wzs[d][col % GRP];
   float ov[8][4];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      ov[ct][j] = o[ct][j] + dpp<dpp_row_shl(GRP)>(o[ct][j]) + (col < GRP ? Wzs[ct >> 1][col] : 0.0f);
+      ov[ct][j] = o[ct][j] + dpp<dpp_row_shl(GRP)>(o[ct][j]) + (col < GRP ? zs[ct >> 1] : 0.0f);
   // the stages take the waves' partial outputs: head hh of wave w at
   // (hh < 4 ? stage0 : stage1)[w] + 512 (hh % 4) bytes, once every copy into
   // them has landed
