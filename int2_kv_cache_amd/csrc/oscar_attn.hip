@@ -38,8 +38,9 @@ struct AttnArgs {
   int32_t* error_flag;
   float2* ws_ml;  // [B][Hq][S] (m, l)
   float* ws_o;    // [B][Hq][S][128]
-  // arrival counters of the cross-split merge, [B][Hkv]: zero before a
-  // launch, and zero again after it (the merging workgroup resets its own)
+  // arrival counters of the cross-split merge, one per (sequence, KV head)
+  // at counter_slot(pair): zero before a launch, and zero again after it
+  // (the merging workgroup resets its own)
   int32_t* counters;
   float* out;     // [B][Hq][128]
   float* lse;     // [B][Hq] or null
@@ -64,6 +65,13 @@ struct AttnArgs {
   int32_t* seq_state_w;
   int32_t* append_sync;   // [B] arrival counters: zero before and after a launch
 };
+
+// The counter of pair p (= b Hkv + h) in the 65536-int counter region:
+// slot 32 (p mod 2048) + p / 2048, a one-to-one map that gives each of the
+// first 2048 pairs a 128-byte line of its own.  Adjacent counters would put
+// every KV head's arrivals (one device-scope atomic per split) on one line,
+// where they serialize.
+__device__ __forceinline__ int counter_slot(int pair) { return ((pair & 2047) << 5) | (pair >> 11); }
 
 // A stored fp16 value from fp32, as the append stores Values and norms:
 // clamped to +-65504 first, a NaN stored as -65504 (the clamp's result in
@@ -1485,9 +1493,9 @@ void attn_mfma_kernel(AttnArgs A) {
   if (tid == 0) {
     int prev;
     if constexpr (PUB == 1)
-      prev = __hip_atomic_fetch_add(A.counters + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      prev = __hip_atomic_fetch_add(A.counters + counter_slot(pair), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
-      prev = __hip_atomic_fetch_add(A.counters + pair, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      prev = __hip_atomic_fetch_add(A.counters + counter_slot(pair), 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if constexpr (STEP != 0) lds_app = 0;
     lds_last = prev == S - 1;
   }
@@ -1544,7 +1552,7 @@ void attn_mfma_kernel(AttnArgs A) {
                 oc[j];
       finish(idx, M, Lw, Ow);
     }
-    if (tid == 0) __hip_atomic_store(A.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(A.counters + counter_slot(pair), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     counted();
     return;
   }
@@ -1593,7 +1601,7 @@ void attn_mfma_kernel(AttnArgs A) {
     }
     finish(idx, M, Lw, Ow);
   }
-  if (tid == 0) __hip_atomic_store(A.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(A.counters + counter_slot(pair), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   counted();
   };
   merge_out();
@@ -1752,7 +1760,7 @@ int auto_splits(const oscar_cache_geom* g, int max_ctx) { return attn_shape(g, m
 
 // Workspace of the matrix-core path: the merge's arrival counters first, at
 // a fixed place and size (one int32 per (sequence, KV head), for up to
-// kMaxPairs pairs), so that a workspace zero-filled once stays valid for any
+// kMaxPairs pairs, at counter_slot), so that a workspace zero-filled once stays valid for any
 // later call whatever its geometry or split count; then the partials in the
 // layout the separate merge launch reads (workspace_bytes below).
 constexpr int kMaxPairs = 65536;
