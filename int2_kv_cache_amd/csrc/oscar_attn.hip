@@ -1029,6 +1029,21 @@ void attn_mfma_kernel(AttnArgs A) {
           w = TPL == 1 ? nrm16
               : (j & 1) ? ((w & 0xFFFFu) | (static_cast<uint32_t>(nrm16) << 16)) : ((w & 0xFFFF0000u) | nrm16);
         }
+      // Without a flush no other wave reads the new token's slot in this
+      // launch (the window holds at most 128 tokens, each slot in one chunk,
+      // and this wave has read its chunk): it stores the append's window
+      // row and column of this head, and the norm, now, so that they complete
+      // during its main loop rather than at the end of the launch.
+      if (!flush_step) {
+        const int slot = n_old % kR;
+        uint16_t* rkw = A.res_k_w + (bh * kR + slot) * kD;
+        rkw[L] = f32_to_f16(mul_rn(step_y[L], r));
+        rkw[L + 64] = f32_to_f16(mul_rn(step_y[L + 64], r));
+        A.res_v_w[(bh * kD + L) * kR + slot] = step_v[L];
+        A.res_v_w[(bh * kD + L + 64) * kR + slot] = step_v[L + 64];
+        if (L == 0 && (A.head_norm || h == 0))
+          A.res_norm_w[A.head_norm ? bh * kR + slot : static_cast<size_t>(b) * kR + slot] = nrm16;
+      }
     }
   }
   float m_run = -INFINITY, l_part = 0.0f;
@@ -1606,25 +1621,6 @@ void attn_mfma_kernel(AttnArgs A) {
   };
   merge_out();
   if constexpr (STEP != 0) {
-    // Without a flush no other wave reads the new token's slot in this
-    // launch (the window holds at most 128 tokens, each slot in one chunk,
-    // and the wave that holds it has read it): that wave stores the
-    // append's window rows of this head, and the norm, at its very end,
-    // where no wait of its own depends on them.
-    if (wave_new && !flush_step) {
-      const float ss = A.head_norm ? step_part[h] : tree16(step_part, A.hkv);
-      float nrm, r;
-      scale_from_ss(ss, nrm, r, A.hw_rsq != 0);
-      const int slot = n_old % kR;
-      uint16_t* rkw = A.res_k_w + (bh * kR + slot) * kD;
-      rkw[L] = f32_to_f16(mul_rn(step_y[L], r));
-      rkw[L + 64] = f32_to_f16(mul_rn(step_y[L + 64], r));
-      A.res_v_w[(bh * kD + L) * kR + slot] = step_v[L];
-      A.res_v_w[(bh * kD + L + 64) * kR + slot] = step_v[L + 64];
-      if (L == 0 && (A.head_norm || h == 0))
-        A.res_norm_w[A.head_norm ? bh * kR + slot : static_cast<size_t>(b) * kR + slot] =
-            f16_sat_bits(nrm);
-    }
     // the sequence's last workgroup makes the append's remaining stores
     // (one place, after whatever merging this workgroup did)
     __syncthreads();
