@@ -645,7 +645,33 @@ void attn_mfma_kernel(AttnArgs A) {
   // set-up (loads, query rotation, the window chunk) runs at the highest
   // priority: the main loop lowers it as a wave progresses
   __builtin_amdgcn_s_setprio(3);
-  int n = A.seq_state[2 * b], Q = A.seq_state[2 * b + 1];
+  // {n, Q} by a scalar load (b is uniform): nothing in the launch writes it
+  // before every workgroup has read it, and the vector loads issued next do
+  // not wait behind it
+  typedef __attribute__((address_space(4))) const int32_t* cst_i32_t;
+  const cst_i32_t st_cst = (cst_i32_t)(A.seq_state);
+  int n = st_cst[2 * b], Q = st_cst[2 * b + 1];
+  const size_t bh = static_cast<size_t>(b) * A.hkv + h;
+  // Decode step: the new token's Keys for the heads this wave rotates (wave,
+  // wave + NW, ..) and this head's Value row (threads 0..127), requested
+  // with the state in every workgroup (the one that appends is known only
+  // from the state), so that their latency hides behind the state's
+  constexpr int HPW = (16 + NW - 1) / NW;  // heads per wave (Hkv <= 16)
+  uint16_t knx[HPW], kny[HPW];
+  auto load_new = [&](int hh, uint16_t& kx, uint16_t& ky) {
+    const size_t base = (static_cast<size_t>(b) * A.hkv + hh) * kD;
+    kx = A.k_new[base + L];
+    ky = A.k_new[base + L + 64];
+  };
+  uint16_t vnew = 0;
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) knx[j] = kny[j] = 0;
+  if constexpr (STEP != 0) {
+#pragma unroll
+    for (int j = 0; j < HPW; ++j)
+      if (wave + NW * j < A.hkv) load_new(wave + NW * j, knx[j], kny[j]);
+    if (tid < kD) vnew = A.v_new[bh * kD + tid];
+  }
   const bool state_good = Q >= 0 && (Q & 31) == 0 && n >= Q && n - Q <= kR && Q / kG <= A.max_blocks;
   if (!state_good) {
     if (tid == 0 && s == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
@@ -702,7 +728,6 @@ void attn_mfma_kernel(AttnArgs A) {
   // s qw + floor(s rw / S), and s rw < S^2 <= 2^20
   const unsigned qw = wt / S_u, rw = wt - qw * S_u;
   const int u0 = unit_at(s * qw + s * rw / S_u), u1 = unit_at((s + 1) * qw + (s + 1) * rw / S_u);
-  const size_t bh = static_cast<size_t>(b) * A.hkv + h;
   const int col = L & 15, g4 = L >> 4;
   const int sm_head = L / LPH, sm_t0 = TPL * (L % LPH), sm_c0 = CPL * (L % LPH);
   const bool sm_on = sm_head < GRP;
@@ -769,24 +794,6 @@ void attn_mfma_kernel(AttnArgs A) {
   const bool q_rope_on = q_rope && n - 1 < A.rope_max_pos;
   const float2 qcs_ld = *(q_rope_on ? reinterpret_cast<const float2*>(A.rope) + static_cast<size_t>(n - 1) * 64 + L
                                     : reinterpret_cast<const float2*>(A.seq_state));
-  // Decode step: the new token's Keys for the heads this wave rotates (wave,
-  // wave + NW, ..), requested with the query when the split's window chunk
-  // holds the token
-  constexpr int HPW = (16 + NW - 1) / NW;  // heads per wave (Hkv <= 16)
-  uint16_t knx[HPW], kny[HPW];
-  auto load_new = [&](int hh, uint16_t& kx, uint16_t& ky) {
-    const size_t base = (static_cast<size_t>(b) * A.hkv + hh) * kD;
-    kx = A.k_new[base + L];
-    ky = A.k_new[base + L + 64];
-  };
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    knx[j] = kny[j] = 0;
-    if (STEP != 0 && wg_new && wave + NW * j < A.hkv) load_new(wave + NW * j, knx[j], kny[j]);
-  }
-  // and this head's Value row (threads 0..127)
-  uint16_t vnew = 0;
-  if (STEP != 0 && wg_new && tid < kD) vnew = A.v_new[bh * kD + tid];
 
   UnitOffs<NR> off;
   off.kc0 = kRecKCodes + 32 * col + 8 * g4;
