@@ -50,19 +50,12 @@ struct AttnArgs {
   const float* rope;
   int rope_max_pos;
   // Decode step (STEP kernels): each sequence's new token, appended by the
-  // same launch, and the cache buffers the append writes (the same buffers
-  // as above)
+  // same launch (it writes the cache buffers above through the same pointers)
   const uint16_t* k_new;  // [B][Hkv][128], bf16 or fp16 (kv_bf16)
   const uint16_t* v_new;
   int kv_bf16;
   int flush_blocks;       // blocks quantized when the window is full: 1 or 4
   int hw_rsq;             // 1: Key scaling factor from the hardware rsqrt
-  uint8_t* pool_w;
-  uint16_t* pool_norm_w;
-  uint16_t* res_k_w;
-  uint16_t* res_v_w;
-  uint16_t* res_norm_w;
-  int32_t* seq_state_w;
   int32_t* append_sync;   // [B] arrival counters: zero before and after a launch
 };
 
@@ -880,7 +873,7 @@ void attn_mfma_kernel(AttnArgs A) {
       for (int fu = f0; fu < f1; ++fu) {
         const int s0 = (Q_old + kG * (fu - Q_old / kG)) % kR;
         const int p = A.block_table[static_cast<size_t>(b) * A.max_blocks + fu];
-        uint8_t* rec = A.pool_w + (static_cast<size_t>(p) * A.hkv + h) * kRec;
+        uint8_t* rec = const_cast<uint8_t*>(A.pool) + (static_cast<size_t>(p) * A.hkv + h) * kRec;
         for (int i = tid; i < 32 * kD / 8; i += NT) {
           reinterpret_cast<uint4*>(fk)[i] =
               reinterpret_cast<const uint4*>(A.res_k + (bh * kR + s0) * kD)[i];
@@ -890,7 +883,7 @@ void attn_mfma_kernel(AttnArgs A) {
         // TOKEN scope: every head writes the same 32 norms
         if (tid < 32) {
           const uint16_t nv = window_norms(A, b, h)[s0 + tid];
-          A.pool_norm_w[A.head_norm ? (static_cast<size_t>(p) * A.hkv + h) * 32 + tid
+          const_cast<uint16_t*>(A.pool_norm)[A.head_norm ? (static_cast<size_t>(p) * A.hkv + h) * 32 + tid
                                     : static_cast<size_t>(p) * 32 + tid] = nv;
         }
         __syncthreads();
@@ -1043,13 +1036,13 @@ void attn_mfma_kernel(AttnArgs A) {
       // during its main loop rather than at the end of the launch.
       if (!flush_step) {
         const int slot = n_old % kR;
-        uint16_t* rkw = A.res_k_w + (bh * kR + slot) * kD;
+        uint16_t* rkw = const_cast<uint16_t*>(A.res_k) + (bh * kR + slot) * kD;
         rkw[L] = f32_to_f16(mul_rn(step_y[L], r));
         rkw[L + 64] = f32_to_f16(mul_rn(step_y[L + 64], r));
-        A.res_v_w[(bh * kD + L) * kR + slot] = step_v[L];
-        A.res_v_w[(bh * kD + L + 64) * kR + slot] = step_v[L + 64];
+        const_cast<uint16_t*>(A.res_v)[(bh * kD + L) * kR + slot] = step_v[L];
+        const_cast<uint16_t*>(A.res_v)[(bh * kD + L + 64) * kR + slot] = step_v[L + 64];
         if (L == 0 && (A.head_norm || h == 0))
-          A.res_norm_w[A.head_norm ? bh * kR + slot : static_cast<size_t>(b) * kR + slot] = nrm16;
+          const_cast<uint16_t*>(A.res_norm)[A.head_norm ? bh * kR + slot : static_cast<size_t>(b) * kR + slot] = nrm16;
       }
     }
   }
@@ -1386,23 +1379,23 @@ void attn_mfma_kernel(AttnArgs A) {
         if (hh < A.hkv) {
           float nrm, r;
           scale_from_ss(A.head_norm ? step_part[hh] : tree16(step_part, A.hkv), nrm, r, A.hw_rsq != 0);
-          uint16_t* rkw = A.res_k_w + ((static_cast<size_t>(b) * A.hkv + hh) * kR + slot) * kD;
+          uint16_t* rkw = const_cast<uint16_t*>(A.res_k) + ((static_cast<size_t>(b) * A.hkv + hh) * kR + slot) * kD;
           rkw[L] = f32_to_f16(mul_rn(ya[j], r));
           rkw[L + 64] = f32_to_f16(mul_rn(yb[j], r));
           if (L == 0 && (A.head_norm || hh == 0))
-            A.res_norm_w[A.head_norm ? (static_cast<size_t>(b) * A.hkv + hh) * kR + slot
+            const_cast<uint16_t*>(A.res_norm)[A.head_norm ? (static_cast<size_t>(b) * A.hkv + hh) * kR + slot
                                      : static_cast<size_t>(b) * kR + slot] = f16_sat_bits(nrm);
         }
       }
       // Value rows [B][Hkv][128][slots]; v_new [B][Hkv][128]
       for (int i = tid; i < A.hkv * kD; i += NT) {
         const size_t row = static_cast<size_t>(b) * A.hkv * kD + i;
-        A.res_v_w[row * kR + slot] = f16_sat_bits(in_to_f32(A.v_new[row], A.kv_bf16));
+        const_cast<uint16_t*>(A.res_v)[row * kR + slot] = f16_sat_bits(in_to_f32(A.v_new[row], A.kv_bf16));
       }
     }
     if (tid == 0) {
-      A.seq_state_w[2 * b] = n_old + 1;
-      A.seq_state_w[2 * b + 1] = Q;
+      const_cast<int32_t*>(A.seq_state)[2 * b] = n_old + 1;
+      const_cast<int32_t*>(A.seq_state)[2 * b + 1] = Q;
       __hip_atomic_store(A.append_sync + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
@@ -1872,12 +1865,6 @@ static oscar_status decode_call(const oscar_cache_geom* geom, const oscar_cache*
   A.kv_bf16 = kv_dtype == OSCAR_BF16 ? 1 : 0;
   A.flush_blocks = geom->flush_tokens == 128 ? 4 : 1;
   A.hw_rsq = geom->key_scale == OSCAR_SCALE_HW_RSQ ? 1 : 0;
-  A.pool_w = static_cast<uint8_t*>(cache->pool);
-  A.pool_norm_w = static_cast<uint16_t*>(cache->pool_norm);
-  A.res_k_w = static_cast<uint16_t*>(cache->res_k);
-  A.res_v_w = static_cast<uint16_t*>(cache->res_v);
-  A.res_norm_w = static_cast<uint16_t*>(cache->res_norm);
-  A.seq_state_w = cache->seq_state;
   A.append_sync = cache->append_sync;
   hipStream_t hs = as_stream(stream);
   const int grp = geom->num_q_heads / geom->num_kv_heads;
