@@ -292,8 +292,10 @@ OSCAR_API oscar_status oscar_decode_workspace_bytes(const oscar_cache_geom *geom
  *            for the cross-split merge that the launch does itself (B * Hkv
  *            <= 65536); every call leaves them zero again, so the workspace
  *            stays valid for any later call whose size fits (any geometry or
- *            split count).  The rest holds the per-split partials (m, l, o),
- *            rewritten by every call.  Two calls in flight at the same time
+ *            split count).  The rest holds the per-split partials (m, l, o)
+ *            and, for a batch of 2..1024 sequences, the launch order
+ *            (sequences longest first, with their {n, Q}), rewritten by
+ *            every call.  Two calls in flight at the same time
  *            must not share a workspace.
  *   num_splits  0 = pick from max_ctx; else 1..1024 splits per (b, KV head).
  *   variant  AUTO / MFMA: one launch (matrix-core attention; the last split

@@ -57,6 +57,9 @@ struct AttnArgs {
   int flush_blocks;       // blocks quantized when the window is full: 1 or 4
   int hw_rsq;             // 1: Key scaling factor from the hardware rsqrt
   int32_t* append_sync;   // [B] arrival counters: zero before and after a launch
+  // null, or the launch order of the sequences: for rank r, {b, n, Q, 0} of
+  // the r-th longest sequence, taken before the launch (sched_kernel)
+  const int32_t* sched;
 };
 
 // The counter of pair p (= b Hkv + h) in the 65536-int counter region:
@@ -621,9 +624,11 @@ void attn_mfma_kernel(AttnArgs A) {
   __shared__ uint16_t step_v[STEP ? kD : 2];
   __shared__ int lds_app;
 
+  // workgroup (r Hkv + h) S + s: split s of KV head h of the sequence of
+  // launch rank r (the sequence itself with no schedule)
   const int wid = static_cast<int>(blockIdx.x);
-  const int pair = wid / A.splits, s = wid - pair * A.splits;
-  const int b = pair / A.hkv, h = pair - b * A.hkv;
+  const int rh = wid / A.splits, s = wid - rh * A.splits;
+  const int rank = rh / A.hkv, h = rh - rank * A.hkv;
   // wave index as a wave-uniform (scalar) value: unit indices and record
   // addresses then stay in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), L = tid & 63;
@@ -638,33 +643,68 @@ void attn_mfma_kernel(AttnArgs A) {
   // set-up (loads, query rotation, the window chunk) runs at the highest
   // priority: the main loop lowers it as a wave progresses
   __builtin_amdgcn_s_setprio(3);
-  // {n, Q} by a scalar load (b is uniform): nothing in the launch writes it
-  // before every workgroup has read it, and the vector loads issued next do
-  // not wait behind it
-  typedef __attribute__((address_space(4))) const int32_t* cst_i32_t;
-  const cst_i32_t st_cst = (cst_i32_t)(A.seq_state);
-  int n = st_cst[2 * b], Q = st_cst[2 * b + 1];
-  const size_t bh = static_cast<size_t>(b) * A.hkv + h;
   // Decode step: the new token's Keys for the heads this wave rotates (wave,
   // wave + NW, ..) and this head's Value row (threads 0..127), requested
   // with the state in every workgroup (the one that appends is known only
   // from the state), so that their latency hides behind the state's
   constexpr int HPW = (16 + NW - 1) / NW;  // heads per wave (Hkv <= 16)
   uint16_t knx[HPW], kny[HPW];
+  uint16_t vnew = 0;
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) knx[j] = kny[j] = 0;
+  // (these pointers are read from the arguments here, before the state's
+  // load: read after it, the wait for them would also wait for the state)
+  const uint16_t* kn_arg = A.k_new;
+  const uint16_t* vn_arg = A.v_new;
+  const int32_t* st_arg = A.seq_state;
+  const int32_t* sc_arg = A.sched;
+  if constexpr (STEP != 0)
+    asm volatile("" : "+s"(kn_arg), "+s"(vn_arg), "+s"(st_arg), "+s"(sc_arg));
+  else
+    asm volatile("" : "+s"(st_arg), "+s"(sc_arg));
+  typedef __attribute__((address_space(1))) const uint16_t* glb_u16_t;  // global loads
+  const glb_u16_t kn_ptr = (glb_u16_t)(kn_arg), vn_ptr = (glb_u16_t)(vn_arg);
+  auto issue_new = [&](int bb) {
+    if constexpr (STEP != 0) {
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        const int hh = wave + NW * j;
+        if (hh < A.hkv) {
+          const size_t base = (static_cast<size_t>(bb) * A.hkv + hh) * kD;
+          knx[j] = kn_ptr[base + L];
+          kny[j] = kn_ptr[base + L + 64];
+        }
+      }
+      if (tid < kD) vnew = vn_ptr[(static_cast<size_t>(bb) * A.hkv + h) * kD + tid];
+    }
+  };
+  // {n, Q} by a scalar load (the index is uniform): with a schedule, the
+  // sequence and its state as they were before the launch; else the state,
+  // which nothing in the launch writes before every workgroup of the
+  // sequence has read it.  The vector loads issued next do not wait
+  // behind it (without a schedule: with a schedule they need b).
+  typedef __attribute__((address_space(4))) const int32_t* cst_i32_t;
+  int b, n, Q;
+  if (sc_arg) {
+    const cst_i32_t sc = (cst_i32_t)(sc_arg) + 4 * rank;
+    b = sc[0];
+    n = sc[1];
+    Q = sc[2];
+    issue_new(b);
+  } else {
+    const cst_i32_t st_cst = (cst_i32_t)(st_arg);
+    b = rank;
+    n = st_cst[2 * b];
+    Q = st_cst[2 * b + 1];
+    issue_new(b);
+  }
+  const int pair = b * A.hkv + h;
+  const size_t bh = static_cast<size_t>(b) * A.hkv + h;
   auto load_new = [&](int hh, uint16_t& kx, uint16_t& ky) {
     const size_t base = (static_cast<size_t>(b) * A.hkv + hh) * kD;
     kx = A.k_new[base + L];
     ky = A.k_new[base + L + 64];
   };
-  uint16_t vnew = 0;
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) knx[j] = kny[j] = 0;
-  if constexpr (STEP != 0) {
-#pragma unroll
-    for (int j = 0; j < HPW; ++j)
-      if (wave + NW * j < A.hkv) load_new(wave + NW * j, knx[j], kny[j]);
-    if (tid < kD) vnew = A.v_new[bh * kD + tid];
-  }
   const bool state_good = Q >= 0 && (Q & 31) == 0 && n >= Q && n - Q <= kR && Q / kG <= A.max_blocks;
   if (!state_good) {
     if (tid == 0 && s == 0) atomicOr(A.error_flag, static_cast<int32_t>(OSCAR_FLAG_BADSTATE));
@@ -1762,10 +1802,42 @@ int auto_splits(const oscar_cache_geom* g, int max_ctx) { return attn_shape(g, m
 constexpr int kMaxPairs = 65536;
 constexpr size_t kCounterBytes = static_cast<size_t>(kMaxPairs) * sizeof(int32_t);
 
-// Partials: ws_ml [B][Hq][S] float2, then (256-B aligned) ws_o [B][Hq][S][128].
+// Partials: ws_ml [B][Hq][S] float2, then (256-B aligned) ws_o [B][Hq][S][128],
+// then (256-B aligned) the launch schedule, [B] x {b, n, Q, 0}.
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 size_t workspace_bytes(const oscar_cache_geom* g, int splits) {
   const size_t n = static_cast<size_t>(g->batch) * g->num_q_heads * splits;
-  return ((n * sizeof(float2) + 255) / 256) * 256 + n * kD * sizeof(float) + 256;
+  return round256(n * sizeof(float2)) + round256(n * kD * sizeof(float)) +
+         round256(static_cast<size_t>(g->batch) * 4 * sizeof(int32_t));
+}
+
+// The launch schedule of a batch: the sequences longest first (ties in
+// index order), each with the {n, Q} it has before the launch.  The GPU
+// starts workgroups in launch order as slots free up, so with contexts of
+// different lengths the long sequences' workgroups, started first, no
+// longer end the launch alone.  The attention kernel reads every {n, Q} from
+// here, so that its workgroups agree on the order even once a decode step's
+// appends have rewritten some states.  One workgroup; B <= 1024.
+constexpr int kSchedMax = 1024;
+__global__ __launch_bounds__(kSchedMax) void sched_kernel(const int32_t* __restrict__ seq_state, int batch,
+                                                         int32_t* __restrict__ sched) {
+  __shared__ int len[kSchedMax];
+  const int t = threadIdx.x;
+  int n = 0, Q = 0;
+  if (t < batch) {
+    n = seq_state[2 * t];
+    Q = seq_state[2 * t + 1];
+    len[t] = n;
+  }
+  __syncthreads();
+  if (t < batch) {
+    int r = 0;
+    for (int j = 0; j < batch; ++j) {
+      const int m = len[j];
+      r += (m > n || (m == n && j < t)) ? 1 : 0;
+    }
+    *reinterpret_cast<int4*>(sched + 4 * r) = make_int4(t, n, Q, 0);
+  }
 }
 static size_t attn_workspace_bytes(const oscar_cache_geom* g, int splits) {
   return kCounterBytes + workspace_bytes(g, splits);
@@ -1866,6 +1938,7 @@ static oscar_status decode_call(const oscar_cache_geom* geom, const oscar_cache*
   A.flush_blocks = geom->flush_tokens == 128 ? 4 : 1;
   A.hw_rsq = geom->key_scale == OSCAR_SCALE_HW_RSQ ? 1 : 0;
   A.append_sync = cache->append_sync;
+  A.sched = nullptr;
   hipStream_t hs = as_stream(stream);
   const int grp = geom->num_q_heads / geom->num_kv_heads;
   if (variant == OSCAR_ATTN_VALU) {
@@ -1887,6 +1960,14 @@ static oscar_status decode_call(const oscar_cache_geom* geom, const oscar_cache*
   // spreads the merging over the chip
   A.merge_in_kernel = shape.merge_in_kernel;
   const int nwg = geom->batch * geom->num_kv_heads * S;
+  if (geom->batch >= 2 && geom->batch <= kSchedMax) {
+    int32_t* sched = reinterpret_cast<int32_t*>(
+        part_base + round256(npart * sizeof(float2)) + round256(npart * kD * sizeof(float)));
+    hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedMax), 0, hs, cache->seq_state, geom->batch, sched);
+    st = launch_status();
+    if (st != OSCAR_OK) return st;
+    A.sched = sched;
+  }
   if (step) {
     switch (grp) {
       case 1: launch_mfma<1, 1>(A, nwg, shape.nw, hs); break;
