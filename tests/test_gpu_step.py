@@ -125,6 +125,22 @@ def test_step_many_pairs():
     _run(pr, twin, 36, check_every=12)
 
 
+def test_step_batch_in_two_rounds():
+    """48 ragged sequences in four splits each: 1536 workgroups, more than the
+    chip holds at once, so the launch runs in two rounds while the first
+    round's appenders already rewrite their sequences' states.  The launch
+    order (longest first) comes from a snapshot taken before the launch;
+    every step must still equal append + attention bit for bit."""
+    cfg = synth.CONFIGS[2]
+    rng = np.random.default_rng(48)
+    lens = [int(x) for x in rng.integers(0, 2600, 48)]
+    lens[5], lens[17] = 0, 127   # an empty sequence, one about to flush
+    c = synth.Config("b48r", 48, cfg.hq, cfg.hkv, None, cfg.dtype, cfg.sigma, cfg.outliers, 1)
+    wl = synth.Workload(c, 48, [L + 40 for L in lens], synth.workload(2, ctx=64).outlier_idx)
+    pr, twin = _prefilled(wl, lens)
+    _run(pr, twin, 34, splits=4, check_every=17)
+
+
 @pytest.mark.parametrize("grp", [1, 2, 8])
 def test_step_group_sizes(grp):
     wl = synth.workload(1, ctx=700)
