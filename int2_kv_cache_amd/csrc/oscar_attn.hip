@@ -607,7 +607,7 @@ void attn_mfma_kernel(AttnArgs A) {
   // user's last reads precede the next user's writes in the wave's program
   // order, and a wave's LDS operations complete in order)
   constexpr int kTileBytes = 4 * 8 * GRP * 16;
-  static_assert(2 * GRP * kRowPad * 4 <= kTileBytes, "scores and probabilities fit a tile");
+  static_assert((NCOL + GRP) * kRowPad * 4 <= kTileBytes, "scores and probabilities fit a tile");
   __shared__ __attribute__((aligned(16))) uint8_t lds_tile[NW][kTileBytes];
   __shared__ float lds_fac[NW][GRP];                     // per wave: rescale factors
   __shared__ float lds_zs[NW][4][GRP];                   // per wave: Value zero-point sums
@@ -634,10 +634,11 @@ void attn_mfma_kernel(AttnArgs A) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), L = tid & 63;
   typedef u32x4 BTiles[4][8 * GRP];   // [K step][row]
   typedef float Rows[GRP][kRowPad];
+  typedef float ScoreRows[NCOL][kRowPad];  // row h: hi part of head h, row h + GRP: lo part
   BTiles& Wbk = *reinterpret_cast<BTiles*>(lds_tile[wave]);
   BTiles& Wbv = *reinterpret_cast<BTiles*>(lds_tile[wave]);
-  Rows& Wsc = *reinterpret_cast<Rows*>(lds_tile[wave]);
-  Rows& Wpr = *reinterpret_cast<Rows*>(lds_tile[wave] + GRP * kRowPad * 4);
+  ScoreRows& Wsc = *reinterpret_cast<ScoreRows*>(lds_tile[wave]);
+  Rows& Wpr = *reinterpret_cast<Rows*>(lds_tile[wave] + NCOL * kRowPad * 4);
   float (&Wfac)[GRP] = lds_fac[wave];
   float (&Wzs)[4][GRP] = lds_zs[wave];
   // set-up (loads, query rotation, the window chunk) runs at the highest
@@ -1103,7 +1104,7 @@ void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
       for (int j = 0; j < TPL; ++j) {
         const int t = sm_t0 + j;
-        sv[j] = t < t_valid ? (Wsc[sm_head][t] + kp) * nt[j] : -INFINITY;
+        sv[j] = t < t_valid ? (Wsc[sm_head][t] + Wsc[sm_head + GRP][t] + kp) * nt[j] : -INFINITY;
         bm = fmaxf(bm, sv[j]);
       }
     }
@@ -1140,15 +1141,14 @@ void attn_mfma_kernel(AttnArgs A) {
     lds_order();
   };
 
-  // combine the hi and lo columns of the q.K^T tiles into Wsc
+  // the q.K^T tiles' score columns into Wsc as they are: the hi column of
+  // head h into row h, its lo column into row h + GRP (the softmax adds the
+  // two, which costs its lanes one LDS read instead of a cross-lane move and
+  // an add per score here)
   auto store_scores = [&](const f32x4* cs) {
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      f32x4 v;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = cs[tau][j] + dpp<dpp_row_shl(GRP)>(cs[tau][j]);
-      if (col < GRP) *reinterpret_cast<f32x4*>(&Wsc[col][16 * tau + 4 * g4]) = v;
-    }
+    for (int tau = 0; tau < 2; ++tau)
+      if (col < NCOL) *reinterpret_cast<f32x4*>(&Wsc[col][16 * tau + 4 * g4]) = cs[tau];
     lds_order();
   };
 
@@ -1178,12 +1178,14 @@ void attn_mfma_kernel(AttnArgs A) {
         u32x4 hi, lo;
         if (cur) {
           _Float16 d8[8];
+          // sum p * z_v with fused mixed-precision multiply-adds (the fp16
+          // zero point enters the fma without a conversion of its own)
           float zsum = 0.0f;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const uint32_t pz = cur->vp[r][k >> 2][k & 3];
             d8[k] = hbits(pz, 0);
-            zsum += pv[k] * static_cast<float>(hbits(pz, 1));
+            zsum = __builtin_fmaf(pv[k], static_cast<float>(hbits(pz, 1)), zsum);
           }
           zacc[r] += zsum;
           split8_mul(pv, d8, hi, lo);
@@ -1225,10 +1227,12 @@ void attn_mfma_kernel(AttnArgs A) {
         Wbk[kk][brow_k<NCOL>(hh + GRP + NCOL * g)] = lo;
       }
     }
-    // q'.z of the softmax lane's head (one row of lanes)
+    // q'.z of the softmax lane's head (one row of lanes), fused
+    // mixed-precision multiply-adds as above
     float kz = 0.0f;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) kz += zq[j] * static_cast<float>(hbits(cur.zz[j >> 3][(j & 7) >> 1], j & 1));
+    for (int j = 0; j < CPL; ++j)
+      kz = __builtin_fmaf(zq[j], static_cast<float>(hbits(cur.zz[j >> 3][(j & 7) >> 1], j & 1)), kz);
     kz = group_sum<LPH>(kz);
     lds_order();
 
