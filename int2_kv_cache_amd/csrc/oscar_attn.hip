@@ -361,6 +361,21 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// max / sum over the whole wave, the same value in every lane: rows of 16
+// lanes reduce with cross-lane moves, then the four row results are read
+// out and combined in row order (no LDS round trip)
+__device__ __forceinline__ float row_value(float v, int row) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16 * row));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max<16>(v);
+  return fmaxf(fmaxf(row_value(v, 0), row_value(v, 1)), fmaxf(row_value(v, 2), row_value(v, 3)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  return ((row_value(v, 0) + row_value(v, 1)) + row_value(v, 2)) + row_value(v, 3);
+}
+
 // fp32 -> packed fp16 pair, rounding toward zero (hi/lo splits: the low part
 // carries the remainder).
 __device__ __forceinline__ uint32_t pk_rtz(float a, float b) {
@@ -1596,13 +1611,9 @@ void attn_mfma_kernel(AttnArgs A) {
       }
 #pragma unroll
       for (int j = 0; j < 32; ++j) oc[j] = j < S ? load_dev(A.ws_o + (base + j) * kD + c) : 0.0f;
-      float M = mj;
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh));
+      const float M = wave_max(mj);
       const float wj = mj == -INFINITY ? 0.0f : exp2f(mj - M);
-      float Lw = wj * lj;
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) Lw += __shfl_xor(Lw, sh);
+      const float Lw = wave_sum(wj * lj);
       float Ow = 0.0f;
 #pragma unroll
       for (int j = 0; j < 32; ++j)
