@@ -1399,12 +1399,16 @@ void attn_mfma_kernel(AttnArgs A) {
   float zs[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) zs[d] = Wzs[d][col % GRP];
+  // (only the lanes of the hi columns, col < GRP, store: the zero-point sum
+  // is chosen once per group of 32 channels, not per element)
+#pragma unroll
+  for (int d = 0; d < 4; ++d) zs[d] = col < GRP ? zs[d] : 0.0f;
   float ov[8][4];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      ov[ct][j] = o[ct][j] + dpp<dpp_row_shl(GRP)>(o[ct][j]) + (col < GRP ? zs[ct >> 1] : 0.0f);
+      ov[ct][j] = o[ct][j] + dpp<dpp_row_shl(GRP)>(o[ct][j]) + zs[ct >> 1];
   // the stages take the waves' partial outputs: head hh of wave w at
   // (hh < 4 ? stage0 : stage1)[w] + 512 (hh % 4) bytes, once every copy into
   // them has landed
@@ -1493,7 +1497,9 @@ void attn_mfma_kernel(AttnArgs A) {
   for (int i = 0; i < NI; ++i) {
     const int idx = tid + NT * i, hh = (idx >> 7) % GRP, c = idx & 127;
     // every operand is read before any is combined; a wave with no tokens
-    // has m = -inf and weight 0
+    // has m = -inf and weight 0.  Weights come from the hardware exp2 here
+    // and in the cross-split merge: each is at most 1, and one below 2^-126
+    // (a partial that small against the largest) may count as 0.
     float mw[NW], lw[NW], ow[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -1507,7 +1513,7 @@ void attn_mfma_kernel(AttnArgs A) {
     float Lw = 0.0f, Ow = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float sc = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - M);
+      const float sc = mw[w] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - M);
       Lw += sc * lw[w];
       Ow += sc * ow[w];
     }
@@ -1612,7 +1618,7 @@ void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
       for (int j = 0; j < 32; ++j) oc[j] = j < S ? load_dev(A.ws_o + (base + j) * kD + c) : 0.0f;
       const float M = wave_max(mj);
-      const float wj = mj == -INFINITY ? 0.0f : exp2f(mj - M);
+      const float wj = mj == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
       const float Lw = wave_sum(wj * lj);
       float Ow = 0.0f;
 #pragma unroll
@@ -1658,12 +1664,12 @@ void attn_mfma_kernel(AttnArgs A) {
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) mb = fmaxf(mb, mc[j]);
       if (mb == -INFINITY) continue;
-      const float f = M == -INFINITY ? 0.0f : exp2f(M - mb);
+      const float f = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - mb);
       Lw *= f;
       Ow *= f;
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
-        const float w = mc[j] == -INFINITY ? 0.0f : exp2f(mc[j] - mb);
+        const float w = mc[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mc[j] - mb);
         Lw += w * lc[j];
         Ow += w * oc[j];
       }
