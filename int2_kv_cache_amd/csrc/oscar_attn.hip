@@ -639,6 +639,22 @@ void attn_mfma_kernel(AttnArgs A) {
   __shared__ uint16_t step_v[STEP ? kD : 2];
   __shared__ int lds_app;
 
+  // The arguments (216 bytes: four 64-byte lines of the scalar cache) are
+  // requested in one batch before anything else: the pointers of the first
+  // loads (read here, before the state's load: read after it, the wait for
+  // them would also wait for the state), the split and head counts, and one
+  // field of every line besides, so that the set-up's later argument reads
+  // hit the scalar cache instead of each waiting for a line of its own.
+  const uint16_t* kn_arg = A.k_new;
+  const uint16_t* vn_arg = A.v_new;
+  const int32_t* st_arg = A.seq_state;
+  const int32_t* sc_arg = A.sched;
+  if constexpr (STEP != 0)
+    asm volatile("" : "+s"(kn_arg), "+s"(vn_arg), "+s"(st_arg), "+s"(sc_arg)
+                 : "s"(A.pool), "s"(A.splits), "s"(A.hkv), "s"(A.out));
+  else
+    asm volatile("" : "+s"(st_arg), "+s"(sc_arg) : "s"(A.pool), "s"(A.splits), "s"(A.hkv), "s"(A.out),
+                 "s"(A.k_new));
   // workgroup (r Hkv + h) S + s: split s of KV head h of the sequence of
   // launch rank r (the sequence itself with no schedule)
   const int wid = static_cast<int>(blockIdx.x);
@@ -668,16 +684,6 @@ void attn_mfma_kernel(AttnArgs A) {
   uint16_t vnew = 0;
 #pragma unroll
   for (int j = 0; j < HPW; ++j) knx[j] = kny[j] = 0;
-  // (these pointers are read from the arguments here, before the state's
-  // load: read after it, the wait for them would also wait for the state)
-  const uint16_t* kn_arg = A.k_new;
-  const uint16_t* vn_arg = A.v_new;
-  const int32_t* st_arg = A.seq_state;
-  const int32_t* sc_arg = A.sched;
-  if constexpr (STEP != 0)
-    asm volatile("" : "+s"(kn_arg), "+s"(vn_arg), "+s"(st_arg), "+s"(sc_arg));
-  else
-    asm volatile("" : "+s"(st_arg), "+s"(sc_arg));
   typedef __attribute__((address_space(1))) const uint16_t* glb_u16_t;  // global loads
   const glb_u16_t kn_ptr = (glb_u16_t)(kn_arg), vn_ptr = (glb_u16_t)(vn_arg);
   auto issue_new = [&](int bb) {
