@@ -1795,9 +1795,11 @@ __global__ __launch_bounds__(256) void lse_reduce_kernel(const float2* __restric
 // SIMD.  Few (sequence, KV head) pairs: one 12-wave workgroup per CU, as
 // many splits as fill all 256 CUs once (a CU left idle costs its share of the
 // bandwidth), while every wave still gets a unit.  Many pairs: three 4-wave
-// workgroups per CU, and twice that many splits where a workgroup would
-// otherwise hold 256 blocks or more (two rounds: the dispatcher's refill
-// evens out ragged sequences).
+// workgroups per CU, one round of them.  The launch order (longest sequence
+// first, dealt round-robin over the CUs) already gives each CU a long, a
+// middle and a short workgroup; a second round would only add a second
+// round of set-up and merge per workgroup slot (ragged batch of 48 at 8K..32K:
+// 180 us per step with two splits per pair against 183 us with four).
 struct AttnShape {
   int nw, splits, merge_in_kernel;
 };
@@ -1811,7 +1813,6 @@ AttnShape attn_shape(const oscar_cache_geom* g, int max_ctx, int num_splits) {
   int s = num_splits;
   if (!s) {
     s = (256 * (12 / nw) + pairs - 1) / pairs;
-    if (nw == 4 && units / s >= 256) s *= 2;
     const int cap = units / (nw == 12 ? nw : 4 * nw) > 1 ? units / (nw == 12 ? nw : 4 * nw) : 1;
     if (s > cap) s = cap;
     if (s > 1024) s = 1024;
