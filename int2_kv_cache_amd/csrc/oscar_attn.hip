@@ -1991,7 +1991,9 @@ static oscar_status decode_call(const oscar_cache_geom* geom, const oscar_cache*
   if (geom->batch >= 2 && geom->batch <= kSchedMax) {
     int32_t* sched = reinterpret_cast<int32_t*>(
         part_base + round256(npart * sizeof(float2)) + round256(npart * kD * sizeof(float)));
-    hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedMax), 0, hs, cache->seq_state, geom->batch, sched);
+    // one thread per sequence, in whole waves (one wave up to 64 sequences)
+    const int threads = (geom->batch + 63) / 64 * 64;
+    hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(threads), 0, hs, cache->seq_state, geom->batch, sched);
     st = launch_status();
     if (st != OSCAR_OK) return st;
     A.sched = sched;
