@@ -435,10 +435,16 @@ __device__ __forceinline__ int bv_row(int x) { return x ^ (2 * ((x >> 4) & 3)); 
 // of K step g4, and lane (col, g4) reads row (col % NCOL) + NCOL g4 (lanes of
 // the unused columns read a duplicate).  Rows are permuted as above so that
 // the writers' and readers' 16-byte accesses fall in distinct bank groups.
+// With 8 used columns (4 query heads per KV head) the Key tiles' writers
+// (units: heads, then channel groups) and the Value tiles' writers (units:
+// token octets, then heads) both reach distinct 16-byte bank groups in every
+// group of 8 lanes and of 16 lanes, and so do the readers, when bit 3 of the
+// row flips bit 2 and bit 4 flips bits 1 and 2.
+__device__ __forceinline__ int b8_row(int x) { return x ^ (4 * ((x >> 3) & 1)) ^ (6 * ((x >> 4) & 1)); }
 template <int NCOL>
-__device__ __forceinline__ int brow_k(int x) { return bk_row(x); }
+__device__ __forceinline__ int brow_k(int x) { return NCOL == 8 ? b8_row(x) : bk_row(x); }
 template <int NCOL>
-__device__ __forceinline__ int brow_v(int x) { return NCOL == 16 ? bv_row(x) : bk_row(x); }
+__device__ __forceinline__ int brow_v(int x) { return NCOL == 16 ? bv_row(x) : NCOL == 8 ? b8_row(x) : bk_row(x); }
 constexpr int kRowPad = 36;  // score / probability rows: 32 floats + 4 of padding
 
 // Global data one lane needs for one INT2 block.
@@ -487,10 +493,18 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // normal lines would evict what the call does reuse (its partials, the state,
 // the block table, its own code) -- measured 1.2 to 1.5 us less per call at
 // batch 1.
+// The Key codes (the record's first 1024 bytes: token t's 32 bytes are
+// 16-byte chunks 2t and 2t + 1) are copied with chunk p at chunk p ^ bit 4
+// of p, one of the copy's free lane-to-chunk choices: the 16 lanes that read
+// 8 bytes of 16 different tokens' chunks then reach 16 different bank pairs.
+// The map is its own inverse.
+// (Used with 4 query heads per KV head, whose readers it was chosen for.)
+__device__ __forceinline__ uint32_t kc_chunk(uint32_t p) { return p ^ ((p >> 4) & 1u); }
+template <bool KC_SWZ>
 __device__ __forceinline__ void dma_unit(__amdgpu_buffer_rsrc_t rec, __amdgpu_buffer_rsrc_t nrm,
                                          const uint8_t* st, int L) {
   const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)st));
-  const uint32_t v0 = 16 * L, v1 = 16 * L + 1024, v2 = 16 * L + 2048, vn = 4 * L;
+  const uint32_t v0 = 16 * (KC_SWZ ? kc_chunk(L) : L), v1 = 16 * L + 1024, v2 = 16 * L + 2048, vn = 4 * L;
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "buffer_load_dwordx4 %1, %5, 0 offen nt lds\n\t"
@@ -851,8 +865,14 @@ void attn_mfma_kernel(AttnArgs A) {
                                     : reinterpret_cast<const float2*>(A.seq_state));
 
   UnitOffs<NR> off;
-  off.kc0 = kRecKCodes + 32 * col + 8 * g4;
-  off.kc1 = kRecKCodes + 32 * (16 + col) + 8 * g4;
+  constexpr bool kKcSwz = GRP == 4;  // Key codes copied with their chunks permuted
+  if constexpr (kKcSwz) {
+    off.kc0 = kRecKCodes + 16 * kc_chunk(2 * col + (g4 >> 1)) + 8 * (g4 & 1);
+    off.kc1 = off.kc0 + 512;  // tokens 16 + col: the chunk map commutes with adding 32 chunks
+  } else {
+    off.kc0 = kRecKCodes + 32 * col + 8 * g4;
+    off.kc1 = kRecKCodes + 32 * (16 + col) + 8 * g4;
+  }
   off.vc = kRecVCodes + 16 * L;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -911,7 +931,7 @@ void attn_mfma_kernel(AttnArgs A) {
   auto dma_block = [&](int j, uint8_t* st) {
     if (j > 0 && (j & 63) == 0) idv = load_ids(j);
     const int p = __builtin_amdgcn_readlane(idv, j & 63);
-    dma_unit(unit_rec(p), unit_nrm(p), st, L);
+    dma_unit<kKcSwz>(unit_rec(p), unit_nrm(p), st, L);
   };
   if (!wg_fresh) {
     if (cnt > 0) dma_block(0, st0);
