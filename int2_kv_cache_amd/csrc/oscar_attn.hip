@@ -1641,8 +1641,11 @@ void attn_mfma_kernel(AttnArgs A) {
         mj = load_dev(ml + 2 * (base + lane));
         lj = load_dev(ml + 2 * (base + lane) + 1);
       }
+      // all 32 loads issued back to back, with no branch between them: a
+      // split index past S re-reads split S - 1, whose weight below is 0
+      const float* const ob = A.ws_o + base * kD + c;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) oc[j] = j < S ? load_dev(A.ws_o + (base + j) * kD + c) : 0.0f;
+      for (int j = 0; j < 32; ++j) oc[j] = load_dev(ob + static_cast<size_t>(j < S ? j : S - 1) * kD);
       const float M = wave_max(mj);
       const float wj = mj == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
       const float Lw = wave_sum(wj * lj);
