@@ -1650,11 +1650,11 @@ void attn_mfma_kernel(AttnArgs A) {
       const float wj = mj == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
       const float Lw = wave_sum(wj * lj);
       float Ow = 0.0f;
+      // (no branch on S: weight j >= S is 0 and oc[j] a finite re-read, so
+      // those terms add zero and leave Ow unchanged)
 #pragma unroll
       for (int j = 0; j < 32; ++j)
-        if (j < S)
-          Ow += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j)) *
-                oc[j];
+        Ow += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j)) * oc[j];
       finish(idx, M, Lw, Ow);
     }
     if (tid == 0) __hip_atomic_store(A.counters + counter_slot(pair), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
