@@ -1671,24 +1671,25 @@ void attn_mfma_kernel(AttnArgs A) {
     float M = -INFINITY, Lw = 0.0f, Ow = 0.0f;
     for (int s0 = 0; s0 < S; s0 += kChunk) {
       float mc[kChunk], lc[kChunk], oc[kChunk];
+      // the chunk's loads back to back, with no branch between them: a split
+      // index past S re-reads split S - 1 and gets m = -inf (weight 0)
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
         const int sj = s0 + j;
-        mc[j] = -INFINITY;
-        lc[j] = oc[j] = 0.0f;
-        if (sj < S) {
-          if constexpr (PUB == 1) {
-            mc[j] = load_dev(ml + 2 * (base + sj));
-            lc[j] = load_dev(ml + 2 * (base + sj) + 1);
-            oc[j] = load_dev(A.ws_o + (base + sj) * kD + c);
-          } else {
-            const float2 v = A.ws_ml[base + sj];
-            mc[j] = v.x;
-            lc[j] = v.y;
-            oc[j] = A.ws_o[(base + sj) * kD + c];
-          }
+        const size_t sc = static_cast<size_t>(sj < S ? sj : S - 1);
+        if constexpr (PUB == 1) {
+          mc[j] = load_dev(ml + 2 * (base + sc));
+          lc[j] = load_dev(ml + 2 * (base + sc) + 1);
+          oc[j] = load_dev(A.ws_o + (base + sc) * kD + c);
+        } else {
+          const float2 v = A.ws_ml[base + sc];
+          mc[j] = v.x;
+          lc[j] = v.y;
+          oc[j] = A.ws_o[(base + sc) * kD + c];
         }
       }
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) mc[j] = s0 + j < S ? mc[j] : -INFINITY;
       float mb = M;
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) mb = fmaxf(mb, mc[j]);
