@@ -933,10 +933,10 @@ void attn_mfma_kernel(AttnArgs A) {
     const int p = __builtin_amdgcn_readlane(idv, j & 63);
     dma_unit<kKcSwz>(unit_rec(p), unit_nrm(p), st, L);
   };
-  if (!wg_fresh) {
-    if (cnt > 0) dma_block(0, st0);
-    if (cnt > 1) dma_block(1, st1);
-  }
+  // Block 0's copy goes out now, block 1's after the query rotation (below):
+  // every wave's first record then lands ahead of the second ones, instead of
+  // the two fills sharing the bandwidth, and the loop starts sooner.
+  if (!wg_fresh && cnt > 0) dma_block(0, st0);
   if constexpr (STEP != 0) {
     if (wg_fresh) {
       // The flushed block(s) of this split: head h's 32 window tokens of
@@ -1066,6 +1066,8 @@ void attn_mfma_kernel(AttnArgs A) {
     }
   }
   __syncthreads();
+  // block 1's copy (a flushing workgroup issued both with its records)
+  if (!wg_fresh && cnt > 1) dma_block(1, st1);
   if constexpr (STEP != 0) {
     if (wave_new) {
       // the token's Key row and norm as the append stores them, put in place
